@@ -1,0 +1,163 @@
+"""CPU oracle for the deformable sampling operators -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, single-threaded and double precision.  Only ``tests/``, the
+smoke check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product library (``sparse_deformable_sampling_amd``)
+never imports it, and the two share no code.
+
+The arithmetic lives in ``dcn_oracle.c`` (compiled with gcc into
+``oracle/_build/liboracle.so``); this module only converts the stored input
+values to float64 exactly and marshals the arrays.  Every function states the
+passage of the pages it follows in the C source:
+
+* "InternImage: Deformable Convolutions at Scale", Ch.2-4 (bilinear read,
+  DCNv3 operator and softmax, groups);
+* "DCNv4: Unbounded Weights", "Why Is Sampling Just 9 Points Still Slow?" and
+  "1. Remove Softmax" (the per-group sum, unnormalised modulation);
+* "Deformable DETR: Learn Where to Read", "A learned location can fall between
+  cells" and "Mix samples with a per-head budget" (MSDA sampling and joint
+  softmax).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dcn_oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (plain -O2, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(_OUT_DIR, exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+                           "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Dcn(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in
+                ("n", "h", "w", "c", "group", "kernel_h", "kernel_w", "stride_h", "stride_w",
+                 "pad_h", "pad_w", "dil_h", "dil_w")] + [
+        ("offset_scale", ctypes.c_double), ("softmax", ctypes.c_int)]
+
+
+class _Msda(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in
+                ("n", "len_q", "heads", "head_dim", "levels", "points", "softmax")]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        pd = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_dcn_out_size.argtypes = [ctypes.POINTER(_Dcn), ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(ctypes.c_int)]
+        for name in ("oracle_dcn_forward", "oracle_dcn_forward_tent"):
+            getattr(lib, name).argtypes = [ctypes.POINTER(_Dcn), pd, pd, pd, pd]
+        lib.oracle_dcn_backward.argtypes = [ctypes.POINTER(_Dcn), pd, pd, pd, pd, pd, pd, pd]
+        for name in ("oracle_msda_forward", "oracle_msda_forward_tent"):
+            getattr(lib, name).argtypes = [ctypes.POINTER(_Msda), ctypes.POINTER(ctypes.c_int),
+                                           pd, pd, pd, pd]
+        _lib = lib
+    return _lib
+
+
+def to_f64(a: np.ndarray, dtype: str | None = None) -> np.ndarray:
+    """Exact float64 copy of stored values.  bf16 arrives as its uint16 bit
+    pattern (numpy has no bfloat16): the bits are the top half of an f32."""
+    if dtype == "bf16" or (dtype is None and a.dtype == np.uint16):
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _dcn_struct(n, h, w, c, group, kernel, stride, pad, dil, offset_scale, softmax):
+    kh, kw = kernel
+    return _Dcn(n, h, w, c, group, kh, kw, stride[0], stride[1], pad[0], pad[1],
+                dil[0], dil[1], float(offset_scale), int(softmax))
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def dcn_out_size(h, w, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dil=(1, 1)):
+    p = _dcn_struct(1, h, w, 1, 1, _pair(kernel), _pair(stride), _pair(pad), _pair(dil), 1.0, 0)
+    ho, wo = ctypes.c_int(), ctypes.c_int()
+    _load().oracle_dcn_out_size(ctypes.byref(p), ctypes.byref(ho), ctypes.byref(wo))
+    return ho.value, wo.value
+
+
+def dcn_forward(x, offset, mask, group, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dil=(1, 1),
+                offset_scale=1.0, softmax=False, dtype=None, tent=False):
+    """out[n,ho,wo,c] of the DCN core op, float64.  x: [n,h,w,c];
+    offset: [n,ho,wo,group,K,2] holding (dx, dy); mask: [n,ho,wo,group,K]."""
+    x64, o64, m64 = to_f64(x, dtype), to_f64(offset, dtype), to_f64(mask, dtype)
+    n, h, w, c = x64.shape
+    kernel, stride, pad, dil = _pair(kernel), _pair(stride), _pair(pad), _pair(dil)
+    p = _dcn_struct(n, h, w, c, group, kernel, stride, pad, dil, offset_scale, softmax)
+    ho, wo = dcn_out_size(h, w, kernel, stride, pad, dil)
+    K = kernel[0] * kernel[1]
+    assert o64.size == n * ho * wo * group * K * 2 and m64.size == n * ho * wo * group * K
+    out = np.zeros((n, ho, wo, c), np.float64)
+    fn = _load().oracle_dcn_forward_tent if tent else _load().oracle_dcn_forward
+    rc = fn(ctypes.byref(p), _ptr(x64), _ptr(np.ascontiguousarray(o64)), _ptr(np.ascontiguousarray(m64)),
+            _ptr(out))
+    assert rc == 0
+    return out
+
+
+def dcn_backward(x, offset, mask, grad_out, group, kernel=(3, 3), stride=(1, 1), pad=(1, 1),
+                 dil=(1, 1), offset_scale=1.0, softmax=False, dtype=None):
+    """(grad_x, grad_offset, grad_mask) in float64; grad_mask is with respect
+    to the values passed in mask (the logits when softmax is set)."""
+    x64, o64, m64 = to_f64(x, dtype), to_f64(offset, dtype), to_f64(mask, dtype)
+    g64 = to_f64(grad_out, dtype)
+    n, h, w, c = x64.shape
+    kernel, stride, pad, dil = _pair(kernel), _pair(stride), _pair(pad), _pair(dil)
+    p = _dcn_struct(n, h, w, c, group, kernel, stride, pad, dil, offset_scale, softmax)
+    gx = np.zeros_like(x64)
+    go = np.zeros(o64.shape, np.float64)
+    gm = np.zeros(m64.shape, np.float64)
+    rc = _load().oracle_dcn_backward(ctypes.byref(p), _ptr(x64), _ptr(np.ascontiguousarray(o64)),
+                                     _ptr(np.ascontiguousarray(m64)), _ptr(np.ascontiguousarray(g64)),
+                                     _ptr(gx), _ptr(go), _ptr(gm))
+    assert rc == 0
+    return gx, go, gm
+
+
+def msda_forward(value, shapes, loc, attn, softmax=True, dtype=None, tent=False):
+    """out[n,q,heads,head_dim] of multi-scale deformable attention, float64.
+    value: [n,S,heads,head_dim]; shapes: [(H_l, W_l)]; loc: [n,q,heads,L,P,2]
+    normalised (u, v); attn: [n,q,heads,L,P] (logits when softmax is set)."""
+    v64, l64, a64 = to_f64(value, dtype), to_f64(loc, dtype), to_f64(attn, dtype)
+    n, S, M, Dh = v64.shape
+    _, Q, M2, L, P, two = l64.shape
+    assert M2 == M and two == 2 and len(shapes) == L
+    sh = np.ascontiguousarray(np.asarray(shapes, np.int32).reshape(L, 2))
+    assert int((sh[:, 0].astype(np.int64) * sh[:, 1]).sum()) == S
+    p = _Msda(n, Q, M, Dh, L, P, int(softmax))
+    out = np.zeros((n, Q, M, Dh), np.float64)
+    fn = _load().oracle_msda_forward_tent if tent else _load().oracle_msda_forward
+    rc = fn(ctypes.byref(p), sh.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _ptr(v64),
+            _ptr(np.ascontiguousarray(l64)), _ptr(np.ascontiguousarray(a64)), _ptr(out))
+    assert rc == 0
+    return out

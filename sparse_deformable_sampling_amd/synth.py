@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs for the deformable sampling operators.
+
+This module holds no arithmetic of the method: it draws random tensors of the
+shapes and distributions of the workloads and stores them in the requested
+dtype.  It is the one module that both the GPU path's callers and the CPU
+oracle's callers use, so that both see identical inputs.
+
+Generator: numpy's Philox4x32-10 counter-based bit generator (Salmon et al.,
+"Parallel random numbers: as easy as 1, 2, 3", SC'11), one independent stream
+per tensor, keyed by ``1000 * seed + tensor_id``.  Values are drawn in float32
+and rounded to nearest-even into f16 or bf16.  bf16 tensors are returned as
+their uint16 bit patterns because numpy has no bfloat16 type.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# stream ids, one per tensor
+X, OFFSET, MASK, GRAD_OUT, VALUE, REF, MSDA_OFFSET, ATTN = 1, 2, 3, 4, 5, 6, 7, 8
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+def _rng(seed: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=1000 * int(seed) + int(tensor_id)))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Store float32 draws in the given dtype ("f32", "f16" or "bf16")."""
+    if dtype == "f32":
+        return np.ascontiguousarray(a, np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(a.astype(np.float16))
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    raise ValueError("dtype must be one of %s" % (DTYPES,))
+
+
+def normal(shape, std: float, seed: int, tensor_id: int) -> np.ndarray:
+    r = _rng(seed, tensor_id).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        r *= np.float32(std)
+    return r
+
+
+def uniform(shape, lo: float, hi: float, seed: int, tensor_id: int) -> np.ndarray:
+    return _rng(seed, tensor_id).uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def dcn_inputs(n, h, w, c, group, out_hw, taps=9, offset=("normal", 1.5), dtype="f32", seed=1,
+               grad=False):
+    """x ~ N(0,1) [n,h,w,c]; offsets [n,ho,wo,group,taps,2] drawn from
+    ``offset`` = ("normal", std) or ("uniform", lo, hi); mask [n,ho,wo,group,taps]
+    ~ N(0,1) (logits for DCNv3, raw modulation for DCNv4); optional
+    grad_out ~ N(0,1) [n,ho,wo,c]."""
+    ho, wo = out_hw
+    out = {"x": store(normal((n, h, w, c), 1.0, seed, X), dtype)}
+    oshape = (n, ho, wo, group, taps, 2)
+    if offset[0] == "normal":
+        off = normal(oshape, offset[1], seed, OFFSET)
+    elif offset[0] == "uniform":
+        off = uniform(oshape, offset[1], offset[2], seed, OFFSET)
+    else:
+        raise ValueError(offset)
+    out["offset"] = store(off, dtype)
+    out["mask"] = store(normal((n, ho, wo, group, taps), 1.0, seed, MASK), dtype)
+    if grad:
+        out["grad_out"] = store(normal((n, ho, wo, c), 1.0, seed, GRAD_OUT), dtype)
+    return out
+
+
+def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype="f32", seed=1):
+    """Value ~ N(0,1) [n,S,heads,head_dim] with S = sum H_l*W_l; per query a
+    reference point ~ U(0,1)^2; each sampling location is that point plus
+    N(0, offset_std) divided by the level's (W_l, H_l); attention logits
+    ~ N(0,1) [n,len_q,heads,L,points]."""
+    L = len(shapes)
+    S = int(sum(int(hh) * int(ww) for hh, ww in shapes))
+    value = store(normal((n, S, heads, head_dim), 1.0, seed, VALUE), dtype)
+    ref = uniform((n, len_q, 1, 1, 1, 2), 0.0, 1.0, seed, REF)
+    dev = normal((n, len_q, heads, L, points, 2), offset_std, seed, MSDA_OFFSET)
+    size = np.array([[ww, hh] for hh, ww in shapes], np.float32).reshape(1, 1, 1, L, 1, 2)
+    loc = (ref + dev / size).astype(np.float32)
+    attn = store(normal((n, len_q, heads, L, points), 1.0, seed, ATTN), dtype)
+    return {"value": value, "loc": store(loc, dtype), "attn": attn}

@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+Every test here runs on the CPU.  None of them re-types the oracle's own
+formula: each checks it against a printed worked example (tests/golden/), a
+closed form, a library routine that the method reduces to in a special case,
+an independent brute-force formulation, an invariant, or finite differences.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from sparse_deformable_sampling_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def zeros_like_offsets(n, ho, wo, g, K):
+    return np.zeros((n, ho, wo, g, K, 2)), np.zeros((n, ho, wo, g, K))
+
+
+# --------------------------------------------------------------------------
+# worked examples printed on the pages
+
+
+def test_bilinear_worked_example():
+    gd = golden("bilinear_worked_example.json")
+    x = np.array(gd["map_rows"], np.float64).reshape(1, 2, 2, 1)
+    off, mask = zeros_like_offsets(1, 2, 2, 1, 1)
+    mask[...] = 1.0
+    off[0, 0, 0, 0, 0] = gd["point_xy"]  # output (0,0) reads at p = (0.25, 0.75)
+    out = oracle.dcn_forward(x, off, mask, group=1, kernel=1, pad=0)
+    assert out[0, 0, 0, 0] == gd["value"]
+    # each corner's weight alone: put a one at that corner, zero elsewhere
+    for key, wt in gd["corner_weights_xy"].items():
+        cx, cy = map(int, key.split(","))
+        one = np.zeros((1, 2, 2, 1))
+        one[0, cy, cx, 0] = 1.0
+        assert oracle.dcn_forward(one, off, mask, group=1, kernel=1, pad=0)[0, 0, 0, 0] == wt
+    assert sum(gd["corner_weights_xy"].values()) == 1.0
+
+
+def test_offset_spike_example():
+    gd = golden("offset_spike_example.json")
+    sig = np.array(gd["signal"], np.float64).reshape(1, 1, len(gd["signal"]), 1)
+    for case in gd["cases"]:
+        off, mask = zeros_like_offsets(1, 1, 5, 1, 1)
+        mask[...] = 1.0
+        off[0, 0, gd["p0"], 0, 0, 0] = case["offset"]
+        out = oracle.dcn_forward(sig, off, mask, group=1, kernel=1, pad=0)
+        assert out[0, 0, gd["p0"], 0] == case["value"]
+
+
+def test_dcnv3_softmax_worked_example():
+    gd = golden("dcnv3_softmax_example.json")
+    v = np.array(gd["sampled"]).reshape(1, 1, 3, 1)
+    # a 1x3 kernel with no padding over a 1x3 map reads the three values as taps
+    off, _ = zeros_like_offsets(1, 1, 1, 1, 3)
+    logits = np.array(gd["logits"]).reshape(1, 1, 1, 1, 3)
+    out = oracle.dcn_forward(v, off, logits, group=1, kernel=(1, 3), pad=0, softmax=True)[0, 0, 0, 0]
+    e = math.e
+    assert out == pytest.approx((2 + 8 * e * e + 4 * e) / (1 + e + e * e), rel=1e-14, abs=0)
+    # the printed 6.480 was formed from 3-decimal modulations: within 0.0005 * sum|v|
+    assert abs(out - gd["printed_output"]) <= 0.0005 * sum(abs(s) for s in gd["sampled"])
+    for j, mj in enumerate(gd["printed_modulation"]):
+        one = np.zeros((1, 1, 3, 1))
+        one[0, 0, j, 0] = 1.0
+        m = oracle.dcn_forward(one, off, logits, group=1, kernel=(1, 3), pad=0, softmax=True)[0, 0, 0, 0]
+        assert round(m, gd["printed_modulation_decimals"]) == pytest.approx(mj, abs=1e-9)
+
+
+# --------------------------------------------------------------------------
+# special cases that reduce to textbook routines
+
+
+def test_zero_offsets_equal_logits_is_average_pool():
+    rng = np.random.default_rng(3)
+    for stride in (1, 2):
+        x = rng.standard_normal((2, 7, 9, 6))
+        ho, wo = oracle.dcn_out_size(7, 9, 3, stride, 1, 1)
+        off, logits = zeros_like_offsets(2, ho, wo, 3, 9)
+        logits[...] = 0.7  # equal logits -> every modulation 1/9
+        out = oracle.dcn_forward(x, off, logits, group=3, kernel=3, stride=stride, pad=1, softmax=True)
+        ref = F.avg_pool2d(torch.from_numpy(x).permute(0, 3, 1, 2), 3, stride=stride, padding=1,
+                           count_include_pad=True).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("kernel,stride,pad,dil", [((3, 2), (2, 1), (1, 2), (1, 2)),
+                                                   ((3, 3), (1, 1), (1, 1), (1, 1)),
+                                                   ((1, 3), (1, 3), (0, 1), (1, 1)),
+                                                   ((2, 3), (1, 2), (2, 0), (3, 1))])
+def test_zero_offsets_constant_mask_is_depthwise_conv(kernel, stride, pad, dil):
+    """Zero offsets and a modulation w_k that is the same at every pixel turn
+    the operator into a depthwise convolution whose kernel is w_k, shared by
+    the channels of a group.  Tap k sits at (kx, ky) = (k // kh, k % kh)."""
+    rng = np.random.default_rng(5)
+    n, h, w, c, g = 2, 8, 9, 6, 2
+    kh, kw = kernel
+    K = kh * kw
+    x = rng.standard_normal((n, h, w, c))
+    ho, wo = oracle.dcn_out_size(h, w, kernel, stride, pad, dil)
+    wk = rng.standard_normal((g, K))
+    off = np.zeros((n, ho, wo, g, K, 2))
+    mask = np.broadcast_to(wk, (n, ho, wo, g, K)).copy()
+    out = oracle.dcn_forward(x, off, mask, group=g, kernel=kernel, stride=stride, pad=pad, dil=dil)
+    weight = np.zeros((c, 1, kh, kw))
+    for ch in range(c):
+        for k in range(K):
+            weight[ch, 0, k % kh, k // kh] = wk[ch // (c // g), k]
+    ref = F.conv2d(torch.from_numpy(x).permute(0, 3, 1, 2), torch.from_numpy(weight), stride=stride,
+                   padding=pad, dilation=dil, groups=c).permute(0, 2, 3, 1).numpy()
+    assert ref.shape == out.shape
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_integer_offsets_shift_exactly():
+    """One-hot DCNv4 modulation on tap k with an integer offset reads the
+    pixel at p0 + p_k + dp exactly, zero outside."""
+    rng = np.random.default_rng(7)
+    n, h, w, c, g = 1, 6, 7, 4, 2
+    x = rng.standard_normal((n, h, w, c))
+    ho, wo = oracle.dcn_out_size(h, w, 3, 1, 1, 1)
+    for k in (0, 4, 5, 8):
+        off = rng.integers(-3, 4, size=(n, ho, wo, g, 9, 2)).astype(np.float64)
+        mask = np.zeros((n, ho, wo, g, 9))
+        mask[..., k] = 1.0
+        out = oracle.dcn_forward(x, off, mask, group=g)
+        kx, ky = k // 3, k % 3
+        ref = np.zeros_like(out)
+        for yo in range(ho):
+            for xo in range(wo):
+                for gg in range(g):
+                    col = xo - 1 + kx + int(off[0, yo, xo, gg, k, 0])
+                    row = yo - 1 + ky + int(off[0, yo, xo, gg, k, 1])
+                    if 0 <= row < h and 0 <= col < w:
+                        ref[0, yo, xo, gg * 2:gg * 2 + 2] = x[0, row, col, gg * 2:gg * 2 + 2]
+        assert np.array_equal(out, ref)
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+
+def test_weights_sum_to_one_on_constant_map():
+    rng = np.random.default_rng(11)
+    n, h, w, c, g = 1, 12, 12, 4, 2
+    x = np.full((n, h, w, c), 3.25)
+    off = rng.uniform(-0.9, 0.9, size=(n, h, w, g, 9, 2))
+    mask = rng.standard_normal((n, h, w, g, 9))
+    out = oracle.dcn_forward(x, off, mask, group=g)
+    inner = out[:, 2:-2, 2:-2]  # every corner of every tap lies inside the map
+    ref = (3.25 * mask.sum(-1))[:, 2:-2, 2:-2]
+    np.testing.assert_allclose(inner, np.repeat(ref, 2, axis=-1), rtol=1e-13, atol=1e-13)
+    soft = oracle.dcn_forward(x, off, mask, group=g, softmax=True)[:, 2:-2, 2:-2]
+    np.testing.assert_allclose(soft, 3.25, rtol=1e-14)
+
+
+def test_group_independence():
+    rng = np.random.default_rng(13)
+    n, h, w, c, g = 1, 6, 6, 12, 3
+    x = rng.standard_normal((n, h, w, c))
+    off = rng.normal(0, 1.5, size=(n, h, w, g, 9, 2))
+    mask = rng.standard_normal((n, h, w, g, 9))
+    base = oracle.dcn_forward(x, off, mask, group=g)
+    x2 = x.copy()
+    x2[..., 4:8] += rng.standard_normal((n, h, w, 4))  # group 1
+    pert = oracle.dcn_forward(x2, off, mask, group=g)
+    assert np.array_equal(base[..., :4], pert[..., :4])
+    assert np.array_equal(base[..., 8:], pert[..., 8:])
+    assert not np.allclose(base[..., 4:8], pert[..., 4:8])
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+@pytest.mark.parametrize("geom", [dict(kernel=3, stride=1, pad=1, dil=1),
+                                  dict(kernel=(3, 2), stride=(2, 1), pad=(0, 2), dil=(2, 1)),
+                                  dict(kernel=(1, 1), stride=1, pad=0, dil=1)])
+def test_tent_brute_force_agrees(softmax, geom):
+    """The floor-corner form equals the tent-weighted sum over all pixels."""
+    rng = np.random.default_rng(17)
+    n, h, w, c, g = 2, 5, 6, 4, 2
+    x = rng.standard_normal((n, h, w, c))
+    ho, wo = oracle.dcn_out_size(h, w, geom["kernel"], geom["stride"], geom["pad"], geom["dil"])
+    K = int(np.prod(geom["kernel"])) if not isinstance(geom["kernel"], int) else geom["kernel"] ** 2
+    off = rng.normal(0, 2.0, size=(n, ho, wo, g, K, 2))
+    off[0, 0, 0, 0, 0] = [0.0, 0.0]        # integer coordinates
+    off[0, 0, 0, 1, 0] = [-40.0, 3.3]      # far outside
+    off[-1, -1, -1, 0, -1] = [0.5, -0.5]   # half-way
+    mask = rng.standard_normal((n, ho, wo, g, K))
+    a = oracle.dcn_forward(x, off, mask, group=g, softmax=softmax, offset_scale=0.75, **geom)
+    b = oracle.dcn_forward(x, off, mask, group=g, softmax=softmax, offset_scale=0.75, tent=True, **geom)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_offset_scale_scales_the_offset():
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((1, 6, 6, 2))
+    off = rng.normal(0, 1.5, size=(1, 6, 6, 1, 9, 2))
+    mask = rng.standard_normal((1, 6, 6, 1, 9))
+    a = oracle.dcn_forward(x, off, mask, group=1, offset_scale=0.5)
+    b = oracle.dcn_forward(x, off * 0.5, mask, group=1, offset_scale=1.0)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# backward
+
+
+def _tiny_problem(seed, softmax, n=1, h=6, w=7, c=4, g=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, h, w, c))
+    off = rng.normal(0, 1.5, size=(n, h, w, g, 9, 2))
+    mask = rng.standard_normal((n, h, w, g, 9))
+    go = rng.standard_normal((n, h, w, c))
+    return x, off, mask, go, g
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_backward_grad_x_adjoint_identity(softmax):
+    """The op is linear in x, so <g, F(x)> = <F^T g, x> for any x and g."""
+    x, off, mask, go, g = _tiny_problem(23, softmax)
+    y = oracle.dcn_forward(x, off, mask, group=g, softmax=softmax, offset_scale=1.3)
+    gx, _, _ = oracle.dcn_backward(x, off, mask, go, group=g, softmax=softmax, offset_scale=1.3)
+    assert float(np.sum(go * y)) == pytest.approx(float(np.sum(gx * x)), rel=1e-12, abs=1e-12)
+    # and F^T g does not depend on x
+    gx2, _, _ = oracle.dcn_backward(x * 0 + 5.0, off, mask, go, group=g, softmax=softmax, offset_scale=1.3)
+    np.testing.assert_allclose(gx, gx2, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("softmax", [False, True])
+def test_backward_offset_and_mask_by_finite_differences(softmax):
+    x, off, mask, go, g = _tiny_problem(29, softmax)
+    sigma = 1.3
+    _, goff, gmask = oracle.dcn_backward(x, off, mask, go, group=g, softmax=softmax, offset_scale=sigma)
+
+    def loss(o, m):
+        return float(np.sum(go * oracle.dcn_forward(x, o, m, group=g, softmax=softmax, offset_scale=sigma)))
+
+    h = 1e-6
+    rng = np.random.default_rng(31)
+    idx = [tuple(int(rng.integers(0, s)) for s in off.shape) for _ in range(60)]
+    checked = 0
+    for ix in idx:
+        # skip samples whose coordinate sits within 2h of an integer (a kink)
+        yo, xo, kk, comp = ix[1], ix[2], ix[4], ix[5]
+        base = (xo - 1 + kk // 3) if comp == 0 else (yo - 1 + kk % 3)
+        coord = base + sigma * off[ix]
+        if abs(coord - round(coord)) < 4 * h * sigma:
+            continue
+        op, om = off.copy(), off.copy()
+        op[ix] += h
+        om[ix] -= h
+        fd = (loss(op, mask) - loss(om, mask)) / (2 * h)
+        assert goff[ix] == pytest.approx(fd, rel=1e-5, abs=1e-6)
+        checked += 1
+    assert checked > 40
+    for _ in range(30):
+        ix = tuple(int(rng.integers(0, s)) for s in mask.shape)
+        mp, mm = mask.copy(), mask.copy()
+        mp[ix] += h
+        mm[ix] -= h
+        fd = (loss(off, mp) - loss(off, mm)) / (2 * h)
+        assert gmask[ix] == pytest.approx(fd, rel=1e-5, abs=1e-6)
+
+
+def test_backward_dcnv4_grad_mask_is_sampled_value():
+    """Without softmax, dL/dm_k is sum_c g_c times the sampled value v_k,c.
+    The sampled value is read off the forward with a one-hot modulation."""
+    x, off, mask, go, g = _tiny_problem(37, False)
+    _, _, gmask = oracle.dcn_backward(x, off, mask, go, group=g)
+    for k in range(9):
+        onehot = np.zeros_like(mask)
+        onehot[..., k] = 1.0
+        v = oracle.dcn_forward(x, off, onehot, group=g)
+        ref = (go * v).reshape(*go.shape[:3], g, -1).sum(-1)
+        np.testing.assert_allclose(gmask[..., k], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_backward_strided_geometry_adjoint():
+    rng = np.random.default_rng(41)
+    n, h, w, c, g = 2, 7, 8, 6, 3
+    geom = dict(kernel=(3, 2), stride=(2, 1), pad=(1, 0), dil=(1, 2))
+    ho, wo = oracle.dcn_out_size(h, w, **geom)
+    x = rng.standard_normal((n, h, w, c))
+    off = rng.normal(0, 1.5, size=(n, ho, wo, g, 6, 2))
+    mask = rng.standard_normal((n, ho, wo, g, 6))
+    go = rng.standard_normal((n, ho, wo, c))
+    y = oracle.dcn_forward(x, off, mask, group=g, **geom)
+    gx, _, _ = oracle.dcn_backward(x, off, mask, go, group=g, **geom)
+    assert float(np.sum(go * y)) == pytest.approx(float(np.sum(gx * x)), rel=1e-12)
+
+
+# --------------------------------------------------------------------------
+# multi-scale deformable attention
+
+
+def _msda_one(value_rows, uv, logits=None, weights=None):
+    """One image, one query, one head, head_dim 1 over the given levels."""
+    shapes = [np.asarray(v).shape for v in value_rows]
+    value = np.concatenate([np.asarray(v, np.float64).reshape(-1) for v in value_rows]).reshape(1, -1, 1, 1)
+    L = len(shapes)
+    P = len(uv) // L
+    loc = np.asarray(uv, np.float64).reshape(1, 1, 1, L, P, 2)
+    if logits is not None:
+        attn = np.asarray(logits, np.float64).reshape(1, 1, 1, L, P)
+        return oracle.msda_forward(value, shapes, loc, attn, softmax=True)[0, 0, 0, 0]
+    attn = np.asarray(weights, np.float64).reshape(1, 1, 1, L, P)
+    return oracle.msda_forward(value, shapes, loc, attn, softmax=False)[0, 0, 0, 0]
+
+
+def test_msda_corner_case():
+    gd = golden("msda_examples.json")["corner_case"]
+    assert _msda_one([gd["map_rows"]], [gd["uv"]], weights=[1.0]) == gd["value"]
+
+
+def test_msda_pixel_centre_reads_the_pixel():
+    rng = np.random.default_rng(43)
+    H, W = 5, 7
+    grid = rng.standard_normal((H, W))
+    for j in range(H):
+        for i in range(W):
+            uv = [((i + 0.5) / W, (j + 0.5) / H)]
+            assert _msda_one([grid], uv, weights=[1.0]) == pytest.approx(grid[j, i], rel=0, abs=1e-15)
+    # far outside: nothing contributes
+    for uv in ([(-0.6, 0.5)], [(0.5, 1.3)], [(2.0, -3.0)]):
+        assert _msda_one([grid], uv, weights=[1.0]) == 0.0
+
+
+def test_msda_joint_softmax_example():
+    gd = golden("msda_examples.json")["joint_softmax"]
+    # two levels, two points each, equal logits; each point reads a distinct
+    # pixel centre of value 1, 10, 100, 1000
+    lv0 = [[1.0, 10.0]]           # H=1, W=2
+    lv1 = [[100.0], [1000.0]]     # H=2, W=1
+    uv = [(0.25, 0.5), (0.75, 0.5), (0.5, 0.25), (0.5, 0.75)]
+    out = _msda_one([lv0, lv1], uv, logits=[0.3] * 4)
+    w = gd["weight_each"]
+    assert out == pytest.approx(w * (1 + 10 + 100 + 1000), rel=1e-15)
+    # an independent per-level softmax would have total mass 2
+    assert gd["per_level_softmax_total_mass"] * (1 + 10 + 100 + 1000) / 4 != pytest.approx(out)
+
+
+def test_msda_matches_grid_sample_per_level():
+    """The sampler is grid_sample at 2s-1 with align_corners=False and zero
+    padding, per level and head, followed by the weighted sum."""
+    shapes = [(6, 9), (3, 5), (2, 2)]
+    n, Q, M, Dh, P = 2, 11, 3, 4, 2
+    d = synth.msda_inputs(n, shapes, Q, M, Dh, P, seed=3)
+    value = d["value"].astype(np.float64)
+    loc = d["loc"].astype(np.float64)
+    attn = d["attn"].astype(np.float64)
+    out = oracle.msda_forward(value, shapes, loc, attn, softmax=True)
+    L = len(shapes)
+    A = torch.softmax(torch.from_numpy(attn).reshape(n, Q, M, L * P), -1).reshape(n, Q, M, L, P)
+    ref = torch.zeros(n, Q, M, Dh, dtype=torch.float64)
+    start = 0
+    for l, (hh, ww) in enumerate(shapes):
+        v = torch.from_numpy(value[:, start:start + hh * ww]).reshape(n, hh, ww, M, Dh)
+        v = v.permute(0, 3, 4, 1, 2).reshape(n * M, Dh, hh, ww)
+        grid = torch.from_numpy(loc[:, :, :, l]).permute(0, 2, 1, 3, 4).reshape(n * M, Q, P, 2) * 2 - 1
+        s = F.grid_sample(v, grid, mode="bilinear", padding_mode="zeros", align_corners=False)
+        s = s.reshape(n, M, Dh, Q, P).permute(0, 3, 1, 4, 2)  # n, Q, M, P, Dh
+        ref += (s * A[:, :, :, l, :, None]).sum(3)
+        start += hh * ww
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_msda_tent_brute_force_agrees():
+    shapes = [(5, 7), (3, 4)]
+    d = synth.msda_inputs(2, shapes, 9, 2, 3, 3, seed=5)
+    args = (d["value"].astype(np.float64), shapes, d["loc"].astype(np.float64), d["attn"].astype(np.float64))
+    np.testing.assert_allclose(oracle.msda_forward(*args), oracle.msda_forward(*args, tent=True),
+                               rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# the stored-value conversions the oracle reads through
+
+
+def test_bf16_bits_convert_exactly():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3EAA, 0x7F7F], np.uint16)
+    got = oracle.to_f64(bits, "bf16")
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 0.0 and math.copysign(1, got[3]) == -1
+    assert got[4] == float(np.float32(np.uint32(0x3EAA0000).view(np.float32)))
+    assert got[5] == float(np.uint32(0x7F7F0000).view(np.float32))
+    # nearest-even rounding of the stored generator values
+    r = synth.f32_to_bf16_bits(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9], np.float32))
+    assert list(r) == [0x3F80, 0x3F82, 0x3F80]
