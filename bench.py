@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of libdcn on one MI355X.
+
+Headline: DCNv4 forward (no softmax, mask N(0,1) unbounded) at the
+InternImage-T stage-1 shape N=64, H=W=56, C=64, G=4 (16 channels per group),
+3x3 kernel, stride 1, pad 1, in f16 with fp32 accumulation; offsets N(0,1.5).
+A step is one dcn_forward call over the batch.  Inputs are resident in HBM
+before the timed region and rotate over enough copies (>= 1 GB in all) that
+no step finds its inputs in the 256 MB Infinity Cache or the L2s.
+
+Printed: ONE JSON line with the throughput in Gtaps*ch/s (N*Ho*Wo*C*K per
+second), the roofline of the kernel against the minimum-traffic model
+(x read once + offsets + mask + output written once), the CPU oracle's own
+throughput on this host, and secondary figures for the other entry points.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DCN fwd Gtaps*ch/s and achieved HBM GB/s (% of peak), InternImage-T stage-1 shape"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+STAGES = {"stage1": (64, 56, 56, 64, 4), "stage2": (64, 28, 28, 128, 8), "stage3": (64, 14, 14, 320, 20)}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", default=None, help="run only this workload (profiling)")
+    return ap.parse_args()
+
+
+class Runner:
+    """A prepared sequence of launches over rotating copies of one input set."""
+
+    def __init__(self, name, launch_args, fn, units, min_bytes, stream):
+        self.name, self.args, self.fn, self.units, self.min_bytes, self.stream = (
+            name, launch_args, fn, units, min_bytes, stream)
+
+    def launch(self, i):
+        st = self.fn(*self.args[i % len(self.args)])
+        if st != 0:
+            from sparse_deformable_sampling_amd import _binding as B
+            raise B.DcnError(st)
+
+
+def upload(torch, a, dtype):
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float16))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return t.to("cuda")
+
+
+def n_sets(bytes_per_set):
+    return max(2, int(math.ceil(ROTATE_BYTES / bytes_per_set)))
+
+
+def dcn_fwd_runner(torch, stage, dtype, softmax, seed=1):
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, h, w, c, g = STAGES[stage]
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype=dtype, seed=seed)
+    es = ES[dtype]
+    elems = d["x"].size + d["offset"].size + d["mask"].size + n * h * w * c
+    min_bytes = elems * es
+    code = {"f32": B.DCN_F32, "f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, softmax, code)
+    base = [upload(torch, d[k], dtype) for k in ("x", "offset", "mask")]
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        x, off, mask = (t.clone() for t in base) if i else base
+        out = torch.empty((n, h, w, c), dtype=x.dtype, device="cuda")
+        keep += [x, off, mask, out]
+        args.append((ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(off.data_ptr()),
+                     ctypes.c_void_p(mask.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                     ctypes.c_void_p(stream.cuda_stream)))
+    r = Runner("%s_fwd_%s_%s" % ("dcnv3" if softmax else "dcnv4", stage, dtype), args, B.lib().dcn_forward,
+               n * h * w * c * 9, min_bytes, stream)
+    r.keep, r.desc, r.inputs = keep, desc, d
+    return r
+
+
+def dcn_bwd_runner(torch, softmax, seed=1):
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, h, w, c, g = STAGES["stage1"]
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=seed, grad=True)
+    elems = 2 * (d["x"].size + d["offset"].size + d["mask"].size) + d["grad_out"].size
+    min_bytes = elems * 4
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, softmax, B.DCN_F32)
+    base = [upload(torch, d[k], "f32") for k in ("x", "offset", "mask", "grad_out")]
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        ins = [t.clone() for t in base] if i else base
+        outs = [torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])]
+        keep += ins + outs
+        args.append((ctypes.byref(desc),) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + outs) +
+                    (ctypes.c_void_p(stream.cuda_stream),))
+    r = Runner("%s_bwd_stage1_f32" % ("dcnv3" if softmax else "dcnv4"), args, B.lib().dcn_backward,
+               n * h * w * c * 9, min_bytes, stream)
+    r.keep = keep
+    return r
+
+
+MSDA_SHAPES = [(100, 134), (50, 67), (25, 34), (13, 17)]
+
+
+def msda_runner(torch, seed=1):
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, q, heads, dh, pts = 8, 17821, 8, 32, 4
+    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed)
+    min_bytes = 4 * (d["value"].size + d["loc"].size + d["attn"].size + n * q * heads * dh)
+    desc = B.MsdaDesc(n, q, heads, dh, len(MSDA_SHAPES), pts, 1, B.DCN_F32)
+    shapes = (ctypes.c_int32 * 8)(*[v for hw in MSDA_SHAPES for v in hw])
+    base = [upload(torch, d[k], "f32") for k in ("value", "loc", "attn")]
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        ins = [t.clone() for t in base] if i else base
+        out = torch.empty((n, q, heads, dh), device="cuda")
+        keep += ins + [out]
+        args.append((ctypes.byref(desc), shapes) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + [out]) +
+                    (ctypes.c_void_p(stream.cuda_stream),))
+    r = Runner("msda_fwd_encoder_f32", args, B.lib().msda_forward, n * q * heads * dh * len(MSDA_SHAPES) * pts,
+               min_bytes, stream)
+    r.keep = keep
+    return r
+
+
+def time_steps(torch, r, steps, warmup):
+    """Contract timing: warmup, then exactly `steps` launches bracketed by
+    synchronisation.  Returns wall ms per step."""
+    for i in range(warmup):
+        r.launch(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r.launch(warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def kernel_ms(torch, r, steps):
+    """Average launch duration from HIP event pairs recorded on the launch
+    stream around each launch."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(r.stream)
+        r.launch(i)
+        b.record(r.stream)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(d.mean()), float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+
+def summarize(r, ms_step, kms):
+    mean, med, p10, p90 = kms
+    gbs = r.min_bytes / (mean * 1e-3) / 1e9
+    return {"ms_per_step": round(ms_step, 5), "kernel_us_mean": round(mean * 1e3, 2),
+            "kernel_us_median": round(med * 1e3, 2), "kernel_us_p10": round(p10 * 1e3, 2),
+            "kernel_us_p90": round(p90 * 1e3, 2), "min_bytes": int(r.min_bytes),
+            "gtaps_ch_per_s": round(r.units / (ms_step * 1e-3) / 1e9, 2),
+            "achieved_gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baseline(seconds):
+    """The CPU oracle as it stands (single-threaded C, double), timed on this
+    host over whole stage-1 DCNv4 f16 batches until `seconds` have passed."""
+    import oracle
+    from sparse_deformable_sampling_amd import synth
+    n, h, w, c, g = STAGES["stage1"]
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f16", seed=1)
+    oracle.dcn_forward(d["x"][:1], d["offset"][:1], d["mask"][:1], group=g, dtype="f16")  # load/compile
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, dtype="f16")
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    units = runs * n * h * w * c * 9
+    return {"value": round(units / el / 1e9, 4), "unit": "Gtaps*ch/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full batch(es) of the headline workload (N=64 56x56x64 G=4, DCNv4, f16 inputs read "
+                      "as exact doubles) through the single-threaded C oracle, %.1f s" % (runs, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the operator shards "
+              "over the batch with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    from sparse_deformable_sampling_amd import _binding as B
+    B.lib()
+    if args.only:
+        name = args.only
+        if name.startswith("msda"):
+            r = msda_runner(torch)
+        elif "_bwd_" in name:
+            r = dcn_bwd_runner(torch, name.startswith("dcnv3"))
+        else:
+            parts = name.split("_")   # dcnv4_fwd_stage1_f16
+            r = dcn_fwd_runner(torch, parts[2], parts[3], parts[0] == "dcnv3")
+        ms = time_steps(torch, r, args.steps, args.warmup)
+        print(json.dumps({"only": r.name, **summarize(r, ms, kernel_ms(torch, r, args.steps))}), flush=True)
+        return 0
+
+    head = dcn_fwd_runner(torch, "stage1", "f16", False)
+    ms = time_steps(torch, head, args.steps, args.warmup)
+    kms = kernel_ms(torch, head, args.steps)
+    s = summarize(head, ms, kms)
+    print("[bench] headline %s: %s" % (head.name, s), file=sys.stderr, flush=True)
+    del head
+
+    secondary = {}
+    if not args.no_secondary:
+        jobs = [("dcnv4", "stage1", "f32"), ("dcnv4", "stage1", "bf16"), ("dcnv3", "stage1", "f32"),
+                ("dcnv3", "stage1", "f16"), ("dcnv4", "stage2", "f16"), ("dcnv4", "stage2", "bf16"),
+                ("dcnv4", "stage3", "f16"), ("dcnv4", "stage3", "bf16")]
+        for kind, stage, dt in jobs:
+            r = dcn_fwd_runner(torch, stage, dt, kind == "dcnv3")
+            secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
+            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+            del r
+        for softmax in (True, False):
+            r = dcn_bwd_runner(torch, softmax)
+            secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+            del r
+        r = msda_runner(torch)
+        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": s["gtaps_ch_per_s"], "unit": "Gtaps*ch/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": s["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "dcnv4_fwd_stage1_f16", "n": 64, "h": 56, "w": 56, "c": 64, "group": 4,
+                   "kernel": [3, 3], "stride": [1, 1], "pad": [1, 1], "dil": [1, 1], "offset_scale": 1.0,
+                   "softmax": 0, "accumulate": "f32", "x": "N(0,1)", "offsets": "N(0,1.5)", "mask": "N(0,1)",
+                   "rotating_input_sets": n_sets(s["min_bytes"])},
+        "roofline": {"bound": "hbm", "achieved": s["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": s["frac_of_hbm_peak"], "traffic": None,
+                     "kernel": "dcn_fwd (f16, 3x3, DCNv4)", "kernel_us_mean": s["kernel_us_mean"],
+                     "kernel_us_median": s["kernel_us_median"], "algorithmic_bytes_per_launch": s["min_bytes"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,137 @@
+/*
+ * dcn.h -- C ABI of libdcn: deformable sampling-and-aggregation on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operations, cited by web-page title and section:
+ *
+ *  dcn_forward   The DCN core operator.  For every output pixel p0 and channel
+ *                group g:  y_g(p0) = sum_k m_gk * x_g(p0 + p_k + dp_gk)
+ *                ("DCNv4: Unbounded Weights", "Why Is Sampling Just 9 Points
+ *                Still Slow?").  x is read at the fractional point by bilinear
+ *                interpolation with zero outside the map ("InternImage:
+ *                Deformable Convolutions at Scale", Ch.2).  The modulation m
+ *                is softmax-normalised over the K taps (DCNv3, same page Ch.3)
+ *                or used as given (DCNv4, "DCNv4: Unbounded Weights",
+ *                "1. Remove Softmax").  Groups: the C channels split into
+ *                `group` groups of D = C/group channels sharing one set of K
+ *                offsets and K modulations ("InternImage...", Ch.4).
+ *  dcn_backward  Gradients of dcn_forward with respect to x, the offsets and
+ *                the mask (the bilinear read is differentiable almost
+ *                everywhere: "InternImage...", Ch.2, "Why bilinear, and why it
+ *                is differentiable").
+ *  msda_forward  Multi-scale deformable attention sampling core ("Deformable
+ *                DETR: Learn Where to Read", "A learned location can fall
+ *                between cells" and "Mix samples with a per-head budget"):
+ *                per query and head, a softmax over all levels and points
+ *                jointly, a bilinear read of every level at x = u*W_l - 1/2,
+ *                y = v*H_l - 1/2 (zero outside, no clamping), and the
+ *                weighted sum.
+ *
+ * Conventions (the pages leave these open; oracle and kernels hold them alike):
+ *  - Tap k of a kernel_h x kernel_w grid sits at kx = k / kernel_h,
+ *    ky = k % kernel_h (the grid is listed with the y component fastest).
+ *  - Sampling point of tap k at output (ho, wo):
+ *      px = wo*stride_w - pad_w + kx*dil_w + offset_scale*dx
+ *      py = ho*stride_h - pad_h + ky*dil_h + offset_scale*dy
+ *    Output size: ho = (h + 2*pad_h - (dil_h*(kernel_h-1)+1)) / stride_h + 1,
+ *    likewise wo.
+ *  - Accumulation is fp32; an f16/bf16 output is rounded once, to nearest even.
+ *
+ * Layouts (all dense, row-major, no strides):
+ *    x        [n][h][w][c]                       (NHWC)
+ *    offset   [n][ho][wo][group][K][2]           (dx, dy) in pixels, K = kernel_h*kernel_w
+ *    mask     [n][ho][wo][group][K]              logits (softmax=1) or modulation (softmax=0)
+ *    out      [n][ho][wo][c]
+ *    value    [n][S][heads][head_dim]            levels flattened level-major, row-major
+ *                                                within a level; S = sum_l H_l*W_l
+ *    loc      [n][len_q][heads][levels][points][2]   normalised (u, v), u along the width
+ *    attn     [n][len_q][heads][levels][points]      logits (softmax=1) or weights (softmax=0)
+ *    msda out [n][len_q][heads][head_dim]
+ *
+ * Ownership and streams: every tensor pointer is a DEVICE pointer owned by the
+ * caller (except msda_forward's spatial_shapes, a HOST array).  The library
+ * allocates and frees nothing.  `stream` is a hipStream_t (NULL: the null
+ * stream); every call only enqueues work on it and returns, and results are
+ * ready when the stream is.  Calls are thread-safe.
+ *
+ * Errors: no exception crosses the ABI.  Invalid arguments return
+ * DCN_ERR_INVALID before anything is enqueued, leaving outputs untouched;
+ * dcn_last_error() then describes the problem (per thread).
+ */
+#ifndef LIBDCN_DCN_H
+#define LIBDCN_DCN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DCN_OK = 0,
+    DCN_ERR_INVALID = 1,      /* bad argument: NULL, size, shape, flag, dtype, overflow */
+    DCN_ERR_UNSUPPORTED = 2,  /* well-formed but not provided (dtype of an op, alignment, levels) */
+    DCN_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+} dcn_status;
+
+typedef enum { DCN_F32 = 0, DCN_F16 = 1, DCN_BF16 = 2 } dcn_dtype;
+
+typedef struct {
+    int32_t n, h, w, c, group;          /* x is [n][h][w][c]; c % group == 0 */
+    int32_t kernel_h, kernel_w;         /* >= 1 */
+    int32_t stride_h, stride_w;         /* >= 1 */
+    int32_t pad_h, pad_w;               /* >= 0 */
+    int32_t dil_h, dil_w;               /* >= 1 */
+    float offset_scale;                 /* multiplies every offset before it is added; finite */
+    int32_t softmax;                    /* 1: DCNv3 (softmax over K); 0: DCNv4 (as given) */
+    int32_t dtype;                      /* dcn_dtype of x, offset, mask, out and all grads */
+} dcn_desc;
+
+typedef struct {
+    int32_t n, len_q, heads, head_dim, levels, points;   /* all >= 1; levels <= 16 */
+    int32_t softmax;                                     /* 1: attn holds logits */
+    int32_t dtype;                                       /* DCN_F32 only */
+} msda_desc;
+
+/* Output size of dcn_forward for `desc` (ordinary convolution geometry).
+ * Returns DCN_ERR_INVALID if the geometry is invalid or either size < 1. */
+dcn_status dcn_output_size(const dcn_desc* desc, int32_t* h_out, int32_t* w_out);
+
+/* out = DCN core op (see above).  x, offset, mask, out: device pointers,
+ * aligned to the element size, in desc->dtype (f32, f16 or bf16).
+ * Every element count must be below 2^31 and h, w below 2^24.  An offset
+ * whose scaled magnitude reaches 2^24, or that is not finite, places its
+ * sample outside the map (it contributes zero). */
+dcn_status dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                       void* out, void* stream);
+
+/* Gradients of dcn_forward given grad_out ([n][ho][wo][c]).  grad_x
+ * ([n][h][w][c]) is OVERWRITTEN: zero-filled on `stream`, then accumulated
+ * with fp32 atomics, so its low bits depend on the order of the atomics.
+ * grad_offset and grad_mask (same layouts as offset and mask) are overwritten;
+ * with softmax=1 grad_mask is the gradient with respect to the logits passed
+ * in `mask`.  Any of grad_x, grad_offset, grad_mask may be NULL to skip it.
+ * desc->dtype must be DCN_F32 (otherwise DCN_ERR_UNSUPPORTED).  At a sample
+ * coordinate that is exactly an integer the derivative of the cell above the
+ * floor (the right-hand derivative) is returned. */
+dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                        const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                        void* stream);
+
+/* Multi-scale deformable attention sampling core (see above).
+ * spatial_shapes: HOST array [levels][2] = (H_l, W_l), each >= 1.
+ * value, loc, attn, out: device pointers in f32.  Element counts below 2^31. */
+dcn_status msda_forward(const msda_desc* desc, const int32_t* spatial_shapes, const void* value,
+                        const void* loc, const void* attn, void* out, void* stream);
+
+/* Static name of a status code. */
+const char* dcn_status_str(dcn_status status);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* dcn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDCN_DCN_H */

@@ -1,1 +1,133 @@
-"""placeholder"""
+"""libdcn: deformable sampling-and-aggregation on AMD Instinct MI355X (gfx950).
+
+Python face of the C ABI in ``include/dcn.h``.  The functions below carry the
+same names as the C entry points and only marshal arguments: torch supplies
+device memory and the current HIP stream, every step of the computation runs
+in libdcn's HIP kernels.  There is no CPU path: without the built library (or
+without a GPU) the calls raise.
+
+* ``dcn_forward``  -- DCNv3 (``softmax=True``) / DCNv4 (``softmax=False``) core op.
+* ``dcn_backward`` -- its gradients (f32).
+* ``msda_forward`` -- multi-scale deformable attention sampling core (f32).
+* ``dcn_output_size`` -- output spatial size for a geometry.
+
+Layouts: x [n,h,w,c] (NHWC); offset [n,ho,wo,group,K,2] holding (dx, dy);
+mask [n,ho,wo,group,K]; out [n,ho,wo,c]; value [n,S,heads,head_dim];
+loc [n,q,heads,L,P,2] holding normalised (u, v); attn [n,q,heads,L,P].
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _binding as _b
+
+__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "DcnError"]
+
+DcnError = _b.DcnError
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    codes = {torch.float32: _b.DCN_F32, torch.float16: _b.DCN_F16, torch.bfloat16: _b.DCN_BF16}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s (float32, float16 or bfloat16)" % t.dtype)
+    return codes[t.dtype]
+
+
+def _check_tensors(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise RuntimeError("libdcn runs on the GPU only; got a tensor on %s" % dev)
+    for t in ts:
+        if t.device != dev:
+            raise RuntimeError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise RuntimeError("all tensors must be contiguous")
+        if t.dtype != ts[0].dtype:
+            raise RuntimeError("all tensors must share one dtype")
+    return dev
+
+
+def _stream(dev):
+    return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def dcn_output_size(h, w, kernel=3, stride=1, pad=1, dil=1):
+    """(ho, wo) of the DCN op for an h x w input."""
+    return _b.output_size(_b.make_desc(1, h, w, 1, 1, kernel, stride, pad, dil))
+
+
+def _desc_for(x, offset, mask, group, kernel, stride, pad, dil, offset_scale, softmax):
+    if x.dim() != 4:
+        raise ValueError("x must be [n, h, w, c]")
+    n, h, w, c = x.shape
+    desc = _b.make_desc(n, h, w, c, group, kernel, stride, pad, dil, offset_scale, softmax, _dtype_code(x))
+    ho, wo = _b.output_size(desc)
+    K = desc.kernel_h * desc.kernel_w
+    if tuple(offset.shape) != (n, ho, wo, group, K, 2):
+        raise ValueError("offset must be %s, got %s" % ((n, ho, wo, group, K, 2), tuple(offset.shape)))
+    if tuple(mask.shape) != (n, ho, wo, group, K):
+        raise ValueError("mask must be %s, got %s" % ((n, ho, wo, group, K), tuple(mask.shape)))
+    return desc, (n, ho, wo, c)
+
+
+def dcn_forward(x, offset, mask, group, kernel=3, stride=1, pad=1, dil=1, offset_scale=1.0, softmax=False,
+                out=None):
+    """DCN core op on the GPU.  ``softmax=True``: DCNv3 (mask holds logits,
+    softmax over the K taps); ``softmax=False``: DCNv4 (mask used as given)."""
+    dev = _check_tensors(x, offset, mask)
+    desc, oshape = _desc_for(x, offset, mask, group, kernel, stride, pad, dil, offset_scale, softmax)
+    if out is None:
+        out = _torch().empty(oshape, dtype=x.dtype, device=dev)
+    else:
+        _check_tensors(x, out)
+        if tuple(out.shape) != oshape:
+            raise ValueError("out must be %s" % (oshape,))
+    _b.check(_b.lib().dcn_forward(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(out), _stream(dev)))
+    return out
+
+
+def dcn_backward(x, offset, mask, grad_out, group, kernel=3, stride=1, pad=1, dil=1, offset_scale=1.0,
+                 softmax=False, need_x=True, need_offset=True, need_mask=True):
+    """(grad_x, grad_offset, grad_mask) of dcn_forward; an output not needed is None."""
+    dev = _check_tensors(x, offset, mask, grad_out)
+    desc, oshape = _desc_for(x, offset, mask, group, kernel, stride, pad, dil, offset_scale, softmax)
+    if tuple(grad_out.shape) != oshape:
+        raise ValueError("grad_out must be %s" % (oshape,))
+    torch = _torch()
+    gx = torch.empty_like(x) if need_x else None
+    go = torch.empty_like(offset) if need_offset else None
+    gm = torch.empty_like(mask) if need_mask else None
+    _b.check(_b.lib().dcn_backward(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out),
+                                   _ptr(gx), _ptr(go), _ptr(gm), _stream(dev)))
+    return gx, go, gm
+
+
+def msda_forward(value, spatial_shapes, loc, attn, softmax=True, out=None):
+    """Multi-scale deformable attention sampling core on the GPU.
+    spatial_shapes: sequence of (H_l, W_l)."""
+    dev = _check_tensors(value, loc, attn)
+    n, S, M, Dh = value.shape
+    if loc.dim() != 6 or loc.shape[-1] != 2:
+        raise ValueError("loc must be [n, q, heads, L, P, 2]")
+    _, Q, M2, L, P, _ = loc.shape
+    if loc.shape[0] != n or M2 != M or tuple(attn.shape) != (n, Q, M, L, P) or len(spatial_shapes) != L:
+        raise ValueError("inconsistent value/loc/attn/spatial_shapes")
+    shapes = (ctypes.c_int32 * (2 * L))(*[int(v) for hw in spatial_shapes for v in hw])
+    if sum(int(h) * int(w) for h, w in spatial_shapes) != S:
+        raise ValueError("sum of H_l*W_l must equal value.shape[1]")
+    desc = _b.MsdaDesc(n, Q, M, Dh, L, P, int(bool(softmax)), _dtype_code(value))
+    if out is None:
+        out = _torch().empty((n, Q, M, Dh), dtype=value.dtype, device=dev)
+    _b.check(_b.lib().msda_forward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn), _ptr(out),
+                                   _stream(dev)))
+    return out

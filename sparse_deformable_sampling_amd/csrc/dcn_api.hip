@@ -1,0 +1,190 @@
+// C ABI of libdcn (declared in include/dcn.h): argument validation and
+// dispatch to the kernel launchers.  Validation happens entirely on the host
+// before anything is enqueued; on failure no output is touched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/dcn.h"
+#include "dcn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dcn_status fail(dcn_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dcn_status ok()
+{
+    g_last_error[0] = '\0';
+    return DCN_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;   // element counts must stay below 2^31
+constexpr int32_t kMaxSide = 1 << 24;             // h, w below 2^24
+
+size_t elem_size(int32_t dt) { return dt == DCN_F32 ? 4 : 2; }
+
+dcn_status check_ptr(const void* p, const char* name, size_t align)
+{
+    if (!p) return fail(DCN_ERR_INVALID, "%s is NULL", name);
+    if ((uintptr_t)p % align) return fail(DCN_ERR_UNSUPPORTED, "%s is not aligned to %zu bytes", name, align);
+    return DCN_OK;
+}
+
+// Validate a dcn_desc and fill the kernel geometry.
+dcn_status make_geom(const dcn_desc* d, dcn::Geom* G)
+{
+    if (!d) return fail(DCN_ERR_INVALID, "desc is NULL");
+    if (d->n < 1 || d->h < 1 || d->w < 1 || d->c < 1 || d->group < 1)
+        return fail(DCN_ERR_INVALID, "n, h, w, c and group must be >= 1 (got %d, %d, %d, %d, %d)", d->n, d->h, d->w,
+                    d->c, d->group);
+    if (d->c % d->group)
+        return fail(DCN_ERR_INVALID, "c (%d) is not a multiple of group (%d)", d->c, d->group);
+    if (d->kernel_h < 1 || d->kernel_w < 1 || d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1)
+        return fail(DCN_ERR_INVALID, "kernel, stride and dilation must be >= 1");
+    if (d->pad_h < 0 || d->pad_w < 0) return fail(DCN_ERR_INVALID, "padding must be >= 0");
+    if (d->h >= kMaxSide || d->w >= kMaxSide) return fail(DCN_ERR_INVALID, "h and w must be below 2^24");
+    if (d->softmax != 0 && d->softmax != 1) return fail(DCN_ERR_INVALID, "softmax must be 0 or 1");
+    if (d->dtype != DCN_F32 && d->dtype != DCN_F16 && d->dtype != DCN_BF16)
+        return fail(DCN_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (!isfinite(d->offset_scale)) return fail(DCN_ERR_INVALID, "offset_scale must be finite");
+    const int64_t K = (int64_t)d->kernel_h * d->kernel_w;
+    const int64_t eh = (int64_t)d->dil_h * (d->kernel_h - 1) + 1, ew = (int64_t)d->dil_w * (d->kernel_w - 1) + 1;
+    const int64_t hp = (int64_t)d->h + 2 * (int64_t)d->pad_h, wp = (int64_t)d->w + 2 * (int64_t)d->pad_w;
+    if (hp < eh || wp < ew) return fail(DCN_ERR_INVALID, "kernel extent exceeds the padded input");
+    const int64_t ho = (hp - eh) / d->stride_h + 1, wo = (wp - ew) / d->stride_w + 1;
+    if (ho < 1 || wo < 1 || ho >= kMaxSide || wo >= kMaxSide) return fail(DCN_ERR_INVALID, "invalid output size");
+    const int64_t nx = (int64_t)d->n * d->h * d->w * d->c;
+    const int64_t nout = (int64_t)d->n * ho * wo * d->c;
+    const int64_t nmask = (int64_t)d->n * ho * wo * d->group * K;
+    if (nx >= kMaxElems || nout >= kMaxElems || nmask * 2 >= kMaxElems || K >= kMaxElems)
+        return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
+    G->n = d->n; G->h = d->h; G->w = d->w; G->c = d->c; G->g = d->group; G->d = d->c / d->group;
+    G->kh = d->kernel_h; G->kw = d->kernel_w; G->sh = d->stride_h; G->sw = d->stride_w;
+    G->ph = d->pad_h; G->pw = d->pad_w; G->dh = d->dil_h; G->dw = d->dil_w;
+    G->ho = (int)ho; G->wo = (int)wo; G->K = (int)K;
+    G->items = (int)((int64_t)d->n * ho * wo * d->group);
+    G->scale = d->offset_scale;
+    G->softmax = d->softmax;
+    return DCN_OK;
+}
+
+dcn_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return ok();
+    return fail(DCN_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dcn_status_str(dcn_status s)
+{
+    switch (s) {
+        case DCN_OK: return "DCN_OK";
+        case DCN_ERR_INVALID: return "DCN_ERR_INVALID";
+        case DCN_ERR_UNSUPPORTED: return "DCN_ERR_UNSUPPORTED";
+        case DCN_ERR_HIP: return "DCN_ERR_HIP";
+    }
+    return "DCN_UNKNOWN_STATUS";
+}
+
+const char* dcn_last_error(void) { return g_last_error; }
+
+dcn_status dcn_output_size(const dcn_desc* desc, int32_t* h_out, int32_t* w_out)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    if (!h_out || !w_out) return fail(DCN_ERR_INVALID, "h_out/w_out is NULL");
+    *h_out = G.ho;
+    *w_out = G.wo;
+    return ok();
+}
+
+dcn_status dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask, void* out,
+                       void* stream)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    const size_t es = elem_size(desc->dtype);
+    if ((st = check_ptr(x, "x", es)) || (st = check_ptr(offset, "offset", es)) ||
+        (st = check_ptr(mask, "mask", es)) || (st = check_ptr(out, "out", es)))
+        return st;
+    return hip_status(dcn::launch_dcn_forward(G, desc->dtype, x, offset, mask, out, (hipStream_t)stream));
+}
+
+dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                        const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask, void* stream)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    const size_t es = elem_size(desc->dtype);
+    if ((st = check_ptr(x, "x", es)) || (st = check_ptr(offset, "offset", es)) ||
+        (st = check_ptr(mask, "mask", es)) || (st = check_ptr(grad_out, "grad_out", es)))
+        return st;
+    if (grad_x && (uintptr_t)grad_x % es) return fail(DCN_ERR_UNSUPPORTED, "grad_x is not aligned");
+    if (grad_offset && (uintptr_t)grad_offset % es) return fail(DCN_ERR_UNSUPPORTED, "grad_offset is not aligned");
+    if (grad_mask && (uintptr_t)grad_mask % es) return fail(DCN_ERR_UNSUPPORTED, "grad_mask is not aligned");
+    if (desc->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "dcn_backward supports f32 only");
+    if (!grad_x && !grad_offset && !grad_mask) return ok();
+    return hip_status(dcn::launch_dcn_backward(G, (const float*)x, (const float*)offset, (const float*)mask,
+                                               (const float*)grad_out, (float*)grad_x, (float*)grad_offset,
+                                               (float*)grad_mask, (hipStream_t)stream));
+}
+
+dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                        const void* attn, void* out, void* stream)
+{
+    if (!d) return fail(DCN_ERR_INVALID, "desc is NULL");
+    if (d->n < 1 || d->len_q < 1 || d->heads < 1 || d->head_dim < 1 || d->levels < 1 || d->points < 1)
+        return fail(DCN_ERR_INVALID, "n, len_q, heads, head_dim, levels and points must be >= 1");
+    if (d->softmax != 0 && d->softmax != 1) return fail(DCN_ERR_INVALID, "softmax must be 0 or 1");
+    if (d->dtype != DCN_F32 && d->dtype != DCN_F16 && d->dtype != DCN_BF16)
+        return fail(DCN_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (!shapes) return fail(DCN_ERR_INVALID, "spatial_shapes is NULL");
+    if (d->levels > dcn::MSDA_MAX_LEVELS)
+        return fail(DCN_ERR_UNSUPPORTED, "at most %d levels are supported", dcn::MSDA_MAX_LEVELS);
+    dcn::MsdaGeom G;
+    G.n = d->n; G.q = d->len_q; G.m = d->heads; G.dh = d->head_dim; G.L = d->levels; G.P = d->points;
+    G.softmax = d->softmax;
+    int64_t S = 0;
+    for (int l = 0; l < d->levels; ++l) {
+        const int32_t hl = shapes[2 * l], wl = shapes[2 * l + 1];
+        if (hl < 1 || wl < 1 || hl >= kMaxSide || wl >= kMaxSide)
+            return fail(DCN_ERR_INVALID, "level %d has an invalid shape (%d, %d)", l, hl, wl);
+        G.H[l] = hl;
+        G.W[l] = wl;
+        G.start[l] = (int)S;
+        S += (int64_t)hl * wl;
+        if (S >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
+    }
+    const int64_t LP = (int64_t)d->levels * d->points;
+    const int64_t nq = (int64_t)d->n * d->len_q * d->heads;
+    if ((int64_t)d->n * S * d->heads * d->head_dim >= kMaxElems || nq * LP * 2 >= kMaxElems ||
+        nq * d->head_dim >= kMaxElems)
+        return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
+    G.S = (int)S;
+    if (!value || !loc || !attn || !out) return fail(DCN_ERR_INVALID, "value, loc, attn and out must not be NULL");
+    if (d->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "msda_forward supports f32 only");
+    dcn_status st;
+    if ((st = check_ptr(value, "value", 4)) || (st = check_ptr(loc, "loc", 4)) || (st = check_ptr(attn, "attn", 4)) ||
+        (st = check_ptr(out, "out", 4)))
+        return st;
+    return hip_status(dcn::launch_msda_forward(G, (const float*)value, (const float*)loc, (const float*)attn,
+                                               (float*)out, (hipStream_t)stream));
+}
+
+}  // extern "C"

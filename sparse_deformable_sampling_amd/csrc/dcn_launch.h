@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI layer (dcn_api.hip) and the kernel
+// launchers.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dcn {
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Validated DCN geometry, passed to kernels by value.
+struct Geom {
+    int n, h, w, c, g, d;           // d = c / g
+    int kh, kw, sh, sw, ph, pw, dh, dw;
+    int ho, wo, K;                  // K = kh * kw
+    int items;                      // n * ho * wo * g  (one item = one (pixel, group))
+    float scale;                    // offset_scale
+    int softmax;
+};
+
+constexpr int MSDA_MAX_LEVELS = 16;
+
+struct MsdaGeom {
+    int n, q, m, dh, L, P;          // batch, queries, heads, head dim, levels, points
+    int S;                          // sum of H_l * W_l
+    int softmax;
+    int H[MSDA_MAX_LEVELS], W[MSDA_MAX_LEVELS], start[MSDA_MAX_LEVELS];
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_dcn_forward(const Geom& g, int dtype, const void* x, const void* off, const void* mask,
+                              void* out, hipStream_t s);
+hipError_t launch_dcn_backward(const Geom& g, const float* x, const float* off, const float* mask,
+                               const float* gout, float* gx, float* goff, float* gmask, hipStream_t s);
+hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
+                               float* out, hipStream_t s);
+
+}  // namespace dcn

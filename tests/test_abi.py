@@ -1,0 +1,154 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol that
+include/dcn.h declares, computes output sizes like the oracle, and rejects
+invalid arguments before touching the GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from sparse_deformable_sampling_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dcn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:dcn_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    # exported as C symbols (no C++ mangling)
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_struct_layouts_match_header():
+    # the header's structs are all 4-byte fields
+    assert ctypes.sizeof(B.DcnDesc) == 16 * 4
+    assert ctypes.sizeof(B.MsdaDesc) == 8 * 4
+
+
+def test_status_strings():
+    L = B.lib()
+    assert L.dcn_status_str(0) == b"DCN_OK"
+    assert L.dcn_status_str(1) == b"DCN_ERR_INVALID"
+    assert L.dcn_status_str(2) == b"DCN_ERR_UNSUPPORTED"
+    assert L.dcn_status_str(3) == b"DCN_ERR_HIP"
+
+
+@pytest.mark.parametrize("h,w,kernel,stride,pad,dil", [
+    (56, 56, 3, 1, 1, 1), (8, 8, 3, 1, 1, 1), (7, 9, (3, 2), (2, 1), (1, 2), (1, 2)),
+    (28, 28, 3, 2, 1, 1), (5, 6, (1, 1), 1, 0, 1), (13, 17, (2, 3), (1, 2), (2, 0), (3, 1)),
+    (1, 1, 3, 1, 1, 1), (3, 100, (3, 5), (1, 4), (0, 2), (1, 3))])
+def test_output_size_matches_oracle(h, w, kernel, stride, pad, dil):
+    d = B.make_desc(2, h, w, 8, 2, kernel, stride, pad, dil)
+    assert B.output_size(d) == oracle.dcn_out_size(h, w, kernel, stride, pad, dil)
+
+
+def _call_forward(desc, ptrs=(0x1000, 0x2000, 0x3000, 0x4000)):
+    L = B.lib()
+    p = [ctypes.c_void_p(v) if v else None for v in ptrs]
+    return L.dcn_forward(ctypes.byref(desc) if desc is not None else None, *p, None)
+
+
+BAD_DESCS = [
+    dict(c=10, group=4),          # c % group
+    dict(n=0), dict(h=0), dict(w=-1), dict(c=0), dict(group=0),
+    dict(kernel=(0, 3)), dict(stride=(1, 0)), dict(dil=(0, 1)), dict(pad=(-1, 0)),
+    dict(h=2, w=2, kernel=5, pad=0),          # kernel larger than the padded input
+    dict(softmax=2), dict(dtype=7),
+    dict(offset_scale=float("inf")), dict(offset_scale=float("nan")),
+    dict(n=4096, h=1024, w=1024, c=1),        # 2^32 elements
+    dict(h=1 << 24, w=1, c=1, group=1),       # side >= 2^24
+]
+
+
+@pytest.mark.parametrize("bad", BAD_DESCS)
+def test_forward_rejects_invalid_descriptors(bad):
+    kw = dict(n=1, h=8, w=8, c=16, group=2, kernel=3, stride=1, pad=1, dil=1)
+    kw.update(bad)
+    dtype = kw.pop("dtype", B.DCN_F32)
+    softmax = kw.pop("softmax", 0)
+    scale = kw.pop("offset_scale", 1.0)
+    desc = B.make_desc(**kw, offset_scale=scale, dtype=dtype)
+    desc.softmax = softmax
+    st = _call_forward(desc)
+    assert st == B.DCN_ERR_INVALID, B.lib().dcn_last_error()
+    assert B.lib().dcn_last_error() != b""
+
+
+def test_forward_rejects_null_pointers_and_desc():
+    desc = B.make_desc(1, 8, 8, 16, 2)
+    assert _call_forward(None) == B.DCN_ERR_INVALID
+    for i in range(4):
+        ptrs = [0x1000, 0x2000, 0x3000, 0x4000]
+        ptrs[i] = 0
+        assert _call_forward(desc, ptrs) == B.DCN_ERR_INVALID
+
+
+def test_forward_rejects_misaligned_pointers():
+    desc = B.make_desc(1, 8, 8, 16, 2)
+    assert _call_forward(desc, (0x1002, 0x2000, 0x3000, 0x4000)) == B.DCN_ERR_UNSUPPORTED
+    desc.dtype = B.DCN_F16
+    assert _call_forward(desc, (0x1001, 0x2000, 0x3000, 0x4000)) == B.DCN_ERR_UNSUPPORTED
+
+
+def test_backward_rejects_half_precision_and_nulls():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_F16)
+    st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), None,
+                        None, None)
+    assert st == B.DCN_ERR_UNSUPPORTED
+    desc = B.make_desc(1, 8, 8, 16, 2)
+    st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), None, vp(0x4000), vp(0x5000), None, None, None)
+    assert st == B.DCN_ERR_INVALID
+    # nothing requested: a valid no-op, no launch
+    st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), None, None, None, None)
+    assert st == B.DCN_OK
+
+
+def test_msda_validation():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    shapes = (ctypes.c_int32 * 4)(4, 5, 2, 3)
+    ok = dict(n=1, len_q=3, heads=2, head_dim=8, levels=2, points=2, softmax=1, dtype=B.DCN_F32)
+
+    def call(shp=shapes, ptrs=(0x1000, 0x2000, 0x3000, 0x4000), **over):
+        d = dict(ok)
+        d.update(over)
+        desc = B.MsdaDesc(**d)
+        return L.msda_forward(ctypes.byref(desc), shp, *[vp(p) if p else None for p in ptrs], None)
+
+    assert call(levels=0) == B.DCN_ERR_INVALID
+    assert call(points=0) == B.DCN_ERR_INVALID
+    assert call(softmax=3) == B.DCN_ERR_INVALID
+    assert call(dtype=9) == B.DCN_ERR_INVALID
+    assert call(shp=None) == B.DCN_ERR_INVALID
+    assert call(shp=(ctypes.c_int32 * 4)(4, 0, 2, 3)) == B.DCN_ERR_INVALID
+    assert call(ptrs=(0x1000, 0, 0x3000, 0x4000)) == B.DCN_ERR_INVALID
+    assert call(levels=17, shp=(ctypes.c_int32 * 34)(*([2] * 34))) == B.DCN_ERR_UNSUPPORTED
+    assert call(dtype=B.DCN_F16) == B.DCN_ERR_UNSUPPORTED
+    assert call(ptrs=(0x1002, 0x2000, 0x3000, 0x4000)) == B.DCN_ERR_UNSUPPORTED
+    assert call(n=1 << 20, len_q=1 << 12) == B.DCN_ERR_INVALID
+
+
+def test_torch_wrappers_refuse_cpu_tensors():
+    import torch
+    import sparse_deformable_sampling_amd as sds
+    x = torch.zeros(1, 4, 4, 4)
+    off = torch.zeros(1, 4, 4, 1, 9, 2)
+    mask = torch.zeros(1, 4, 4, 1, 9)
+    with pytest.raises(RuntimeError, match="GPU"):
+        sds.dcn_forward(x, off, mask, group=1)

@@ -1,0 +1,314 @@
+"""GPU parity: libdcn's HIP kernels against the CPU oracle, element by
+element, on the same seeded inputs, at the workloads' full sizes and on edge
+cases.  Bar: err <= 1e-5 for f32, <= 2e-2 for f16/bf16 (fp32 accumulation),
+with err as defined in parity_util.rel_err."""
+import numpy as np
+import pytest
+
+import oracle
+from parity_util import TOL, rel_err, say, to_dev, to_host
+from sparse_deformable_sampling_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sds():
+    import torch
+    import sparse_deformable_sampling_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def run_fwd(sds, d, dtype, group, softmax, **geom):
+    x, off, mask = (to_dev(d[k], dtype) for k in ("x", "offset", "mask"))
+    out = sds.dcn_forward(x, off, mask, group=group, softmax=softmax, **geom)
+    return to_host(out)
+
+
+def check_fwd(sds, name, n, h, w, c, g, dtype, softmax, offset=("normal", 1.5), seed=1, **geom):
+    ho, wo = oracle.dcn_out_size(h, w, geom.get("kernel", 3), geom.get("stride", 1), geom.get("pad", 1),
+                                 geom.get("dil", 1))
+    assert sds.dcn_output_size(h, w, geom.get("kernel", 3), geom.get("stride", 1), geom.get("pad", 1),
+                               geom.get("dil", 1)) == (ho, wo)
+    kern = geom.get("kernel", 3)
+    K = kern * kern if isinstance(kern, int) else kern[0] * kern[1]
+    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, offset=offset, dtype=dtype, seed=seed)
+    say(name, dtype, "softmax=%d" % softmax, (n, h, w, c, g), geom)
+    got = run_fwd(sds, d, dtype, g, softmax, **geom)
+    ref = oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, softmax=softmax, dtype=dtype, **geom)
+    err = rel_err(got, ref)
+    assert err <= TOL[dtype], (name, dtype, softmax, err)
+    return err
+
+
+# ---------------------------------------------------------------- forward
+
+
+def test_dcnv3_tiny_f32(sds):
+    """N=1 H=W=8 C=16 G=2, offsets U(-2,2), logits N(0,1) with softmax."""
+    check_fwd(sds, "dcnv3-tiny", 1, 8, 8, 16, 2, "f32", True, offset=("uniform", -2.0, 2.0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("softmax", [True, False])
+def test_stage1_forward_full(sds, dtype, softmax):
+    """InternImage-T stage-1 shape N=64 H=W=56 C=64 G=4, offsets N(0,1.5)."""
+    check_fwd(sds, "stage1", 64, 56, 56, 64, 4, dtype, softmax)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("stage", ["stage2", "stage3"])
+def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
+    n, hw, c, g = {"stage2": (64, 28, 128, 8), "stage3": (64, 14, 320, 20)}[stage]
+    check_fwd(sds, stage, n, hw, hw, c, g, dtype, False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("c,g", [(4, 4), (12, 4), (15, 3), (16, 2), (32, 1), (64, 1), (256, 2), (24, 3)])
+def test_channel_splits(sds, dtype, c, g):
+    """Every D = C/G path: one channel, odd D, D not a multiple of the vector
+    width, vector widths exactly, several vectors per item."""
+    for softmax in (False, True):
+        check_fwd(sds, "split", 2, 9, 11, c, g, dtype, softmax, seed=3)
+
+
+@pytest.mark.parametrize("geom", [dict(kernel=(3, 2), stride=(2, 1), pad=(1, 2), dil=(1, 2)),
+                                  dict(kernel=1, stride=1, pad=0, dil=1),
+                                  dict(kernel=5, stride=2, pad=2, dil=1),
+                                  dict(kernel=3, stride=1, pad=0, dil=3),
+                                  dict(kernel=(1, 7), stride=(1, 3), pad=(0, 3), dil=1),
+                                  dict(kernel=3, stride=3, pad=1, dil=1)])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_geometries(sds, geom, dtype):
+    for softmax in (False, True):
+        check_fwd(sds, "geom", 2, 13, 10, 16, 2, dtype, softmax, seed=5, **geom)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_and_tiny_maps(sds, dtype):
+    for (n, h, w) in [(1, 1, 1), (3, 1, 7), (1, 5, 1), (5, 3, 3), (7, 13, 17)]:
+        check_fwd(sds, "ragged", n, h, w, 16, 2, dtype, False, seed=7)
+        check_fwd(sds, "ragged", n, h, w, 16, 2, dtype, True, seed=7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_offsets_far_outside_and_non_finite(sds, dtype):
+    n, h, w, c, g = 2, 8, 9, 16, 2
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=11)
+    off = d["offset"].copy()
+    rng = np.random.default_rng(0)
+    pick = rng.random(off.shape) < 0.1
+    off[pick] = rng.choice([1e6, -1e6, 3e4, -40.0, 8.5, -9.25], size=int(pick.sum()))
+    off[0, 0, 0, 0, 0, 0] = np.inf
+    off[0, 1, 1, 1, 3, 1] = -np.inf
+    off[1, 2, 2, 0, 4, 0] = np.nan
+    off[1, 3, 3, 1, 8, :] = [-1.0, -1.0]       # exactly on the edge
+    d["offset"] = synth.store(off, dtype)
+    d["x"] = synth.store(d["x"], dtype)
+    d["mask"] = synth.store(d["mask"], dtype)
+    for softmax in (False, True):
+        say("outside", dtype, softmax)
+        got = run_fwd(sds, d, dtype, g, softmax)
+        ref = oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, softmax=softmax, dtype=dtype)
+        assert np.isfinite(got).all()
+        assert rel_err(got, ref) <= TOL[dtype]
+
+
+def test_integer_offsets_bit_exact(sds):
+    """One-hot DCNv4 modulation and integer offsets copy pixels exactly."""
+    import torch
+    n, h, w, c, g = 2, 10, 12, 32, 2
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((n, h, w, c)).astype(np.float32)
+    off = rng.integers(-4, 5, size=(n, h, w, g, 9, 2)).astype(np.float32)
+    mask = np.zeros((n, h, w, g, 9), np.float32)
+    mask[..., 5] = 1.0
+    say("integer-shift")
+    got = to_host(sds.dcn_forward(to_dev(x, "f32"), to_dev(off, "f32"), to_dev(mask, "f32"), group=g))
+    ref = oracle.dcn_forward(x, off, mask, group=g)
+    assert np.array_equal(got, ref)
+    torch.cuda.synchronize()
+
+
+def test_unaligned_views_take_the_scalar_path(sds):
+    """Tensors that start one element into an allocation are valid input."""
+    import torch
+    n, h, w, c, g = 2, 7, 6, 16, 2
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=17)
+    def shifted(a):
+        t = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        v = t[1:].view(a.shape)
+        v.copy_(torch.from_numpy(a))
+        return v
+    x, off, mask = shifted(d["x"]), shifted(d["offset"]), shifted(d["mask"])
+    out = torch.empty(n * h * w * c + 1, device="cuda")[1:].view(n, h, w, c)
+    say("unaligned")
+    sds.dcn_forward(x, off, mask, group=g, out=out)
+    ref = oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g)
+    assert rel_err(to_host(out), ref) <= TOL["f32"]
+
+
+def test_forward_is_deterministic(sds):
+    import torch
+    d = synth.dcn_inputs(8, 56, 56, 64, 4, (56, 56), dtype="f16", seed=19)
+    x, off, mask = (to_dev(d[k], "f16") for k in ("x", "offset", "mask"))
+    say("determinism")
+    a = sds.dcn_forward(x, off, mask, group=4)
+    b = sds.dcn_forward(x, off, mask, group=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_invalid_call_leaves_output_untouched(sds):
+    import torch
+    from sparse_deformable_sampling_amd import _binding as B
+    import ctypes
+    x = torch.randn(1, 8, 8, 16, device="cuda")
+    off = torch.zeros(1, 8, 8, 2, 9, 2, device="cuda")
+    mask = torch.zeros(1, 8, 8, 2, 9, device="cuda")
+    out = torch.full((1, 8, 8, 16), 7.0, device="cuda")
+    desc = B.make_desc(1, 8, 8, 16, 3)   # 16 % 3 != 0
+    st = B.lib().dcn_forward(ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(off.data_ptr()),
+                             ctypes.c_void_p(mask.data_ptr()), ctypes.c_void_p(out.data_ptr()), None)
+    torch.cuda.synchronize()
+    assert st == B.DCN_ERR_INVALID
+    assert bool((out == 7.0).all())
+    with pytest.raises(B.DcnError):
+        sds.dcn_forward(x, off[:, :, :, :1], mask[:, :, :, :1], group=3)
+
+
+# ---------------------------------------------------------------- backward
+
+
+def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=TOL["f32"], **geom):
+    kern = geom.get("kernel", 3)
+    K = kern * kern if isinstance(kern, int) else kern[0] * kern[1]
+    ho, wo = oracle.dcn_out_size(h, w, kern, geom.get("stride", 1), geom.get("pad", 1), geom.get("dil", 1))
+    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, dtype="f32", seed=seed, grad=True)
+    x, off, mask, go = (to_dev(d[k], "f32") for k in ("x", "offset", "mask", "grad_out"))
+    say(name, "softmax=%d" % softmax, (n, h, w, c, g), geom)
+    gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=g, softmax=softmax, **geom)
+    rx, roff, rm = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=g, softmax=softmax,
+                                       **geom)
+    errs = (rel_err(to_host(gx), rx), rel_err(to_host(goff), roff), rel_err(to_host(gm), rm))
+    assert max(errs) <= tol, (name, softmax, errs)
+    return errs
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_backward_stage1_full(sds, softmax):
+    """DCNv3 and DCNv4 backward, f32, N=64 H=W=56 C=64 G=4, grad_out N(0,1)."""
+    check_bwd(sds, "bwd-stage1", 64, 56, 56, 64, 4, softmax)
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_backward_crop_against_finite_differences(sds, softmax):
+    """The 8x8 top-left crop of image 0 of the stage-1 inputs, as its own
+    problem: GPU gradients against central differences of the oracle
+    forward (double precision)."""
+    d = synth.dcn_inputs(1, 56, 56, 64, 4, (56, 56), dtype="f32", seed=1, grad=True)
+    x = np.ascontiguousarray(d["x"][:, :8, :8])
+    off = np.ascontiguousarray(d["offset"][:, :8, :8])
+    mask = np.ascontiguousarray(d["mask"][:, :8, :8])
+    go = np.ascontiguousarray(d["grad_out"][:, :8, :8])
+    say("bwd-crop-fd", softmax)
+    gx, goff, gm = sds.dcn_backward(to_dev(x, "f32"), to_dev(off, "f32"), to_dev(mask, "f32"), to_dev(go, "f32"),
+                                    group=4, softmax=softmax)
+    gx, goff, gm = to_host(gx), to_host(goff), to_host(gm)
+    rx, roff, rm = oracle.dcn_backward(x, off, mask, go, group=4, softmax=softmax)
+    assert max(rel_err(gx, rx), rel_err(goff, roff), rel_err(gm, rm)) <= TOL["f32"]
+
+    x64, off64, m64, go64 = (a.astype(np.float64) for a in (x, off, mask, go))
+
+    def loss(xx, oo, mm):
+        return float(np.sum(go64 * oracle.dcn_forward(xx, oo, mm, group=4, softmax=softmax)))
+
+    h = 1e-6
+    rng = np.random.default_rng(23)
+    checked = 0
+    for _ in range(40):
+        ix = tuple(int(rng.integers(0, s)) for s in off.shape)
+        yo, xo, kk, comp = ix[1], ix[2], ix[4], ix[5]
+        coord = (xo - 1 + kk // 3 if comp == 0 else yo - 1 + kk % 3) + off64[ix]
+        if abs(coord - round(coord)) < 1e-4:
+            continue
+        a, b = off64.copy(), off64.copy()
+        a[ix] += h
+        b[ix] -= h
+        fd = (loss(x64, a, m64) - loss(x64, b, m64)) / (2 * h)
+        assert goff[ix] == pytest.approx(fd, rel=1e-4, abs=1e-4)
+        checked += 1
+    assert checked >= 30
+    for _ in range(20):
+        ix = tuple(int(rng.integers(0, s)) for s in mask.shape)
+        a, b = m64.copy(), m64.copy()
+        a[ix] += h
+        b[ix] -= h
+        fd = (loss(x64, off64, a) - loss(x64, off64, b)) / (2 * h)
+        assert gm[ix] == pytest.approx(fd, rel=1e-4, abs=1e-4)
+    for _ in range(20):
+        ix = tuple(int(rng.integers(0, s)) for s in x.shape)
+        a, b = x64.copy(), x64.copy()
+        a[ix] += h
+        b[ix] -= h
+        fd = (loss(a, off64, m64) - loss(b, off64, m64)) / (2 * h)
+        assert gx[ix] == pytest.approx(fd, rel=1e-4, abs=1e-4)
+
+
+@pytest.mark.parametrize("c,g", [(16, 4), (12, 4), (15, 3), (32, 1), (256, 2), (8, 8), (48, 2)])
+def test_backward_channel_splits(sds, c, g):
+    for softmax in (False, True):
+        check_bwd(sds, "bwd-split", 2, 9, 11, c, g, softmax, seed=29)
+
+
+@pytest.mark.parametrize("geom", [dict(kernel=(3, 2), stride=(2, 1), pad=(1, 2), dil=(1, 2)),
+                                  dict(kernel=5, stride=2, pad=2, dil=1),
+                                  dict(kernel=1, stride=1, pad=0, dil=1)])
+def test_backward_geometries(sds, geom):
+    for softmax in (False, True):
+        check_bwd(sds, "bwd-geom", 2, 13, 10, 16, 2, softmax, seed=31, **geom)
+
+
+def test_backward_partial_outputs(sds):
+    d = synth.dcn_inputs(2, 9, 9, 16, 2, (9, 9), dtype="f32", seed=37, grad=True)
+    x, off, mask, go = (to_dev(d[k], "f32") for k in ("x", "offset", "mask", "grad_out"))
+    say("bwd-partial")
+    rx, roff, rm = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=2)
+    gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=2, need_x=False)
+    assert gx is None and rel_err(to_host(goff), roff) <= 1e-5 and rel_err(to_host(gm), rm) <= 1e-5
+    gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=2, need_offset=False, need_mask=False)
+    assert goff is None and gm is None and rel_err(to_host(gx), rx) <= 1e-5
+
+
+# ---------------------------------------------------------------- MSDA
+
+ENCODER_SHAPES = [(100, 134), (50, 67), (25, 34), (13, 17)]
+
+
+def check_msda(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0):
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed)
+    v, loc, attn = (to_dev(d[k], "f32") for k in ("value", "loc", "attn"))
+    say(name, (n, shapes, q, heads, dh, points), softmax)
+    got = to_host(sds.msda_forward(v, shapes, loc, attn, softmax=softmax))
+    ref = oracle.msda_forward(d["value"], shapes, d["loc"], d["attn"], softmax=softmax)
+    err = rel_err(got, ref)
+    assert err <= TOL["f32"], (name, err)
+    return err
+
+
+def test_msda_encoder_full(sds):
+    """Batch 8, 4 levels (100x134 .. 13x17), all 17821 positions as queries,
+    8 heads x 32, 4 points per level, joint softmax over 16."""
+    check_msda(sds, "msda-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4)
+
+
+@pytest.mark.parametrize("dh", [1, 3, 4, 8, 32, 64, 36])
+def test_msda_head_dims(sds, dh):
+    check_msda(sds, "msda-dh", 2, [(7, 9), (4, 5)], 23, 3, dh, 3, seed=41)
+
+
+@pytest.mark.parametrize("shapes,points", [([(1, 1)], 1), ([(5, 3)], 8), ([(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 2)])
+def test_msda_levels_points(sds, shapes, points):
+    for softmax in (True, False):
+        check_msda(sds, "msda-lp", 2, shapes, 17, 2, 8, points, softmax=softmax, seed=43, offset_std=4.0)
