@@ -15,6 +15,7 @@
 // reads are 16-byte vector loads along the NHWC channel axis; accumulation is
 // fp32; there are no atomics (each output element has exactly one writer).
 #include "dcn_device.h"
+#include "dcn_ring.h"
 
 namespace dcn {
 
@@ -293,6 +294,11 @@ hipError_t launch_typed(const Geom& G, const void* x, const void* off, const voi
 hipError_t launch_dcn_forward(const Geom& G, int dtype, const void* x, const void* off, const void* mask, void* out,
                               hipStream_t s)
 {
+    int lds_limit, num_cus;
+    device_limits(&lds_limit, &num_cus);
+    RingCfg rc;
+    if (plan_ring(G, dtype, x, off, mask, out, lds_limit, num_cus, &rc))
+        return launch_dcn_forward_ring(G, rc, dtype, x, off, mask, out, s);
     switch (dtype * 2 + (G.softmax ? 1 : 0)) {
         case DT_F32 * 2 + 0: return launch_typed<DT_F32, false>(G, x, off, mask, out, s);
         case DT_F32 * 2 + 1: return launch_typed<DT_F32, true>(G, x, off, mask, out, s);

@@ -115,6 +115,24 @@ def test_offsets_far_outside_and_non_finite(sds, dtype):
         assert rel_err(got, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("std", [4.0, 12.0])
+def test_wide_offsets_stage1(sds, dtype, std):
+    """Offsets wide enough that many samples leave any row window kept
+    on chip: every read path of the kernel, at the stage-1 shape."""
+    for softmax in (False, True):
+        check_fwd(sds, "wide-offsets", 16, 56, 56, 64, 4, dtype, softmax, offset=("normal", std), seed=23)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 40, 9, 32, 2), (2, 7, 130, 16, 1), (5, 23, 5, 48, 3), (1, 3, 3, 64, 8)])
+def test_tall_wide_and_short_maps(sds, dtype, shape):
+    n, h, w, c, g = shape
+    for softmax in (False, True):
+        for geom in (dict(), dict(stride=2), dict(dil=2, pad=2)):
+            check_fwd(sds, "shape", n, h, w, c, g, dtype, softmax, seed=29, **geom)
+
+
 def test_integer_offsets_bit_exact(sds):
     """One-hot DCNv4 modulation and integer offsets copy pixels exactly."""
     import torch
@@ -175,7 +193,7 @@ def test_invalid_call_leaves_output_untouched(sds):
     assert st == B.DCN_ERR_INVALID
     assert bool((out == 7.0).all())
     with pytest.raises(B.DcnError):
-        sds.dcn_forward(x, off[:, :, :, :1], mask[:, :, :, :1], group=3)
+        sds.dcn_forward(x, off[:, :, :, :1].contiguous(), mask[:, :, :, :1].contiguous(), group=3)
 
 
 # ---------------------------------------------------------------- backward
