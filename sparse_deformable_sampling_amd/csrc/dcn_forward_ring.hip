@@ -7,23 +7,24 @@
 //
 // Why a different kernel: on gfx950 a scattered 16-32 byte read through the
 // vector L1 costs about one cache-line lookup (~2.3 clocks per line per CU),
-// so gathering 36 corners per output from L1 runs far below HBM speed.  The
-// LDS serves the same random 16-byte reads 6x faster.  Each workgroup
-// therefore owns one image and a chunk of output rows, keeps a ring of input
-// rows (all channels, one zero column on each side) in LDS, and walks down
-// the chunk TR output rows per step:
-//   - the window of input rows a step can touch without leaving the ring is
-//     [lo, lo + NW): the rows the 3x3 footprint reaches plus HY halo rows
-//     above and below for the learned offsets;
-//   - while a step computes, the rows the next step adds and the next step's
-//     offsets and mask are already in flight to registers, then written to
-//     LDS before the step's closing barrier;
-//   - a sample whose two rows fall outside the window but touch the image is
-//     rare (|dy| > HY); it is skipped in the LDS pass and read with global
-//     loads in a tail pass by the lanes that need it.
-// Lane = one (output pixel, group) item holding all D channels, so the tap
+// so gathering 36 corners per output from L1 runs far below HBM speed; the
+// LDS serves random 16-byte reads several times faster.  Each workgroup
+// therefore owns one image, a set of GS channel groups and a chunk of output
+// rows.  It keeps a ring of input rows of those groups in LDS (one zero
+// column on each side, plus a mirror of slot 0 after the last slot so the row
+// below any slot is the next slot in memory) and walks down the chunk TR
+// output rows per step:
+//   - the rows a step may read through LDS form the window [lo, lo + NW): the
+//     3x3 footprint of its output rows plus HY halo rows above and below for
+//     the learned offsets;
+//   - while a step computes, buffer-to-LDS loads bring in the rows the next
+//     step adds and the next step's offsets and mask, with no VGPR round trip;
+//   - a sample whose two rows fall outside the window (|dy| > HY) is given
+//     zero weight in the LDS pass and read with global loads in a tail pass by
+//     the lanes that need it.
+// Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
-// accumulation; stores are 16-byte vectors, one writer per element.
+// accumulation; 16-byte vector stores, one writer per output element.
 #include "dcn_device.h"
 #include "dcn_ring.h"
 
@@ -32,6 +33,8 @@ namespace dcn {
 namespace {
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past any accepted tensor: reads as zero
+constexpr int ROW_IT = 4;               // per-thread 16-byte chunks of one input row
+constexpr int ST_IT = 8;                // per-thread 16-byte chunks of one step's offsets (and of its mask)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -40,60 +43,58 @@ __device__ __forceinline__ u32x4 lds_ld16(const unsigned char* base, uint32_t of
     return *reinterpret_cast<const u32x4*>(base + off);
 }
 
+// acc[0..V) += w * (16 bytes of x in the storage type)
 template <int DT>
 __device__ __forceinline__ void fma16(float* acc, float w, u32x4 r)
 {
     const uint32_t q[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (DT == DT_F32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (DT == DT_F16) {
-            acc[2 * i] = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] & 0xffffu)), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] >> 16)), acc[2 * i + 1]);
-        } else {
-            acc[2 * i] = fmaf(w, __uint_as_float(q[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(w, __uint_as_float(q[i] & 0xffff0000u), acc[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, __uint_as_float(q[i]), acc[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == DT_F16) {
+                acc[2 * i] = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] & 0xffffu)), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] >> 16)), acc[2 * i + 1]);
+            } else {
+                acc[2 * i] = fmaf(w, __uint_as_float(q[i] << 16), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(w, __uint_as_float(q[i] & 0xffff0000u), acc[2 * i + 1]);
+            }
         }
     }
 }
 
 template <int DT>
-__device__ __forceinline__ float half_lo(uint32_t p)
+__device__ __forceinline__ float h2f(uint32_t h16)
 {
-    if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu));
-    return __uint_as_float(p << 16);
-}
-template <int DT>
-__device__ __forceinline__ float half_hi(uint32_t p)
-{
-    if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
-    return __uint_as_float(p & 0xffff0000u);
+    if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+    return __uint_as_float(h16 << 16);
 }
 
-// One wave copies `bytes` (a multiple of 16) from a buffer into LDS at
-// `dst`, 1 KB per instruction: lane l of the wave lands at dst + c + 16*l.
-// `src` == OOB copies zeros.  The wave's share is every nwaves-th kilobyte.
+// One wave copies `bytes` (a multiple of 16) of a buffer into LDS at `dst`,
+// 1 KB per instruction: lane l of the wave lands at dst + c + 16*l.
 __device__ __forceinline__ void wave_copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t src, unsigned char* dst,
                                                  uint32_t bytes, int wave, int nwaves, int lane)
 {
     for (uint32_t c = (uint32_t)wave * 1024u; c < bytes; c += (uint32_t)nwaves * 1024u) {
         const uint32_t o = c + 16u * lane;
-        if (o < bytes)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + c), 16, src == OOB ? OOB : src + o, 0, 0, 0);
+        if (o < bytes) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + c), 16, src + o, 0, 0, 0);
     }
 }
 
 template <int DT, int KH, int KW, bool SOFTMAX, int NCH>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dcn_fwd_ring(Geom G, RingCfg rc, const typename Elem<DT>::T* __restrict__ x,
-                                                    const typename Elem<DT>::T* __restrict__ off,
-                                                    const typename Elem<DT>::T* __restrict__ mask,
-                                                    typename Elem<DT>::T* __restrict__ out)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dcn_fwd_ring(
+    Geom G, RingCfg rc, const typename Elem<DT>::T* __restrict__ x, const typename Elem<DT>::T* __restrict__ off,
+    const typename Elem<DT>::T* __restrict__ mask, typename Elem<DT>::T* __restrict__ out)
 {
     using T = typename Elem<DT>::T;
     constexpr int ES = sizeof(T);
     constexpr int V = 16 / ES;               // channels per 16-byte chunk
     constexpr int KF = KH * KW;
+    constexpr uint32_t K2B = KF * 2 * ES;    // offset bytes of one item
+    constexpr uint32_t KMB = KF * ES;        // mask bytes of one item
     static_assert(KF > 0, "ring kernel is instantiated for fixed kernels");
-    static_assert(ES == 2, "ring kernel stages 16-bit offsets and mask");
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
     unsigned char* stage = lds + rc.ring_bytes;
@@ -102,7 +103,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     int L = blockIdx.x;
     if (rc.nwg % 8 == 0) L = (blockIdx.x % 8) * (rc.nwg / 8) + blockIdx.x / 8;   // neighbours share an XCD
-    const int n = L / rc.chunks, chunk = L - n * rc.chunks;
+    const int chunk = L % rc.chunks;
+    const int ng = L / rc.chunks;
+    const int gset = ng % rc.gsets, n = ng / rc.gsets;
+    const int g0 = gset * rc.gs;
     const int r_begin = chunk * rc.chunk_rows;
     const int r_end = min(G.ho, r_begin + rc.chunk_rows);
     if (r_begin >= r_end) return;
@@ -113,45 +117,79 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)rc.x_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc((void*)off, (short)0, (int)rc.off_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc((void*)mask, (short)0, (int)rc.mask_bytes, 0x00020000);
-    const uint32_t img_bytes = (uint32_t)G.h * G.w * G.c * ES;
-    const uint32_t row_bytes = (uint32_t)G.w * G.c * ES;
+    const uint32_t pix_g = (uint32_t)G.c * ES;          // global bytes per pixel
+    const uint32_t row_bytes = (uint32_t)G.w * pix_g;
+    const uint32_t img_bytes = (uint32_t)G.h * row_bytes;
+    const uint32_t gsize = (uint32_t)G.d * ES;
+    const uint32_t goff = (uint32_t)g0 * gsize;         // first byte of the group set in a global pixel
 
-    // Input row `row` into its ring slot (zeros outside the image).
-    // Slot R mirrors slot 0, so the row below any slot is always the next slot in memory.
+    // Per-lane source offsets of the 16-byte chunks this lane copies in every
+    // input row (the same chunks for every row).
+    const uint32_t row_chunks = (uint32_t)G.w * rc.cpp;
+    uint32_t row_src[ROW_IT];
+#pragma unroll
+    for (int i = 0; i < ROW_IT; ++i) {
+        const uint32_t t = (uint32_t)(wave + i * nwaves) * 64u + lane;
+        const uint32_t pix = t / rc.cpp, u = t - pix * rc.cpp;
+        row_src[i] = t < row_chunks ? pix * pix_g + goff + 16u * u : OOB;
+    }
     auto load_row = [&](int row) {
         const int slot = (row - lo0) % rc.R;
-        const uint32_t src = (unsigned)row < (unsigned)G.h ? n * img_bytes + (uint32_t)row * row_bytes : OOB;
-        wave_copy_to_lds(xr, src, ring + slot * rc.pitch + rc.pb, row_bytes, wave, nwaves, lane);
-        if (slot == 0) wave_copy_to_lds(xr, src, ring + rc.R * rc.pitch + rc.pb, row_bytes, wave, nwaves, lane);
-    };
-    // Offsets and mask of one step's items: the items of a step are
-    // contiguous, so both runs are staged with aligned 16-byte loads.
-    auto stage_range = [&](int s, uint32_t& o_lo, uint32_t& m_lo, uint32_t& o_len, uint32_t& m_len) {
-        const int r_s = r_begin + s * rc.tr;
-        const int rows = min(rc.tr, r_end - r_s);
-        const uint32_t first = ((uint32_t)(n * G.ho + r_s) * G.wo) * G.g;
-        const uint32_t cnt = (uint32_t)rows * G.wo * G.g;
-        const uint32_t ob = first * KF * 2 * ES, oe = (first + cnt) * KF * 2 * ES;
-        const uint32_t mb = first * KF * ES, me = (first + cnt) * KF * ES;
-        o_lo = ob & ~15u;
-        m_lo = mb & ~15u;
-        o_len = ((oe + 15u) & ~15u) - o_lo;
-        m_len = ((me + 15u) & ~15u) - m_lo;
-    };
-    auto load_stage = [&](int s) {
-        uint32_t o_lo, m_lo, o_len, m_len;
-        stage_range(s, o_lo, m_lo, o_len, m_len);
-        wave_copy_to_lds(orr, o_lo, stage, o_len, wave, nwaves, lane);
-        wave_copy_to_lds(mr, m_lo, stage + o_len, m_len, wave, nwaves, lane);
+        const bool inside = (unsigned)row < (unsigned)G.h;
+        const uint32_t base = n * img_bytes + (uint32_t)row * row_bytes;
+#pragma unroll
+        for (int i = 0; i < ROW_IT; ++i) {
+            if (i >= rc.row_iters) break;
+            const uint32_t c = (uint32_t)(wave + i * nwaves) * 1024u;
+            if (row_src[i] != OOB) {
+                const uint32_t src = inside ? base + row_src[i] : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + slot * rc.pitch + rc.pb + c), 16, src,
+                                                         0, 0, 0);
+                if (slot == 0)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + rc.R * rc.pitch + rc.pb + c), 16,
+                                                             src, 0, 0, 0);
+            }
+        }
     };
 
-    // Zero the two border columns of every ring slot (never written again).
+    // Offsets and mask of one step.  With every group in the workgroup the
+    // step's items are contiguous and are staged with aligned 16-byte loads;
+    // otherwise each pixel contributes one aligned run per tensor of cpo
+    // (offsets) and cpm (mask) chunks.
+    const uint32_t GK2 = (uint32_t)G.g * K2B, GKM = (uint32_t)G.g * KMB;
+    auto first_pixel = [&](int s) { return (uint32_t)(n * G.ho + r_begin + s * rc.tr) * G.wo; };
+    auto step_pixels = [&](int s) { return (uint32_t)min(rc.tr, r_end - (r_begin + s * rc.tr)) * G.wo; };
+    auto load_stage = [&](int s) {
+        const uint32_t P0 = first_pixel(s), np = step_pixels(s);
+        if (rc.st_contig) {
+            const uint32_t ob = P0 * GK2, oe = (P0 + np) * GK2, mb = P0 * GKM, me = (P0 + np) * GKM;
+            const uint32_t o_lo = ob & ~15u, m_lo = mb & ~15u;
+            const uint32_t o_len = ((oe + 15u) & ~15u) - o_lo, m_len = ((me + 15u) & ~15u) - m_lo;
+            wave_copy_to_lds(orr, o_lo, stage, o_len, wave, nwaves, lane);
+            wave_copy_to_lds(mr, m_lo, stage + rc.stage_o_bytes, m_len, wave, nwaves, lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < ST_IT; ++i) {
+                const uint32_t c = (uint32_t)(wave + i * nwaves) * 1024u;
+                const uint32_t t = c / 16u + lane;
+                const uint32_t p = t / rc.cpo, j = t - p * rc.cpo;
+                if (t < np * rc.cpo)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_ptr_t)(stage + c), 16,
+                                                             (((P0 + p) * GK2 + g0 * K2B) & ~15u) + 16u * j, 0, 0, 0);
+                const uint32_t pm = t / rc.cpm, jm = t - pm * rc.cpm;
+                if (t < np * rc.cpm)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_ptr_t)(stage + rc.stage_o_bytes + c), 16,
+                                                             (((P0 + pm) * GKM + g0 * KMB) & ~15u) + 16u * jm, 0, 0, 0);
+            }
+        }
+    };
+
+    // Zero the two border columns of every ring slot, mirror included (never written again).
     {
-        const int pbc = rc.pb / 16;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < (rc.R + 1) * 2 * pbc; i += nthr) {
-            const int slot = i / (2 * pbc), j = i - slot * 2 * pbc;
-            const uint32_t col_off = j < pbc ? 16u * j : (uint32_t)(G.w + 1) * rc.pb + 16u * (j - pbc);
+        for (int i = tid; i < (rc.R + 1) * 2 * rc.cpp; i += nthr) {
+            const int slot = i / (2 * rc.cpp), j = i - slot * 2 * rc.cpp;
+            const uint32_t col_off = j < rc.cpp ? 16u * j : (uint32_t)(G.w + 1) * rc.pb + 16u * (j - rc.cpp);
             *reinterpret_cast<u32x4*>(ring + slot * rc.pitch + col_off) = z;
         }
     }
@@ -160,35 +198,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    const int items_row = G.wo * G.g;
+    // This lane's item within every step: row rl of the step, column c, group gl of the set.
+    const int items_row = G.wo * rc.gs;
+    const int rl = tid / items_row;
+    const int rem = tid - rl * items_row;
+    const int c = rem / rc.gs, gl = rem - c * rc.gs;
+    const int g = g0 + gl;
+    const uint32_t gbyte = (uint32_t)gl * gsize;
     const float lim = 16777216.0f;
+    uint32_t qoff[NCH];   // byte offset of the chunk held in accumulator slot q
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) qoff[q] = NCH == 2 ? 16u * ((uint32_t)(q + c) & 1u) : 16u * q;
+    // Window-relative row and LDS column of each tap's top-left corner before
+    // the offset (they do not change from step to step).
+    int bxk[KW], byk[KH];
+#pragma unroll
+    for (int kx = 0; kx < KW; ++kx) bxk[kx] = c * G.sw - G.pw + 1 + kx * G.dw;
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky) byk[ky] = (r_begin + rl) * G.sh - G.ph - lo0 + ky * G.dh;
 
     for (int s = 0; s < nsteps; ++s) {
         const int r_s = r_begin + s * rc.tr;
-        const int rows_s = min(rc.tr, r_end - r_s);
+        const int r = r_s + rl;
+        const bool live = rl < rc.tr && r < r_end;
         const int lo = lo0 + s * adv;
         const int slot_lo = (s * adv) % rc.R;
 
-        // ---- this lane's item; its offsets and mask come out of the staging area
-        const int i = tid;
-        const bool live = i < rows_s * items_row;
-        const int rl = live ? i / items_row : 0;
-        const int rem = live ? i - rl * items_row : 0;
-        const int c = rem / G.g, g = rem - c * G.g;
-        const int r = r_s + rl;
-        uint32_t dxy[KF];
-        float m[KF];
+        // ---- offsets and mask of this lane's item, out of the staging area
+        float dx[KF], dy[KF], m[KF];
         {
-            uint32_t o_lo, m_lo, o_len, m_len;
-            stage_range(s, o_lo, m_lo, o_len, m_len);
-            const uint32_t item = ((uint32_t)(n * G.ho + r) * G.wo + c) * G.g + g;
-            const uint32_t ob = item * KF * 2 * ES - o_lo;
-            const uint32_t mb = o_len + item * KF * ES - m_lo;
+            const uint32_t P0 = first_pixel(s);
+            const uint32_t pl = (uint32_t)(live ? rl : 0) * G.wo + c;    // pixel within the step
+            uint32_t ob, mb;
+            if (rc.st_contig) {
+                const uint32_t o_lo = (P0 * GK2) & ~15u, m_lo = (P0 * GKM) & ~15u;
+                ob = (P0 + pl) * GK2 + gl * K2B - o_lo;
+                mb = rc.stage_o_bytes + (P0 + pl) * GKM + gl * KMB - m_lo;
+            } else {
+                const uint32_t so = (P0 + pl) * GK2 + g0 * K2B, sm = (P0 + pl) * GKM + g0 * KMB;
+                ob = pl * rc.cpo * 16u + (so & 15u) + gl * K2B;
+                mb = rc.stage_o_bytes + pl * rc.cpm * 16u + (sm & 15u) + gl * KMB;
+            }
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
-                dxy[k] = *reinterpret_cast<const uint32_t*>(stage + ob + 4u * k);
-                const uint16_t h = *reinterpret_cast<const uint16_t*>(stage + mb + 2u * k);
-                m[k] = half_lo<DT>((uint32_t)h);
+                if constexpr (ES == 4) {
+                    const float2 d = *reinterpret_cast<const float2*>(stage + ob + 8u * k);
+                    dx[k] = d.x;
+                    dy[k] = d.y;
+                    m[k] = *reinterpret_cast<const float*>(stage + mb + 4u * k);
+                } else {
+                    const uint32_t p = *reinterpret_cast<const uint32_t*>(stage + ob + 4u * k);
+                    dx[k] = h2f<DT>(p & 0xffffu);
+                    dy[k] = h2f<DT>(p >> 16);
+                    m[k] = h2f<DT>(*reinterpret_cast<const uint16_t*>(stage + mb + 2u * k));
+                }
             }
         }
         __syncthreads();   // the staging area is free for the next step
@@ -199,7 +262,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             load_stage(s + 1);
         }
 
-        // ---- compute this lane's item from the ring
         if (live) {
             if constexpr (SOFTMAX) {
                 float mx = m[0];
@@ -215,59 +277,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             float acc[NCH * V];
 #pragma unroll
             for (int q = 0; q < NCH * V; ++q) acc[q] = 0.f;
-            // Geometry of all taps first: one LDS address (top-left corner, the
-            // other three are +pb, +pitch, +pitch+pb) and four weights per tap.
-            const int bx = c * G.sw - G.pw, by = r * G.sh - G.ph;
-            const int bx1 = bx + 1;                        // LDS column of tap column 0 (image column + 1)
-            const int byw = r * G.sh - G.ph - lo;          // window row of tap row 0
-            const uint32_t gbyte = (uint32_t)g * G.d * ES;
+            // Geometry of all taps first: the LDS address of the top-left
+            // corner (the others are +pb, +pitch, +pitch+pb) and four weights.
             uint32_t A[KF];
             float W00[KF], W01[KF], W10[KF], W11[KF];
             uint32_t fb = 0;
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
                 const int kx = k / KH, ky = k - (k / KH) * KH;
-                const float tx = fminf(fmaxf(G.scale * half_lo<DT>(dxy[k]), -lim), lim);
-                const float ty = fminf(fmaxf(G.scale * half_hi<DT>(dxy[k]), -lim), lim);
+                const float tx = fminf(fmaxf(G.scale * dx[k], -lim), lim);
+                const float ty = fminf(fmaxf(G.scale * dy[k], -lim), lim);
                 const float fx = floorf(tx), fy = floorf(ty);
                 const float a = tx - fx, b = ty - fy;
-                int xs = bx1 + kx * G.dw + (int)fx;                 // column of the left corners, +1
-                int yi = byw + ky * G.dh + (int)fy;                 // window row of the top corners
+                const int xs = bxk[kx] + (int)fx;                   // LDS column of the left corners
+                const int yi = byk[ky] + (int)fy;                   // window row of the top corners
                 const bool colok = (unsigned)xs <= (unsigned)G.w;   // image column in [-1, W-1]
                 const bool inwin = (unsigned)yi < (unsigned)(rc.nw - 1);
                 fb |= (colok && !inwin) ? (1u << k) : 0u;
                 const bool use = colok && inwin;
-                const float mm = use ? m[k] : 0.f;
-                xs = use ? xs : 0;
-                yi = use ? yi : 0;
                 uint32_t s0 = (uint32_t)(slot_lo + yi);
                 s0 = min(s0, s0 - (uint32_t)rc.R);                  // wrap once
-                A[k] = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
+                const uint32_t addr = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
+                A[k] = use ? addr : 0u;
+                const float mm = use ? m[k] : 0.f;
                 const float ma = mm * (1.f - a), mb = mm * a;
                 W00[k] = ma * (1.f - b);
                 W01[k] = mb * (1.f - b);
                 W10[k] = ma * b;
                 W11[k] = mb * b;
             }
-            // Reads of tap k+1 are in flight while tap k accumulates.
+            // Reads of tap k+1 are in flight while tap k accumulates (with four
+            // chunks per corner the two taps' data would not fit in registers,
+            // so each tap's reads are issued just before its math).  With two
+            // chunks per corner, slot q holds chunk (q + column) % 2, so that
+            // neighbouring lanes read different 16-byte bank groups in the same
+            // instruction; the stores undo the rotation.
+            constexpr bool PIPE = NCH <= 2;
             const uint32_t o01 = (uint32_t)rc.pb, o10 = (uint32_t)rc.pitch, o11 = (uint32_t)(rc.pitch + rc.pb);
-            u32x4 cur[4 * NCH], nxt[4 * NCH];
+            u32x4 cur[4 * NCH], nxt[PIPE ? 4 * NCH : 1];
 #pragma unroll
             for (int q = 0; q < NCH; ++q) {
-                cur[4 * q + 0] = lds_ld16(ring, A[0] + 16u * q);
-                cur[4 * q + 1] = lds_ld16(ring, A[0] + o01 + 16u * q);
-                cur[4 * q + 2] = lds_ld16(ring, A[0] + o10 + 16u * q);
-                cur[4 * q + 3] = lds_ld16(ring, A[0] + o11 + 16u * q);
+                cur[4 * q + 0] = lds_ld16(ring, A[0] + qoff[q]);
+                cur[4 * q + 1] = lds_ld16(ring, A[0] + o01 + qoff[q]);
+                cur[4 * q + 2] = lds_ld16(ring, A[0] + o10 + qoff[q]);
+                cur[4 * q + 3] = lds_ld16(ring, A[0] + o11 + qoff[q]);
             }
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
-                if (k + 1 < KF) {
+                if (!PIPE && k > 0) {
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
-                        nxt[4 * q + 0] = lds_ld16(ring, A[k + 1] + 16u * q);
-                        nxt[4 * q + 1] = lds_ld16(ring, A[k + 1] + o01 + 16u * q);
-                        nxt[4 * q + 2] = lds_ld16(ring, A[k + 1] + o10 + 16u * q);
-                        nxt[4 * q + 3] = lds_ld16(ring, A[k + 1] + o11 + 16u * q);
+                        cur[4 * q + 0] = lds_ld16(ring, A[k] + qoff[q]);
+                        cur[4 * q + 1] = lds_ld16(ring, A[k] + o01 + qoff[q]);
+                        cur[4 * q + 2] = lds_ld16(ring, A[k] + o10 + qoff[q]);
+                        cur[4 * q + 3] = lds_ld16(ring, A[k] + o11 + qoff[q]);
+                    }
+                }
+                if (PIPE && k + 1 < KF) {
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        nxt[4 * q + 0] = lds_ld16(ring, A[k + 1] + qoff[q]);
+                        nxt[4 * q + 1] = lds_ld16(ring, A[k + 1] + o01 + qoff[q]);
+                        nxt[4 * q + 2] = lds_ld16(ring, A[k + 1] + o10 + qoff[q]);
+                        nxt[4 * q + 3] = lds_ld16(ring, A[k + 1] + o11 + qoff[q]);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);   // keep the next tap's reads ahead of this tap's math
@@ -279,46 +351,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     fma16<DT>(acc + q * V, W11[k], cur[4 * q + 3]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (k + 1 < KF) {
+                if (PIPE && k + 1 < KF) {
 #pragma unroll
-                    for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[q];
+                    for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[PIPE ? q : 0];
                 }
             }
-            // Tail: samples outside the window but touching the image, read from global memory.
+            // Tail: samples outside the window that may touch the image, read from global memory.
             if (fb) {
-                const uint32_t base_img = n * img_bytes + gbyte;
-                const uint32_t pixb = (uint32_t)G.c * ES;
+                const uint32_t base_img = n * img_bytes + (uint32_t)g * gsize;
                 for (int k = 0; k < KF; ++k) {
                     if (!((fb >> k) & 1u)) continue;
                     const int kx = k / KH, ky = k - (k / KH) * KH;
-                    const float tx = fminf(fmaxf(G.scale * half_lo<DT>(dxy[k]), -lim), lim);
-                    const float ty = fminf(fmaxf(G.scale * half_hi<DT>(dxy[k]), -lim), lim);
+                    const float tx = fminf(fmaxf(G.scale * dx[k], -lim), lim);
+                    const float ty = fminf(fmaxf(G.scale * dy[k], -lim), lim);
                     const float fx = floorf(tx), fy = floorf(ty);
                     const float a = tx - fx, b = ty - fy;
-                    const int x0 = bx + kx * G.dw + (int)fx;
-                    const int y0 = by + ky * G.dh + (int)fy;
+                    const int x0 = bxk[kx] - 1 + (int)fx;
+                    const int y0 = byk[ky] + lo + (int)fy;
                     const bool cx0 = (unsigned)x0 < (unsigned)G.w, cx1 = (unsigned)(x0 + 1) < (unsigned)G.w;
                     const bool cy0 = (unsigned)y0 < (unsigned)G.h, cy1 = (unsigned)(y0 + 1) < (unsigned)G.h;
-                    const uint32_t p00 = base_img + ((uint32_t)y0 * G.w + (uint32_t)x0) * pixb;
-                    const uint32_t o00 = (cy0 && cx0) ? p00 : OOB, o01 = (cy0 && cx1) ? p00 + pixb : OOB;
-                    const uint32_t o10 = (cy1 && cx0) ? p00 + row_bytes : OOB;
-                    const uint32_t o11 = (cy1 && cx1) ? p00 + row_bytes + pixb : OOB;
+                    const uint32_t p00 = base_img + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_g;
+                    const uint32_t o00 = (cy0 && cx0) ? p00 : OOB, o01g = (cy0 && cx1) ? p00 + pix_g : OOB;
+                    const uint32_t o10g = (cy1 && cx0) ? p00 + row_bytes : OOB;
+                    const uint32_t o11g = (cy1 && cx1) ? p00 + row_bytes + pix_g : OOB;
                     const float ma = m[k] * (1.f - a), mb = m[k] * a;
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
-                        fma16<DT>(acc + q * V, ma * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o00 + 16u * q, 0, 0));
-                        fma16<DT>(acc + q * V, mb * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o01 + 16u * q, 0, 0));
-                        fma16<DT>(acc + q * V, ma * b, __builtin_amdgcn_raw_buffer_load_b128(xr, o10 + 16u * q, 0, 0));
-                        fma16<DT>(acc + q * V, mb * b, __builtin_amdgcn_raw_buffer_load_b128(xr, o11 + 16u * q, 0, 0));
+                        const uint32_t qo = qoff[q];   // chunk held in slot q
+                        fma16<DT>(acc + q * V, ma * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o00 + qo, 0, 0));
+                        fma16<DT>(acc + q * V, mb * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o01g + qo, 0, 0));
+                        fma16<DT>(acc + q * V, ma * b, __builtin_amdgcn_raw_buffer_load_b128(xr, o10g + qo, 0, 0));
+                        fma16<DT>(acc + q * V, mb * b, __builtin_amdgcn_raw_buffer_load_b128(xr, o11g + qo, 0, 0));
                     }
                 }
             }
             T* op = out + (((long)(n * G.ho + r) * G.wo + c) * G.c + (long)g * G.d);
 #pragma unroll
-            for (int q = 0; q < NCH; ++q) store_vec<DT>(op + q * V, acc + q * V);
+            for (int q = 0; q < NCH; ++q) store_vec<DT>(op + qoff[q] / ES, acc + q * V);
         }
 
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's direct-to-LDS loads have landed
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's buffer-to-LDS loads have landed
         __syncthreads();
     }
 }
@@ -355,6 +427,8 @@ hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, 
                                    const void* mask, void* out, hipStream_t s)
 {
     switch (dtype * 2 + (G.softmax ? 1 : 0)) {
+        case DT_F32 * 2 + 0: return launch_ring_typed<DT_F32, false>(G, rc, x, off, mask, out, s);
+        case DT_F32 * 2 + 1: return launch_ring_typed<DT_F32, true>(G, rc, x, off, mask, out, s);
         case DT_F16 * 2 + 0: return launch_ring_typed<DT_F16, false>(G, rc, x, off, mask, out, s);
         case DT_F16 * 2 + 1: return launch_ring_typed<DT_F16, true>(G, rc, x, off, mask, out, s);
         case DT_BF16 * 2 + 0: return launch_ring_typed<DT_BF16, false>(G, rc, x, off, mask, out, s);
@@ -363,70 +437,107 @@ hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, 
     return hipErrorInvalidValue;
 }
 
-}  // namespace dcn
-
-namespace dcn {
-
+// Choose the group set, rows per step, halo and chunking for geometry G, or
+// return false when the sliding-window kernel does not apply.
 bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
                int lds_limit, int num_cus, RingCfg* rc)
 {
-    if (dtype != DT_F16 && dtype != DT_BF16) return false;
     if (G.kh != 3 || G.kw != 3) return false;
-    const int es = 2;
+    const int es = dtype == DT_F32 ? 4 : 2;
     const int nch = G.d * es / 16;
     if (G.d * es % 16 != 0 || (nch != 1 && nch != 2 && nch != 4)) return false;
     if ((uintptr_t)x % 16 || (uintptr_t)off % 16 || (uintptr_t)mask % 16 || (uintptr_t)out % 16) return false;
     const long x_bytes = (long)G.n * G.h * G.w * G.c * es;
     const long off_bytes = (long)G.items * G.K * 2 * es, mask_bytes = (long)G.items * G.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
-    const int items_row = G.wo * G.g;
-    if (items_row > 512) return false;
-    int tr = (384 + items_row - 1) / items_row;
-    tr = std::max(1, std::min(tr, std::min(512 / items_row, G.ho)));
-    const int items_step = tr * items_row;
-    const int threads = (items_step + 63) / 64 * 64;
-    const int pb = G.c * es;
-    const long pitch = (long)(G.w + 2) * pb + 16;
-    const int stage_bytes = 16 * ((items_step * G.K * 2 * es + 15) / 16 + 2 + (items_step * G.K * es + 15) / 16 + 2);
-    const int adv = tr * G.sh;
-    int hy = -1, nw = 0, R = 0;
-    for (int h = 8; h >= 2; --h) {
-        const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
-        const int Rh = nwh + adv;
-        if ((long)(Rh + 1) * pitch + stage_bytes <= lds_limit) {
-            hy = h;
-            nw = nwh;
-            R = Rh;
-            break;
+    const int K2B = G.K * 2 * es, KMB = G.K * es;
+
+    // Try group sets from all groups down; take the first that keeps a halo of
+    // at least HY_MIN rows in LDS with one workgroup per CU.
+    const int HY_MIN = 4, HY_MAX = 8;
+    for (int gs = G.g; gs >= 1; --gs) {
+        if (G.g % gs) continue;
+        const int items_row = G.wo * gs;
+        if (items_row > 512) continue;
+        int tr = (448 + items_row - 1) / items_row;
+        tr = std::max(1, std::min(tr, std::min(512 / items_row, G.ho)));
+        const int items_step = tr * items_row;
+        const int threads = (items_step + 63) / 64 * 64;
+        const int pb = gs * G.d * es;
+        const int cpp = pb / 16;
+        const long pitch = (long)(G.w + 2) * pb + 80;   // 5 bank groups of skew: nearby rows spread over the banks
+        const int nwaves = threads / 64;
+        const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
+        if (row_iters > 4) continue;   // ROW_IT
+        const int np = tr * G.wo;      // pixels per step
+        int stage_o, stage_m, st_contig, cpo = 0, cpm = 0;
+        if (gs == G.g) {
+            st_contig = 1;
+            stage_o = (np * G.g * K2B + 15) / 16 * 16 + 16;
+            stage_m = (np * G.g * KMB + 15) / 16 * 16 + 16;
+        } else {
+            st_contig = 0;
+            // a run starts at a multiple of gcd(item bytes, 16) within its 16-byte line
+            auto gcd16 = [](int v) { int gdiv = 16; while (v % gdiv) gdiv >>= 1; return gdiv; };
+            cpo = (gs * K2B + (16 - gcd16(K2B)) + 15) / 16;
+            cpm = (gs * KMB + (16 - gcd16(KMB)) + 15) / 16;
+            stage_o = np * cpo * 16;
+            stage_m = np * cpm * 16;
+            const long iters = ((long)np * std::max(cpo, cpm) + 63) / 64;
+            if ((iters + nwaves - 1) / nwaves > 8) continue;   // ST_IT
         }
+        const int stage_bytes = stage_o + stage_m;
+        const int adv = tr * G.sh;
+        int hy = -1, nw = 0, R = 0;
+        for (int h = HY_MAX; h >= HY_MIN; --h) {
+            const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
+            const int Rh = nwh + adv;
+            if ((long)(Rh + 1) * pitch + stage_bytes <= lds_limit) {
+                hy = h;
+                nw = nwh;
+                R = Rh;
+                break;
+            }
+        }
+        if (hy < 0) continue;
+        const int gsets = G.g / gs;
+        const long units = (long)G.n * gsets;
+        int chunks = (int)std::max(1L, ((long)num_cus + units - 1) / units);
+        chunks = std::min(chunks, (G.ho + tr - 1) / tr);
+        int chunk_rows = (G.ho + chunks - 1) / chunks;
+        chunk_rows = (chunk_rows + tr - 1) / tr * tr;
+        chunks = (G.ho + chunk_rows - 1) / chunk_rows;
+        if (units * chunks >= (1L << 31)) continue;
+        rc->gs = gs;
+        rc->gsets = gsets;
+        rc->pb = pb;
+        rc->cpp = cpp;
+        rc->pitch = (int)pitch;
+        rc->R = R;
+        rc->nw = nw;
+        rc->hy = hy;
+        rc->tr = tr;
+        rc->chunk_rows = chunk_rows;
+        rc->chunks = chunks;
+        rc->nwg = (int)(units * chunks);
+        rc->threads = threads;
+        rc->row_iters = row_iters;
+        rc->st_contig = st_contig;
+        rc->cpo = cpo;
+        rc->cpm = cpm;
+        rc->stage_o_bytes = stage_o;
+        rc->ring_bytes = (int)((R + 1) * pitch);
+        rc->lds_bytes = rc->ring_bytes + stage_bytes;
+        // Buffer loads range-check each dword: a dword that straddles num_records
+        // reads as zero.  Rounding the extents up to whole dwords keeps the last
+        // values of an odd-length 16-bit tensor readable; the extra bytes share
+        // a dword (and so a page) with valid data and are never used.
+        rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
+        rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
+        rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
+        return true;
     }
-    if (hy < 0) return false;
-    int chunks = std::max(1, (num_cus + G.n - 1) / G.n);
-    chunks = std::min(chunks, (G.ho + tr - 1) / tr);
-    int chunk_rows = (G.ho + chunks - 1) / chunks;
-    chunk_rows = (chunk_rows + tr - 1) / tr * tr;
-    chunks = (G.ho + chunk_rows - 1) / chunk_rows;
-    if ((long)G.n * chunks >= (1L << 31)) return false;
-    rc->pb = pb;
-    rc->pitch = (int)pitch;
-    rc->R = R;
-    rc->nw = nw;
-    rc->hy = hy;
-    rc->tr = tr;
-    rc->chunk_rows = chunk_rows;
-    rc->chunks = chunks;
-    rc->nwg = G.n * chunks;
-    rc->threads = threads;
-    rc->ring_bytes = (int)((R + 1) * pitch);
-    rc->lds_bytes = rc->ring_bytes + stage_bytes;
-    // Buffer loads range-check each dword: a dword that straddles num_records
-    // reads as zero.  Rounding the extents up to whole dwords keeps the last
-    // values of an odd-length f16 tensor readable; the extra bytes share a
-    // dword (and so a page) with valid data and are never used.
-    rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
-    rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
-    rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
-    return true;
+    return false;
 }
 
 void device_limits(int* lds_limit, int* num_cus)

@@ -9,19 +9,26 @@
 namespace dcn {
 
 struct RingCfg {
-    int pb;           // bytes of one pixel in LDS (all channels)
-    int pitch;        // bytes of one ring row: (w + 2) pixels (zero column each side) + 16 bytes of bank skew
-    int R;            // ring rows (plus one mirror slot)
-    int nw;           // window rows a step may read
+    int gs;           // channel groups per workgroup (a divisor of the group count)
+    int gsets;        // group sets per image (= groups / gs)
+    int pb;           // bytes of one pixel in LDS (gs groups)
+    int cpp;          // 16-byte chunks per LDS pixel (pb / 16)
+    int pitch;        // bytes of one ring row: (w + 2) pixels (zero column each side) + 80 bytes of bank skew
+    int R;            // ring rows (slot R, one more, mirrors slot 0)
+    int nw;           // window rows a step may read through LDS
     int hy;           // halo rows above and below the footprint
     int tr;           // output rows per step
     int chunk_rows;   // output rows per workgroup
-    int chunks;       // workgroups per image
+    int chunks;       // row chunks per (image, group set)
     int nwg;          // workgroups
     int threads;      // threads per workgroup (one item per thread per step)
-    int ring_bytes;   // (R + 1) * pitch: slot R mirrors slot 0
+    int row_iters;    // 1 KB copy instructions per wave for one input row
+    int st_contig;    // 1: offsets/mask of a step are one contiguous run (gs == groups)
+    int cpo, cpm;     // otherwise: 16-byte chunks staged per pixel for offsets and for mask
+    int stage_o_bytes;  // bytes of the offsets part of the staging area
+    int ring_bytes;   // (R + 1) * pitch
     int lds_bytes;    // ring + staging of one step's offsets and mask
-    uint32_t x_bytes, off_bytes, mask_bytes;
+    uint32_t x_bytes, off_bytes, mask_bytes;   // buffer extents, rounded up to whole dwords
 };
 
 // Fill `rc` for geometry G; false if the sliding-window kernel does not apply.
