@@ -23,7 +23,13 @@ __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, long n)
 {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long stride = (long)gridDim.x * blockDim.x;
-    for (long j = i; j < n; j += stride) p[j] = 0.f;
+    if ((uintptr_t)p % 16 == 0) {
+        const long n4 = n / 4;
+        for (long j = i; j < n4; j += stride) reinterpret_cast<float4*>(p)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (long j = n4 * 4 + i; j < n; j += stride) p[j] = 0.f;
+    } else {
+        for (long j = i; j < n; j += stride) p[j] = 0.f;
+    }
 }
 
 __device__ __forceinline__ float softmax_inputs(const float* mk, int K, float* m, bool softmax)
@@ -231,26 +237,23 @@ __global__ __launch_bounds__(256) void dcn_bwd_generic(Geom G, const float* __re
         for (int kk = 0; kk < K; ++kk) gmask[(long)item * K + kk] = SOFTMAX ? m[kk] * (dm[kk] - sdm) : dm[kk];
 }
 
+// Dispatch.  grad_x is accumulated with fp32 atomics, whose throughput on
+// gfx950 scales with the contiguous bytes one instruction adds to (about 21,
+// 84 and 330 G adds/s for 4, 16 and 64-byte runs per lane group), so the
+// preferred mapping is one lane per channel: the D lanes of an item add to D
+// contiguous floats of each corner in one instruction.
 template <bool SOFTMAX>
 hipError_t launch_typed(const Geom& G, const float* x, const float* off, const float* mask, const float* gout,
                         float* gx, float* goff, float* gmask, hipStream_t s)
 {
     const dim3 block(256);
-    const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)gout % 16 == 0) && ((uintptr_t)gx % 16 == 0);
-    const int P4 = G.d / 4;
-    const bool pow2_4 = G.d % 4 == 0 && P4 <= 64 && (P4 & (P4 - 1)) == 0;
     const bool pow2_1 = G.d <= 64 && (G.d & (G.d - 1)) == 0;
     const bool k_ok = G.K <= KMAX_BWD;
-    if (aligned && pow2_4 && G.kh == 3 && G.kw == 3) {
-        const long lanes = (long)G.items * P4;
-        dcn_bwd_lane<4, 3, 3, SOFTMAX><<<dim3((unsigned)((lanes + 255) / 256)), block, 0, s>>>(
-            G, x, off, mask, gout, gx, goff, gmask);
-    } else if (aligned && pow2_4 && k_ok) {
-        const long lanes = (long)G.items * P4;
-        dcn_bwd_lane<4, 0, 0, SOFTMAX><<<dim3((unsigned)((lanes + 255) / 256)), block, 0, s>>>(
+    const long lanes = (long)G.items * G.d;
+    if (pow2_1 && G.kh == 3 && G.kw == 3) {
+        dcn_bwd_lane<1, 3, 3, SOFTMAX><<<dim3((unsigned)((lanes + 255) / 256)), block, 0, s>>>(
             G, x, off, mask, gout, gx, goff, gmask);
     } else if (pow2_1 && k_ok) {
-        const long lanes = (long)G.items * G.d;
         dcn_bwd_lane<1, 0, 0, SOFTMAX><<<dim3((unsigned)((lanes + 255) / 256)), block, 0, s>>>(
             G, x, off, mask, gout, gx, goff, gmask);
     } else {
