@@ -184,6 +184,23 @@ def summarize(r, ms_step, kms):
             "achieved_gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+COPY_CALIB_BYTES = 256 << 20
+
+
+def copy_calib(torch, steps, warmup):
+    """A plain device-to-device copy of COPY_CALIB_BYTES per launch over
+    rotating buffers: the known-size reference that scales the memory-side
+    byte counters (FETCH_SIZE, WRITE_SIZE) read for the kernels."""
+    nel = COPY_CALIB_BYTES // 4
+    bufs = [torch.empty(nel, dtype=torch.float32, device="cuda").fill_(i) for i in range(8)]
+    for i in range(warmup + steps):
+        bufs[(2 * i + 1) % 8].copy_(bufs[(2 * i) % 8])
+    torch.cuda.synchronize()
+    print(json.dumps({"only": "copy_calib", "bytes_read": COPY_CALIB_BYTES, "bytes_written": COPY_CALIB_BYTES,
+                      "launches": warmup + steps}), flush=True)
+    return 0
+
+
 def cpu_baseline(seconds):
     """The CPU oracle as it stands (single-threaded C, double), timed on this
     host over whole stage-1 DCNv4 f16 batches until `seconds` have passed."""
@@ -219,6 +236,8 @@ def main():
     B.lib()
     if args.only:
         name = args.only
+        if name == "copy_calib":
+            return copy_calib(torch, args.steps, args.warmup)
         if name.startswith("msda"):
             r = msda_runner(torch)
         elif "_bwd_" in name:

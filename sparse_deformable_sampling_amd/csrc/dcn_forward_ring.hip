@@ -263,6 +263,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         }
 
         if (live) {
+            float smax = 0.f, sinv = 1.f;   // softmax max and 1/sum, kept for the tail
             if constexpr (SOFTMAX) {
                 float mx = m[0];
 #pragma unroll
@@ -273,6 +274,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 const float inv = 1.0f / sum;
 #pragma unroll
                 for (int k = 0; k < KF; ++k) m[k] *= inv;
+                smax = mx;
+                sinv = inv;
             }
             float acc[NCH * V];
 #pragma unroll
@@ -356,25 +359,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[PIPE ? q : 0];
                 }
             }
-            // Tail: samples outside the window that may touch the image, read from global memory.
+            // Tail: samples outside the window that may touch the image, read
+            // from global memory.  Each lane walks only its own such taps, so a
+            // wave runs as many iterations as its busiest lane; the tap's
+            // offsets and modulation are read again from global memory (the
+            // staging area has been released) rather than indexed in registers.
             if (fb) {
                 const uint32_t base_img = n * img_bytes + (uint32_t)g * gsize;
-                for (int k = 0; k < KF; ++k) {
-                    if (!((fb >> k) & 1u)) continue;
-                    const int kx = k / KH, ky = k - (k / KH) * KH;
-                    const float tx = fminf(fmaxf(G.scale * dx[k], -lim), lim);
-                    const float ty = fminf(fmaxf(G.scale * dy[k], -lim), lim);
+                const uint32_t item = ((uint32_t)(n * G.ho + r) * G.wo + c) * G.g + g;
+                while (fb) {
+                    const int k = __builtin_ctz(fb);
+                    fb &= fb - 1u;
+                    const int kx = k / KH, ky = k - kx * KH;
+                    float dxk, dyk, mk;
+                    if constexpr (ES == 4) {
+                        const uint32_t o = item * K2B + 8u * k;
+                        dxk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, o, 0, 0));
+                        dyk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, o + 4u, 0, 0));
+                        mk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, item * KMB + 4u * k, 0, 0));
+                    } else {
+                        const uint32_t pr = __builtin_amdgcn_raw_buffer_load_b32(orr, item * K2B + 4u * k, 0, 0);
+                        dxk = h2f<DT>(pr & 0xffffu);
+                        dyk = h2f<DT>(pr >> 16);
+                        mk = h2f<DT>(__builtin_amdgcn_raw_buffer_load_b16(mr, item * KMB + 2u * k, 0, 0));
+                    }
+                    if constexpr (SOFTMAX) mk = exp_nonpos(mk - smax) * sinv;
+                    const float tx = fminf(fmaxf(G.scale * dxk, -lim), lim);
+                    const float ty = fminf(fmaxf(G.scale * dyk, -lim), lim);
                     const float fx = floorf(tx), fy = floorf(ty);
                     const float a = tx - fx, b = ty - fy;
-                    const int x0 = bxk[kx] - 1 + (int)fx;
-                    const int y0 = byk[ky] + lo + (int)fy;
+                    const int x0 = c * G.sw - G.pw + kx * G.dw + (int)fx;
+                    const int y0 = (r_begin + rl) * G.sh - G.ph + ky * G.dh + (int)fy + s * adv;
                     const bool cx0 = (unsigned)x0 < (unsigned)G.w, cx1 = (unsigned)(x0 + 1) < (unsigned)G.w;
                     const bool cy0 = (unsigned)y0 < (unsigned)G.h, cy1 = (unsigned)(y0 + 1) < (unsigned)G.h;
                     const uint32_t p00 = base_img + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_g;
                     const uint32_t o00 = (cy0 && cx0) ? p00 : OOB, o01g = (cy0 && cx1) ? p00 + pix_g : OOB;
                     const uint32_t o10g = (cy1 && cx0) ? p00 + row_bytes : OOB;
                     const uint32_t o11g = (cy1 && cx1) ? p00 + row_bytes + pix_g : OOB;
-                    const float ma = m[k] * (1.f - a), mb = m[k] * a;
+                    const float ma = mk * (1.f - a), mb = mk * a;
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
                         const uint32_t qo = qoff[q];   // chunk held in slot q
