@@ -326,6 +326,21 @@ def test_msda_head_dims(sds, dh):
     check_msda(sds, "msda-dh", 2, [(7, 9), (4, 5)], 23, 3, dh, 3, seed=41)
 
 
+@pytest.mark.parametrize("n,shapes,q,heads,dh,points", [
+    (2, [(6, 5), (3, 3)], 77, 3, 4, 8),          # 16 samples, one channel chunk per query
+    (2, [(9, 7), (5, 4)], 50, 5, 64, 2),         # 4 samples, 16 lanes per query
+    (1, [(4, 4)], 9, 1, 256, 32),                # 32 samples, 64 lanes per query
+    (3, [(7, 6), (4, 3), (2, 2), (1, 1)], 45, 2, 16, 8),   # 32 samples over 4 levels
+    (1, [(3, 3)], 40, 2, 4, 32),                 # a 32-lane workgroup
+    (2, [(5, 8)], 300, 3, 8, 1),                 # one sample per head
+])
+def test_msda_tiled_shapes(sds, n, shapes, q, heads, dh, points):
+    """Power-of-two sample counts and head sizes (the tiled kernel): ragged
+    query tiles and workgroup counts that are not a multiple of eight."""
+    for softmax in (True, False):
+        check_msda(sds, "msda-tiled", n, shapes, q, heads, dh, points, softmax=softmax, seed=47, offset_std=3.0)
+
+
 @pytest.mark.parametrize("shapes,points", [([(1, 1)], 1), ([(5, 3)], 8), ([(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 2)])
 def test_msda_levels_points(sds, shapes, points):
     for softmax in (True, False):
