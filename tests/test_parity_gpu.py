@@ -133,18 +133,23 @@ def test_tall_wide_and_short_maps(sds, dtype, shape):
             check_fwd(sds, "shape", n, h, w, c, g, dtype, softmax, seed=29, **geom)
 
 
-def test_integer_offsets_bit_exact(sds):
-    """One-hot DCNv4 modulation and integer offsets copy pixels exactly."""
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("c,g", [(32, 2), (64, 4)])
+def test_integer_offsets_bit_exact(sds, dtype, c, g):
+    """One-hot DCNv4 modulation and integer offsets copy pixels exactly, in
+    every storage type (the stored values are compared bit for bit)."""
     import torch
-    n, h, w, c, g = 2, 10, 12, 32, 2
+    n, h, w = 2, 10, 12
     rng = np.random.default_rng(13)
-    x = rng.standard_normal((n, h, w, c)).astype(np.float32)
-    off = rng.integers(-4, 5, size=(n, h, w, g, 9, 2)).astype(np.float32)
+    x = synth.store(rng.standard_normal((n, h, w, c)).astype(np.float32), dtype)
+    off = synth.store(rng.integers(-4, 5, size=(n, h, w, g, 9, 2)).astype(np.float32), dtype)
     mask = np.zeros((n, h, w, g, 9), np.float32)
     mask[..., 5] = 1.0
-    say("integer-shift")
-    got = to_host(sds.dcn_forward(to_dev(x, "f32"), to_dev(off, "f32"), to_dev(mask, "f32"), group=g))
-    ref = oracle.dcn_forward(x, off, mask, group=g)
+    mask = synth.store(mask, dtype)
+    say("integer-shift", dtype, c, g)
+    out = sds.dcn_forward(to_dev(x, dtype), to_dev(off, dtype), to_dev(mask, dtype), group=g)
+    ref = oracle.dcn_forward(x, off, mask, group=g, dtype=dtype)
+    got = to_host(out)
     assert np.array_equal(got, ref)
     torch.cuda.synchronize()
 
@@ -167,11 +172,12 @@ def test_unaligned_views_take_the_scalar_path(sds):
     assert rel_err(to_host(out), ref) <= TOL["f32"]
 
 
-def test_forward_is_deterministic(sds):
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_forward_is_deterministic(sds, dtype):
     import torch
-    d = synth.dcn_inputs(8, 56, 56, 64, 4, (56, 56), dtype="f16", seed=19)
-    x, off, mask = (to_dev(d[k], "f16") for k in ("x", "offset", "mask"))
-    say("determinism")
+    d = synth.dcn_inputs(8, 56, 56, 64, 4, (56, 56), dtype=dtype, seed=19)
+    x, off, mask = (to_dev(d[k], dtype) for k in ("x", "offset", "mask"))
+    say("determinism", dtype)
     a = sds.dcn_forward(x, off, mask, group=4)
     b = sds.dcn_forward(x, off, mask, group=4)
     torch.cuda.synchronize()
