@@ -71,6 +71,8 @@ def _load():
         for name in ("oracle_msda_forward", "oracle_msda_forward_tent"):
             getattr(lib, name).argtypes = [ctypes.POINTER(_Msda), ctypes.POINTER(ctypes.c_int),
                                            pd, pd, pd, pd]
+        lib.oracle_msda_backward.argtypes = [ctypes.POINTER(_Msda), ctypes.POINTER(ctypes.c_int),
+                                             pd, pd, pd, pd, pd, pd, pd]
         _lib = lib
     return _lib
 
@@ -161,3 +163,25 @@ def msda_forward(value, shapes, loc, attn, softmax=True, dtype=None, tent=False)
             _ptr(np.ascontiguousarray(l64)), _ptr(np.ascontiguousarray(a64)), _ptr(out))
     assert rc == 0
     return out
+
+
+def msda_backward(value, shapes, loc, attn, grad_out, softmax=True, dtype=None):
+    """(grad_value, grad_loc, grad_attn) of msda_forward in float64;
+    grad_attn is with respect to the values passed in attn (the logits when
+    softmax is set)."""
+    v64, l64, a64 = to_f64(value, dtype), to_f64(loc, dtype), to_f64(attn, dtype)
+    g64 = to_f64(grad_out, dtype)
+    n, S, M, Dh = v64.shape
+    _, Q, M2, L, P, two = l64.shape
+    assert M2 == M and two == 2 and len(shapes) == L and g64.shape == (n, Q, M, Dh)
+    sh = np.ascontiguousarray(np.asarray(shapes, np.int32).reshape(L, 2))
+    assert int((sh[:, 0].astype(np.int64) * sh[:, 1]).sum()) == S
+    p = _Msda(n, Q, M, Dh, L, P, int(softmax))
+    gv = np.zeros_like(v64)
+    gl = np.zeros(l64.shape, np.float64)
+    ga = np.zeros(a64.shape, np.float64)
+    rc = _load().oracle_msda_backward(ctypes.byref(p), sh.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _ptr(v64),
+                                      _ptr(np.ascontiguousarray(l64)), _ptr(np.ascontiguousarray(a64)),
+                                      _ptr(np.ascontiguousarray(g64)), _ptr(gv), _ptr(gl), _ptr(ga))
+    assert rc == 0
+    return gv, gl, ga

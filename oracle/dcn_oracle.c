@@ -390,3 +390,86 @@ int oracle_msda_forward_tent(const omsda_t* p, const int* shapes, const double* 
     free(A);
     return 0;
 }
+
+/* MSDA backward: the derivative of oracle_msda_forward, written out.
+ *
+ * For one query, head and sample i (level l, point p) at pixel coordinate
+ * x = u*W_l - 1/2, y = v*H_l - 1/2 with x0 = floor(x), a = x - x0 (y0, b
+ * likewise), corners V_rc (row y0+r, column x0+c, zero outside) and the
+ * output gradient g of that query and head ([DDETR] "A learned location can
+ * fall between cells": the read is a function of the location, so it is
+ * differentiable in it; "Mix samples with a per-head budget"):
+ *   s_i        = (1-a)(1-b) V00 + a(1-b) V01 + (1-a) b V10 + a b V11
+ *   dL/dA_i    = <g, s_i>
+ *   dL/dV_rc  += A_i * (corner weight) * g            (corners inside the level)
+ *   dL/du_i    = W_l * A_i * <g, (1-b)(V01-V00) + b(V11-V10)>
+ *   dL/dv_i    = H_l * A_i * <g, (1-a)(V10-V00) + a(V11-V01)>
+ * and, when attn holds logits z of the joint softmax A = softmax(z),
+ *   dL/dz_i    = A_i (dL/dA_i - sum_j A_j dL/dA_j).
+ * A sample that is outside the level (every corner outside) contributes
+ * nothing and has zero location gradient.  At an integer coordinate the floor
+ * cell's (right-hand) derivative is taken.  grad_value is overwritten (zeroed
+ * first).  Any grad pointer may be NULL to skip that output. */
+int oracle_msda_backward(const omsda_t* p, const int* shapes, const double* value,
+                         const double* loc, const double* attn, const double* grad_out,
+                         double* grad_value, double* grad_loc, double* grad_attn)
+{
+    const int L = p->levels, P = p->points, M = p->heads, Dh = p->head_dim, LP = L * P;
+    const size_t S = level_start(shapes, L);
+    double* A = (double*)malloc(sizeof(double) * LP);
+    double* dA = (double*)malloc(sizeof(double) * LP);
+    if (grad_value) memset(grad_value, 0, sizeof(double) * (size_t)p->n * S * M * Dh);
+    for (int n = 0; n < p->n; ++n)
+        for (int q = 0; q < p->len_q; ++q)
+            for (int h = 0; h < M; ++h) {
+                const size_t qh = ((size_t)n * p->len_q + q) * M + h;
+                head_weights(attn + qh * LP, LP, p->softmax, A);
+                const double* g = grad_out + qh * Dh;
+                for (int l = 0; l < L; ++l) {
+                    const int Hl = shapes[2 * l], Wl = shapes[2 * l + 1];
+                    const size_t base = (size_t)n * S + level_start(shapes, l);
+                    for (int pt = 0; pt < P; ++pt) {
+                        const int i = l * P + pt;
+                        const double* uv = loc + (qh * LP + i) * 2;
+                        double du = 0.0, dv = 0.0, da_i = 0.0;
+                        const double x = uv[0] * Wl - 0.5, y = uv[1] * Hl - 0.5;
+                        if (x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl) {
+                            const int x0 = (int)floor(x), y0 = (int)floor(y);
+                            const double a = x - x0, b = y - y0;
+                            const double wt[4] = {(1 - a) * (1 - b), a * (1 - b), (1 - a) * b, a * b};
+                            for (int d = 0; d < Dh; ++d) {
+                                double V[4];
+                                for (int c = 0; c < 4; ++c) {
+                                    const int row = y0 + c / 2, col = x0 + c % 2;
+                                    const int in = row >= 0 && row < Hl && col >= 0 && col < Wl;
+                                    const size_t idx = ((base + (size_t)row * Wl + col) * M + h) * Dh + d;
+                                    V[c] = in ? value[idx] : 0.0;
+                                    if (in && grad_value) grad_value[idx] += A[i] * wt[c] * g[d];
+                                }
+                                const double s = wt[0] * V[0] + wt[1] * V[1] + wt[2] * V[2] + wt[3] * V[3];
+                                da_i += g[d] * s;
+                                du += g[d] * ((1 - b) * (V[1] - V[0]) + b * (V[3] - V[2]));
+                                dv += g[d] * ((1 - a) * (V[2] - V[0]) + a * (V[3] - V[1]));
+                            }
+                            du *= A[i] * Wl;
+                            dv *= A[i] * Hl;
+                        }
+                        dA[i] = da_i;
+                        if (grad_loc) {
+                            grad_loc[(qh * LP + i) * 2] = du;
+                            grad_loc[(qh * LP + i) * 2 + 1] = dv;
+                        }
+                    }
+                }
+                if (grad_attn) {
+                    double t = 0.0;
+                    if (p->softmax)
+                        for (int i = 0; i < LP; ++i) t += A[i] * dA[i];
+                    for (int i = 0; i < LP; ++i)
+                        grad_attn[qh * LP + i] = p->softmax ? A[i] * (dA[i] - t) : dA[i];
+                }
+            }
+    free(A);
+    free(dA);
+    return 0;
+}

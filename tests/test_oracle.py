@@ -384,6 +384,92 @@ def test_msda_tent_brute_force_agrees():
 
 
 # --------------------------------------------------------------------------
+# MSDA backward
+
+
+def _msda_tiny(seed, softmax, offset_std=2.0):
+    shapes = [(4, 5), (2, 3)]
+    d = synth.msda_inputs(2, shapes, 5, 2, 3, 2, offset_std=offset_std, seed=seed)
+    value = d["value"].astype(np.float64)
+    loc = d["loc"].astype(np.float64)
+    attn = d["attn"].astype(np.float64)
+    g = np.random.default_rng(seed + 100).standard_normal((2, 5, 2, 3))
+    return shapes, value, loc, attn, g
+
+
+def test_msda_backward_grad_value_brute_force():
+    """grad_value[j] = <g, F(e_j)> with F the independent tent-form forward,
+    for every element j: the whole transposed map, column by column."""
+    shapes, value, loc, attn, g = _msda_tiny(61, True)
+    gv, _, _ = oracle.msda_backward(value, shapes, loc, attn, g, softmax=True)
+    ref = np.zeros_like(value)
+    for j in range(value.size):
+        e = np.zeros(value.size)
+        e[j] = 1.0
+        ref.flat[j] = np.sum(g * oracle.msda_forward(e.reshape(value.shape), shapes, loc, attn, softmax=True,
+                                                    tent=True))
+    np.testing.assert_allclose(gv, ref, rtol=0, atol=1e-12)
+    # and the adjoint identity on the real values
+    out = oracle.msda_forward(value, shapes, loc, attn, softmax=True)
+    assert np.sum(g * out) == pytest.approx(np.sum(gv * value), rel=1e-12)
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_msda_backward_loc_and_attn_by_finite_differences(softmax):
+    shapes, value, loc, attn, g = _msda_tiny(67, softmax)
+    _, gl, ga = oracle.msda_backward(value, shapes, loc, attn, g, softmax=softmax)
+    f = lambda lc, at: np.sum(g * oracle.msda_forward(value, shapes, lc, at, softmax=softmax))
+    h = 1e-7
+    Ws = np.array([w for _, w in shapes], np.float64)
+    Hs = np.array([hh for hh, _ in shapes], np.float64)
+    checked = 0
+    for idx in np.ndindex(*loc.shape[:-1]):
+        l = idx[3]
+        x = loc[idx + (0,)] * Ws[l] - 0.5
+        y = loc[idx + (1,)] * Hs[l] - 0.5
+        near_kink = min(abs(x - round(x)), abs(y - round(y))) < 1e-4
+        near_edge = min(abs(x + 1), abs(x - Ws[l]), abs(y + 1), abs(y - Hs[l])) < 1e-4
+        if near_kink or near_edge:
+            continue
+        for comp in (0, 1):
+            lp, lm = loc.copy(), loc.copy()
+            lp[idx + (comp,)] += h
+            lm[idx + (comp,)] -= h
+            fd = (f(lp, attn) - f(lm, attn)) / (2 * h)
+            assert gl[idx + (comp,)] == pytest.approx(fd, rel=1e-5, abs=1e-6)
+            checked += 1
+    assert checked > 50
+    for idx in np.ndindex(*attn.shape):
+        ap, am = attn.copy(), attn.copy()
+        ap[idx] += h
+        am[idx] -= h
+        fd = (f(loc, ap) - f(loc, am)) / (2 * h)
+        assert ga[idx] == pytest.approx(fd, rel=1e-5, abs=1e-7)
+
+
+def test_msda_backward_raw_weights_gradient_is_sampled_value():
+    """Without softmax, dL/dA_i = <g, s_i>, s_i the read of sample i alone."""
+    shapes, value, loc, attn, g = _msda_tiny(71, False)
+    _, _, ga = oracle.msda_backward(value, shapes, loc, attn, g, softmax=False)
+    for i in range(attn.shape[-1] * attn.shape[-2]):
+        onehot = np.zeros_like(attn).reshape(attn.shape[:3] + (-1,))
+        onehot[..., i] = 1.0
+        s = oracle.msda_forward(value, shapes, loc, onehot.reshape(attn.shape), softmax=False, tent=True)
+        np.testing.assert_allclose(ga.reshape(onehot.shape)[..., i], np.sum(g * s, -1), rtol=0, atol=1e-12)
+
+
+def test_msda_backward_softmax_gradient_sums_to_zero_and_far_samples_are_flat():
+    shapes, value, loc, attn, g = _msda_tiny(73, True)
+    loc[0, 1, 0, 0, 1] = [-3.0, 0.5]      # far outside level 0
+    loc[1, 2, 1, 1, 0] = [0.5, 4.0]       # far outside level 1
+    _, gl, ga = oracle.msda_backward(value, shapes, loc, attn, g, softmax=True)
+    np.testing.assert_allclose(ga.reshape(2, 5, 2, -1).sum(-1), 0.0, atol=1e-14)
+    assert np.all(gl[0, 1, 0, 0, 1] == 0.0) and np.all(gl[1, 2, 1, 1, 0] == 0.0)
+    _, _, ga_raw = oracle.msda_backward(value, shapes, loc, attn, g, softmax=False)
+    assert ga_raw[0, 1, 0, 0, 1] == 0.0 and ga_raw[1, 2, 1, 1, 0] == 0.0
+
+
+# --------------------------------------------------------------------------
 # the stored-value conversions the oracle reads through
 
 
