@@ -148,6 +148,30 @@ def msda_runner(torch, seed=1):
     return r
 
 
+def msda_bwd_runner(torch, seed=1):
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, q, heads, dh, pts = 8, 17821, 8, 32, 4
+    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed)
+    g = np.random.default_rng(seed + 1000).standard_normal((n, q, heads, dh)).astype(np.float32)
+    # value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written once
+    min_bytes = 4 * (2 * (d["value"].size + d["loc"].size + d["attn"].size) + g.size)
+    desc = B.MsdaDesc(n, q, heads, dh, len(MSDA_SHAPES), pts, 1, B.DCN_F32)
+    shapes = (ctypes.c_int32 * 8)(*[v for hw in MSDA_SHAPES for v in hw])
+    base = [upload(torch, a, "f32") for a in (d["value"], d["loc"], d["attn"], g)]
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        ins = [t.clone() for t in base] if i else base
+        outs = [torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])]
+        keep += ins + outs
+        args.append((ctypes.byref(desc), shapes) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + outs) +
+                    (ctypes.c_void_p(stream.cuda_stream),))
+    r = Runner("msda_bwd_encoder_f32", args, B.lib().msda_backward, n * q * heads * dh * len(MSDA_SHAPES) * pts,
+               min_bytes, stream)
+    r.keep = keep
+    return r
+
+
 def time_steps(torch, r, steps, warmup):
     """Contract timing: warmup, then exactly `steps` launches bracketed by
     synchronisation.  Returns wall ms per step."""
@@ -280,7 +304,9 @@ def main():
         name = args.only
         if name == "copy_calib":
             return copy_calib(torch, args.steps, args.warmup)
-        if name.startswith("msda"):
+        if name.startswith("msda_bwd"):
+            r = msda_bwd_runner(torch)
+        elif name.startswith("msda"):
             r = msda_runner(torch)
         elif "_bwd_" in name:
             r = dcn_bwd_runner(torch, name.startswith("dcnv3"))
@@ -315,6 +341,10 @@ def main():
             del r
         r = msda_runner(torch)
         secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+        del r
+        r = msda_bwd_runner(torch)
+        secondary[r.name] = summarize(r, time_steps(torch, r, 10, 2), kernel_ms(torch, r, 10))
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
         torch.cuda.empty_cache()

@@ -26,6 +26,10 @@
  *                jointly, a bilinear read of every level at x = u*W_l - 1/2,
  *                y = v*H_l - 1/2 (zero outside, no clamping), and the
  *                weighted sum.
+ *  msda_backward Gradients of msda_forward with respect to value, loc and
+ *                attn (the read is differentiable in the location: "Deformable
+ *                DETR...", "A learned location can fall between cells"; the
+ *                joint softmax backward: "Mix samples with a per-head budget").
  *
  * Conventions (the pages leave these open; oracle and kernels hold them alike):
  *  - Tap k of a kernel_h x kernel_w grid sits at kx = k / kernel_h,
@@ -123,6 +127,21 @@ dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset,
  * value, loc, attn, out: device pointers in f32.  Element counts below 2^31. */
 dcn_status msda_forward(const msda_desc* desc, const int32_t* spatial_shapes, const void* value,
                         const void* loc, const void* attn, void* out, void* stream);
+
+/* Gradients of msda_forward given grad_out ([n][len_q][heads][head_dim]).
+ * grad_value ([n][S][heads][head_dim]) is OVERWRITTEN: zero-filled on
+ * `stream`, then accumulated with fp32 atomics, so its low bits depend on the
+ * order of the atomics.  grad_loc and grad_attn (the layouts of loc and attn)
+ * are overwritten; with softmax=1 grad_attn is the gradient with respect to
+ * the logits passed in `attn`.  Any of grad_value, grad_loc, grad_attn may be
+ * NULL to skip it.  A sample that falls outside its level has zero location
+ * gradient; at a coordinate that is exactly an integer the derivative of the
+ * cell above the floor (the right-hand derivative) is returned.
+ * desc->dtype must be DCN_F32 (otherwise DCN_ERR_UNSUPPORTED); the other
+ * requirements are those of msda_forward. */
+dcn_status msda_backward(const msda_desc* desc, const int32_t* spatial_shapes, const void* value,
+                         const void* loc, const void* attn, const void* grad_out, void* grad_value,
+                         void* grad_loc, void* grad_attn, void* stream);
 
 /* Static name of a status code. */
 const char* dcn_status_str(dcn_status status);

@@ -21,7 +21,7 @@ import ctypes
 
 from . import _binding as _b
 
-__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "DcnError"]
+__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_backward", "DcnError"]
 
 DcnError = _b.DcnError
 
@@ -131,3 +131,28 @@ def msda_forward(value, spatial_shapes, loc, attn, softmax=True, out=None):
     _b.check(_b.lib().msda_forward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn), _ptr(out),
                                    _stream(dev)))
     return out
+
+
+def msda_backward(value, spatial_shapes, loc, attn, grad_out, softmax=True, need_value=True, need_loc=True,
+                  need_attn=True):
+    """Gradients (grad_value, grad_loc, grad_attn) of msda_forward; a
+    gradient that is not needed comes back as None and is not computed."""
+    dev = _check_tensors(value, loc, attn, grad_out)
+    n, S, M, Dh = value.shape
+    if loc.dim() != 6 or loc.shape[-1] != 2:
+        raise ValueError("loc must be [n, q, heads, L, P, 2]")
+    _, Q, M2, L, P, _ = loc.shape
+    if (loc.shape[0] != n or M2 != M or tuple(attn.shape) != (n, Q, M, L, P) or len(spatial_shapes) != L
+            or tuple(grad_out.shape) != (n, Q, M, Dh)):
+        raise ValueError("inconsistent value/loc/attn/grad_out/spatial_shapes")
+    shapes = (ctypes.c_int32 * (2 * L))(*[int(v) for hw in spatial_shapes for v in hw])
+    if sum(int(h) * int(w) for h, w in spatial_shapes) != S:
+        raise ValueError("sum of H_l*W_l must equal value.shape[1]")
+    desc = _b.MsdaDesc(n, Q, M, Dh, L, P, int(bool(softmax)), _dtype_code(value))
+    torch = _torch()
+    gv = torch.empty_like(value) if need_value else None
+    gl = torch.empty_like(loc) if need_loc else None
+    ga = torch.empty_like(attn) if need_attn else None
+    _b.check(_b.lib().msda_backward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn), _ptr(grad_out),
+                                    _ptr(gv), _ptr(gl), _ptr(ga), _stream(dev)))
+    return gv, gl, ga

@@ -29,7 +29,7 @@ class MsdaDesc(ctypes.Structure):
                 ("n", "len_q", "heads", "head_dim", "levels", "points", "softmax", "dtype")]
 
 
-EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "dcn_status_str",
+EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_backward", "dcn_status_str",
            "dcn_last_error")
 
 _lib = None
@@ -54,6 +54,9 @@ def lib():
     L.dcn_backward.restype = ctypes.c_int
     L.msda_forward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp]
     L.msda_forward.restype = ctypes.c_int
+    L.msda_backward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
+                                vp]
+    L.msda_backward.restype = ctypes.c_int
     L.dcn_status_str.argtypes = [ctypes.c_int]
     L.dcn_status_str.restype = ctypes.c_char_p
     L.dcn_last_error.argtypes = []

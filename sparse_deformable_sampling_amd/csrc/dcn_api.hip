@@ -145,8 +145,8 @@ dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset,
                                                (float*)grad_mask, (hipStream_t)stream));
 }
 
-dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
-                        const void* attn, void* out, void* stream)
+// Validation shared by the MSDA entry points; fills G on success.
+static dcn_status msda_geom(const msda_desc* d, const int32_t* shapes, dcn::MsdaGeom& G)
 {
     if (!d) return fail(DCN_ERR_INVALID, "desc is NULL");
     if (d->n < 1 || d->len_q < 1 || d->heads < 1 || d->head_dim < 1 || d->levels < 1 || d->points < 1)
@@ -157,7 +157,6 @@ dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* v
     if (!shapes) return fail(DCN_ERR_INVALID, "spatial_shapes is NULL");
     if (d->levels > dcn::MSDA_MAX_LEVELS)
         return fail(DCN_ERR_UNSUPPORTED, "at most %d levels are supported", dcn::MSDA_MAX_LEVELS);
-    dcn::MsdaGeom G;
     G.n = d->n; G.q = d->len_q; G.m = d->heads; G.dh = d->head_dim; G.L = d->levels; G.P = d->points;
     G.softmax = d->softmax;
     int64_t S = 0;
@@ -177,14 +176,44 @@ dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* v
         nq * d->head_dim >= kMaxElems)
         return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
     G.S = (int)S;
+    return DCN_OK;
+}
+
+dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                        const void* attn, void* out, void* stream)
+{
+    dcn::MsdaGeom G;
+    dcn_status st = msda_geom(d, shapes, G);
+    if (st) return st;
     if (!value || !loc || !attn || !out) return fail(DCN_ERR_INVALID, "value, loc, attn and out must not be NULL");
     if (d->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "msda_forward supports f32 only");
-    dcn_status st;
     if ((st = check_ptr(value, "value", 4)) || (st = check_ptr(loc, "loc", 4)) || (st = check_ptr(attn, "attn", 4)) ||
         (st = check_ptr(out, "out", 4)))
         return st;
     return hip_status(dcn::launch_msda_forward(G, (const float*)value, (const float*)loc, (const float*)attn,
                                                (float*)out, (hipStream_t)stream));
+}
+
+dcn_status msda_backward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                         const void* attn, const void* grad_out, void* grad_value, void* grad_loc, void* grad_attn,
+                         void* stream)
+{
+    dcn::MsdaGeom G;
+    dcn_status st = msda_geom(d, shapes, G);
+    if (st) return st;
+    if (!value || !loc || !attn || !grad_out)
+        return fail(DCN_ERR_INVALID, "value, loc, attn and grad_out must not be NULL");
+    if (d->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "msda_backward supports f32 only");
+    if ((st = check_ptr(value, "value", 4)) || (st = check_ptr(loc, "loc", 4)) || (st = check_ptr(attn, "attn", 4)) ||
+        (st = check_ptr(grad_out, "grad_out", 4)))
+        return st;
+    if (grad_value && (st = check_ptr(grad_value, "grad_value", 4))) return st;
+    if (grad_loc && (st = check_ptr(grad_loc, "grad_loc", 4))) return st;
+    if (grad_attn && (st = check_ptr(grad_attn, "grad_attn", 4))) return st;
+    if (!grad_value && !grad_loc && !grad_attn) return ok();
+    return hip_status(dcn::launch_msda_backward(G, (const float*)value, (const float*)loc, (const float*)attn,
+                                                (const float*)grad_out, (float*)grad_value, (float*)grad_loc,
+                                                (float*)grad_attn, (hipStream_t)stream));
 }
 
 }  // extern "C"

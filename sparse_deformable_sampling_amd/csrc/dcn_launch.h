@@ -35,5 +35,7 @@ hipError_t launch_dcn_backward(const Geom& g, const float* x, const float* off, 
                                const float* gout, float* gx, float* goff, float* gmask, hipStream_t s);
 hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
                                float* out, hipStream_t s);
+hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
+                                const float* gout, float* gvalue, float* gloc, float* gattn, hipStream_t s);
 
 }  // namespace dcn

@@ -144,6 +144,37 @@ def test_msda_validation():
     assert call(n=1 << 20, len_q=1 << 12) == B.DCN_ERR_INVALID
 
 
+def test_msda_backward_validation():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    shapes = (ctypes.c_int32 * 4)(4, 5, 2, 3)
+    ok = dict(n=1, len_q=3, heads=2, head_dim=8, levels=2, points=2, softmax=1, dtype=B.DCN_F32)
+    inputs = (0x1000, 0x2000, 0x3000, 0x4000)   # value, loc, attn, grad_out
+
+    def call(shp=shapes, ins=inputs, grads=(0x5000, 0x6000, 0x7000), **over):
+        d = dict(ok)
+        d.update(over)
+        desc = B.MsdaDesc(**d)
+        args = [vp(p) if p else None for p in tuple(ins) + tuple(grads)]
+        return L.msda_backward(ctypes.byref(desc), shp, *args, None)
+
+    assert call(levels=0) == B.DCN_ERR_INVALID
+    assert call(head_dim=0) == B.DCN_ERR_INVALID
+    assert call(softmax=2) == B.DCN_ERR_INVALID
+    assert call(dtype=7) == B.DCN_ERR_INVALID
+    assert call(shp=None) == B.DCN_ERR_INVALID
+    assert call(shp=(ctypes.c_int32 * 4)(4, 5, -1, 3)) == B.DCN_ERR_INVALID
+    assert call(ins=(0x1000, 0x2000, 0x3000, 0)) == B.DCN_ERR_INVALID      # grad_out is required
+    assert call(ins=(0, 0x2000, 0x3000, 0x4000)) == B.DCN_ERR_INVALID
+    assert call(dtype=B.DCN_BF16) == B.DCN_ERR_UNSUPPORTED
+    assert call(grads=(0x5002, 0x6000, 0x7000)) == B.DCN_ERR_UNSUPPORTED  # misaligned grad_value
+    assert call(grads=(0x5000, 0x6001, 0x7000)) == B.DCN_ERR_UNSUPPORTED
+    assert call(levels=17, shp=(ctypes.c_int32 * 34)(*([2] * 34))) == B.DCN_ERR_UNSUPPORTED
+    assert call(n=1 << 20, len_q=1 << 12) == B.DCN_ERR_INVALID
+    # nothing requested: nothing is enqueued
+    assert call(grads=(0, 0, 0)) == B.DCN_OK
+
+
 def test_torch_wrappers_refuse_cpu_tensors():
     import torch
     import sparse_deformable_sampling_amd as sds

@@ -351,3 +351,79 @@ def test_msda_tiled_shapes(sds, n, shapes, q, heads, dh, points):
 def test_msda_levels_points(sds, shapes, points):
     for softmax in (True, False):
         check_msda(sds, "msda-lp", 2, shapes, 17, 2, 8, points, softmax=softmax, seed=43, offset_std=4.0)
+
+
+# ---------------------------------------------------------------- MSDA backward
+
+
+# grad_value elements are fp32 sums of atomically added terms, one per
+# (query, sample, corner) that lands on the cell; at the encoder shape a cell
+# of the 13x17 level takes about 17821*4*4/221 ~ 1300 of them per head.  The
+# round-off of a k-term fp32 sum is bounded by about k * 2^-24 of the sum of
+# the terms' magnitudes (~8e-5 for k = 1300), hence a 1e-4 bar for that
+# output; grad_loc and grad_attn are per-sample sums over head_dim channels
+# and keep the f32 bar.
+MSDA_BWD_TOL = (1e-4, TOL["f32"], TOL["f32"])
+
+
+def check_msda_bwd(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0):
+    import torch
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed)
+    g = synth.store(np.random.default_rng(seed + 1000).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
+    v, loc, attn, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
+    say(name, (n, shapes, q, heads, dh, points), softmax)
+    gv, gl, ga = sds.msda_backward(v, shapes, loc, attn, go, softmax=softmax)
+    torch.cuda.synchronize()
+    rv, rl, ra = oracle.msda_backward(d["value"], shapes, d["loc"], d["attn"], g, softmax=softmax)
+    errs = (rel_err(to_host(gv), rv), rel_err(to_host(gl), rl), rel_err(to_host(ga), ra))
+    assert all(e <= t for e, t in zip(errs, MSDA_BWD_TOL)), (name, softmax, errs)
+    return errs
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_msda_backward_encoder_full(sds, softmax):
+    """Batch 8, 4 levels (100x134 .. 13x17), all 17821 positions as queries,
+    8 heads x 32, 4 points per level."""
+    check_msda_bwd(sds, "msda-bwd-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4, softmax=softmax)
+
+
+@pytest.mark.parametrize("n,shapes,q,heads,dh,points", [
+    (2, [(6, 5), (3, 3)], 77, 3, 4, 8),          # tiled: 16 samples, 4 lanes per query
+    (2, [(9, 7), (5, 4)], 50, 5, 64, 2),         # tiled: 64 lanes per query
+    (1, [(4, 4)], 9, 1, 1, 32),                  # tiled: one channel, 32 samples
+    (3, [(7, 6), (4, 3), (2, 2), (1, 1)], 45, 2, 16, 8),
+    (2, [(7, 9), (4, 5)], 23, 3, 36, 3),         # generic: 6 samples, head_dim 36
+    (2, [(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 17, 2, 8, 2),   # generic: 10 samples
+])
+def test_msda_backward_shapes(sds, n, shapes, q, heads, dh, points):
+    for softmax in (True, False):
+        check_msda_bwd(sds, "msda-bwd", n, shapes, q, heads, dh, points, softmax=softmax, seed=53, offset_std=3.0)
+
+
+def test_msda_backward_far_outside_and_partial_outputs(sds):
+    import torch
+    shapes = [(6, 5), (3, 4)]
+    n, q, heads, dh, points = 2, 33, 2, 8, 4
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, seed=59)
+    loc = d["loc"].copy()
+    loc[0, 3, 1, 0, 2] = [-2.5, 0.5]
+    loc[1, 7, 0, 1, 1] = [0.5, 3.0]
+    loc[1, 8, 1, 1, 3] = [1.0 + 0.5 / 4, 0.5]     # x exactly at W: outside
+    d["loc"] = synth.store(loc, "f32")
+    g = synth.store(np.random.default_rng(5).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
+    v, lc, at, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
+    rv, rl, ra = oracle.msda_backward(d["value"], shapes, d["loc"], d["attn"], g, softmax=True)
+    say("msda-bwd-partial")
+    full = sds.msda_backward(v, shapes, lc, at, go)
+    torch.cuda.synchronize()
+    for got, ref, tol in zip(full, (rv, rl, ra), MSDA_BWD_TOL):
+        assert rel_err(to_host(got), ref) <= tol
+    assert np.all(to_host(full[1])[0, 3, 1, 0, 2] == 0.0)
+    for need in [(True, False, False), (False, True, False), (False, False, True)]:
+        got = sds.msda_backward(v, shapes, lc, at, go, need_value=need[0], need_loc=need[1], need_attn=need[2])
+        torch.cuda.synchronize()
+        for flag, t, ref, tol in zip(need, got, (rv, rl, ra), MSDA_BWD_TOL):
+            if flag:
+                assert rel_err(to_host(t), ref) <= tol
+            else:
+                assert t is None
