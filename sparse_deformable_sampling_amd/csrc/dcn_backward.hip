@@ -14,6 +14,8 @@
 // and, for DCNv3's softmax ("InternImage...", Ch.3),
 //   dL/dz_k = m_k (dL/dm_k - sum_j m_j dL/dm_j).
 #include "dcn_device.h"
+#include "dcn_bwd_win.h"
+#include "dcn_ring.h"
 
 namespace dcn {
 
@@ -274,6 +276,13 @@ hipError_t launch_dcn_backward(const Geom& G, const float* x, const float* off, 
         fill_zero<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(gx, nx);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        // grad_x requested: sum the scatter in LDS (dcn_backward_win.hip)
+        // when the window of grad_x rows fits.
+        int lds_limit, num_cus;
+        device_limits(&lds_limit, &num_cus);
+        BwdWinCfg bc;
+        if (plan_bwd_win(G, x, gout, lds_limit, num_cus, &bc))
+            return launch_dcn_backward_win(G, bc, x, off, mask, gout, gx, goff, gmask, s);
     }
     return G.softmax ? launch_typed<true>(G, x, off, mask, gout, gx, goff, gmask, s)
                      : launch_typed<false>(G, x, off, mask, gout, gx, goff, gmask, s);

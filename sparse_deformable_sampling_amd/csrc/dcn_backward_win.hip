@@ -1,0 +1,353 @@
+// DCN backward with grad_x accumulated on chip, for gfx950 (fp32).
+//
+// The gradients are those of dcn_backward.hip (the derivative of y_g(p0) =
+// sum_k m_gk x_g(p0 + p_k + dp_gk), "DCNv4: Unbounded Weights", "Why Is
+// Sampling Just 9 Points Still Slow?", through the bilinear read of
+// "InternImage: Deformable Convolutions at Scale", Ch.2).  What differs is
+// how the scatter into grad_x is summed.
+//
+// fp32 atomics into global memory are served at about 21 G requests of up to
+// 64 bytes per second on this chip, so scattering 36 corner contributions per
+// (pixel, group, channel) straight to grad_x is bound by them.  LDS integer
+// atomics run about twenty times faster (ds_add_u64 ~7 lanes/clk/CU), LDS
+// float atomics do not (ds_add_f32 ~0.3 lanes/clk/CU).  So each workgroup
+// owns one image, one channel group and a chunk of output rows, walks down
+// the chunk a few rows per step, and keeps a window of grad_x rows of its
+// group in LDS as 64-bit fixed-point sums:
+//  - a contribution v to a cell whose row is in the window is added as
+//    round-down(v * 2^e) with ds_add_u64; its row leaves the window once no
+//    later output row of the chunk can reach it through LDS, and is then
+//    converted back to fp32 and added to grad_x with one fp32 atomic per
+//    element (neighbouring chunks share halo rows);
+//  - a contribution to a row outside the window (an offset beyond the halo)
+//    goes to grad_x with an fp32 atomic directly.
+// The scale 2^e is chosen per workgroup from the bound S = sum over its items
+// of (sum_k |m_k|) * max_c |g_c|, which no cell's sum can exceed: e makes
+// S * 2^e < 2^61, so the 64-bit sums cannot overflow and resolve 2^-61 of S.
+// Non-finite inputs, or an S outside [2^-60, 2^60), turn the fixed-point path
+// off for that workgroup (every contribution then takes the fp32 atomic).
+// Integer sums do not depend on the order of the additions.
+#include <algorithm>
+
+#include "dcn_device.h"
+#include "dcn_bwd_win.h"
+
+namespace dcn {
+
+namespace {
+
+constexpr uint32_t OOB = 0x80000000u;
+constexpr int KMAX_WIN = 64;
+
+__device__ __forceinline__ float lane_sum(float v, int width)
+{
+    for (int o = 1; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Fixed-point image of t (|t| < 2^31): floor(t * 2^32) as a two's-complement
+// 64-bit integer.
+__device__ __forceinline__ unsigned long long to_fixed(float t)
+{
+    const float fl = floorf(t);
+    const uint32_t hi = (uint32_t)(int)fl;
+    const uint32_t lo = (uint32_t)fminf((t - fl) * 4294967296.0f, 4294967040.0f);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int KH, int KW, bool SOFTMAX>
+__global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const float* __restrict__ x,
+                                                   const float* __restrict__ off, const float* __restrict__ mask,
+                                                   const float* __restrict__ gout, float* __restrict__ gx,
+                                                   float* __restrict__ goff, float* __restrict__ gmask)
+{
+    constexpr int KF = KH * KW;
+    extern __shared__ unsigned long long acc[];   // [aw][w][d] fixed-point sums
+    __shared__ float red_s[16];
+    __shared__ int red_bad[16];
+    const int K = KF ? KF : G.K;
+    const int kh = KH ? KH : G.kh;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    int L = blockIdx.x;
+    if (bc.nwg % 8 == 0) L = (blockIdx.x % 8) * (bc.nwg / 8) + blockIdx.x / 8;   // neighbours share an XCD
+    const int chunk = L % bc.chunks;
+    const int ng = L / bc.chunks;
+    const int g = ng % G.g, n = ng / G.g;
+    const int r_begin = chunk * bc.chunk_rows;
+    const int r_end = min(G.ho, r_begin + bc.chunk_rows);
+    if (r_begin >= r_end) return;
+    const int D = G.d, C = G.c, W = G.w, H = G.h;
+    const int rowe = W * D;                          // elements of one window row
+    const int wlo0 = r_begin * G.sh - G.ph - bc.hy - 1;
+    const int lq = 1 << bc.lq_log;
+    const int li = tid >> bc.lq_log, c4 = tid & (lq - 1);
+
+    // ---- the bound S of this workgroup, and whether every input is finite
+    float part = 0.f;
+    int bad = 0;
+    const int nitems = (r_end - r_begin) * G.wo;
+    for (int it = tid; it < nitems; it += nthr) {
+        const long pix = ((long)n * G.ho + r_begin + it / G.wo) * G.wo + it % G.wo;
+        const long item = pix * G.g + g;
+        float ms = 0.f;
+        for (int k = 0; k < K; ++k) {
+            const float v = mask[item * K + k];
+            ms += fabsf(v);
+            bad |= !(fabsf(v) <= 3.0e38f);
+        }
+        if (SOFTMAX) ms = 1.f;
+        float gm = 0.f;
+        for (int c = 0; c < D; ++c) {
+            const float v = gout[pix * C + (long)g * D + c];
+            gm = fmaxf(gm, fabsf(v));
+            bad |= !(fabsf(v) <= 3.0e38f);
+        }
+        part += ms * gm;
+    }
+    part = lane_sum(part, 64);
+    for (int o = 1; o < 64; o <<= 1) bad |= __shfl_xor(bad, o, 64);
+    if ((tid & 63) == 0) {
+        red_s[tid >> 6] = part;
+        red_bad[tid >> 6] = bad;
+    }
+    __syncthreads();
+    float S = 0.f;
+    bad = 0;
+    for (int w = 0; w < (nthr + 63) / 64; ++w) {
+        S += red_s[w];
+        bad |= red_bad[w];
+    }
+    const bool fixed = !bad && S >= 0x1p-60f && S < 0x1p60f;
+    int ex = 0;
+    if (fixed) (void)frexpf(S, &ex);        // S < 2^ex
+    const int e = 61 - ex;                   // S * 2^e < 2^61
+    const float tscale = ldexpf(1.f, e - 32);
+    const float s_hi = ldexpf(1.f, 32 - e), s_lo = ldexpf(1.f, -e);
+
+    for (int i = tid; i < bc.aw * rowe; i += nthr) acc[i] = 0ull;
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)bc.x_bytes, 0x00020000);
+    const long img = (long)n * H * W * C;
+    const int items_step = bc.tr * G.wo;
+    const int nsteps = (r_end - r_begin + bc.tr - 1) / bc.tr;
+    for (int s = 0; s < nsteps; ++s) {
+        const int r_s = r_begin + s * bc.tr;
+        const int lo = wlo0 + s * bc.tr * G.sh;       // first row of this step's window
+        for (int p0 = 0; p0 < items_step; p0 += bc.ip) {
+            const int it = p0 + li;
+            const int r = r_s + it / G.wo, wo = it % G.wo;
+            // All lanes of an item share `live`, so the item's reductions are whole.
+            if (it >= items_step || r >= r_end) continue;
+            const long pix = ((long)n * G.ho + r) * G.wo + wo;
+            const long item = pix * G.g + g;
+            float m[KF ? KF : KMAX_WIN], dm[KF ? KF : KMAX_WIN];
+#pragma unroll
+            for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                if (!KF && k >= K) break;
+                m[k] = mask[item * K + k];
+            }
+            if constexpr (SOFTMAX) {
+                float mx = m[0];
+#pragma unroll
+                for (int k = 1; k < (KF ? KF : KMAX_WIN); ++k) {
+                    if (!KF && k >= K) break;
+                    mx = fmaxf(mx, m[k]);
+                }
+                float sum = 0.f;
+#pragma unroll
+                for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                    if (!KF && k >= K) break;
+                    m[k] = exp_nonpos(m[k] - mx);
+                    sum += m[k];
+                }
+                const float inv = 1.0f / sum;
+#pragma unroll
+                for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                    if (!KF && k >= K) break;
+                    m[k] *= inv;
+                }
+            }
+            const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + 4 * c4);
+            const float gc[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float* ob = off + item * K * 2;
+            const int bx = wo * G.sw - G.pw, by = r * G.sh - G.ph;
+            float sdm = 0.f;
+#pragma unroll
+            for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                if (!KF && k >= K) break;
+                const int kx = k / kh, ky = k - kx * kh;
+                const float tx = G.scale * ob[2 * k], ty = G.scale * ob[2 * k + 1];
+                float sm = 0.f, sdx = 0.f, sdy = 0.f;
+                if (coord_ok(tx) && coord_ok(ty)) {
+                    const float fx = floorf(tx), fy = floorf(ty);
+                    const float a = tx - fx, b = ty - fy;
+                    const int x0 = bx + kx * G.dw + (int)fx;
+                    const int y0 = by + ky * G.dh + (int)fy;
+                    if (x0 >= -1 && x0 < W && y0 >= -1 && y0 < H) {
+                        const bool cx0 = x0 >= 0, cx1 = x0 + 1 < W, cy0 = y0 >= 0, cy1 = y0 + 1 < H;
+                        // element offsets of corner (y0, x0), channel 4*c4, and the buffer byte offsets
+                        const long e00 = img + ((long)y0 * W + x0) * C + (long)g * D + 4 * c4;
+                        const uint32_t b00 = (uint32_t)(e00 * 4);
+                        const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
+                        const u32x4 q00 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy0 && cx0) ? b00 : OOB, 0, 0);
+                        const u32x4 q01 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy0 && cx1) ? b00 + bC : OOB, 0, 0);
+                        const u32x4 q10 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy1 && cx0) ? b00 + bR : OOB, 0, 0);
+                        const u32x4 q11 =
+                            __builtin_amdgcn_raw_buffer_load_b128(xr, (cy1 && cx1) ? b00 + bR + bC : OOB, 0, 0);
+                        const float X00[4] = {__uint_as_float(q00.x), __uint_as_float(q00.y), __uint_as_float(q00.z),
+                                              __uint_as_float(q00.w)};
+                        const float X01[4] = {__uint_as_float(q01.x), __uint_as_float(q01.y), __uint_as_float(q01.z),
+                                              __uint_as_float(q01.w)};
+                        const float X10[4] = {__uint_as_float(q10.x), __uint_as_float(q10.y), __uint_as_float(q10.z),
+                                              __uint_as_float(q10.w)};
+                        const float X11[4] = {__uint_as_float(q11.x), __uint_as_float(q11.y), __uint_as_float(q11.z),
+                                              __uint_as_float(q11.w)};
+                        const float wa = 1.f - a, wb = 1.f - b;
+                        const float w4[4] = {wa * wb, a * wb, wa * b, a * b};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float v = w4[0] * X00[j] + w4[1] * X01[j] + w4[2] * X10[j] + w4[3] * X11[j];
+                            sm = fmaf(gc[j], v, sm);
+                            sdx = fmaf(gc[j], wb * (X01[j] - X00[j]) + b * (X11[j] - X10[j]), sdx);
+                            sdy = fmaf(gc[j], wa * (X10[j] - X00[j]) + a * (X11[j] - X01[j]), sdy);
+                        }
+                        if (gx) {
+                            const bool cin[4] = {cy0 && cx0, cy0 && cx1, cy1 && cx0, cy1 && cx1};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                if (!cin[q]) continue;
+                                const int yc = y0 + (q >> 1), xc = x0 + (q & 1);
+                                const float mw = m[k] * w4[q];
+                                if (fixed && yc >= lo && yc < lo + bc.aw) {
+                                    unsigned long long* dst =
+                                        acc + ((yc - wlo0) % bc.aw) * rowe + xc * D + 4 * c4;
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, to_fixed(mw * gc[j] * tscale));
+                                } else {
+                                    float* dst = gx + img + ((long)yc * W + xc) * C + (long)g * D + 4 * c4;
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, mw * gc[j]);
+                                }
+                            }
+                        }
+                    }
+                }
+                sm = lane_sum(sm, lq);
+                sdx = lane_sum(sdx, lq);
+                sdy = lane_sum(sdy, lq);
+                dm[k] = sm;
+                sdm += m[k] * sm;
+                if (c4 == 0 && goff) {
+                    goff[(item * K + k) * 2 + 0] = G.scale * m[k] * sdx;
+                    goff[(item * K + k) * 2 + 1] = G.scale * m[k] * sdy;
+                }
+            }
+            if (c4 == 0 && gmask) {
+#pragma unroll
+                for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                    if (!KF && k >= K) break;
+                    gmask[item * K + k] = SOFTMAX ? m[k] * (dm[k] - sdm) : dm[k];
+                }
+            }
+        }
+        __syncthreads();
+        // Rows that leave the window (all of them after the last step) go to
+        // grad_x; their slots are cleared for the rows that enter.
+        if (gx) {
+            const int nflush = s + 1 < nsteps ? bc.tr * G.sh : bc.aw;
+            for (int i = tid; i < nflush * rowe; i += nthr) {
+                const int rr = i / rowe, el = i - rr * rowe;
+                const int y = lo + rr;
+                unsigned long long* a = acc + ((y - wlo0) % bc.aw) * rowe + el;
+                const unsigned long long q = *a;
+                if (q != 0ull) {
+                    *a = 0ull;
+                    const float v = (float)(int)(uint32_t)(q >> 32) * s_hi + (float)(uint32_t)q * s_lo;
+                    const int xc = el / D, c = el - xc * D;
+                    atomicAdd(gx + img + ((long)y * W + xc) * C + (long)g * D + c, v);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace
+
+bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit, int num_cus, BwdWinCfg* bc)
+{
+    if (G.d % 4 != 0) return false;
+    const int lq = G.d / 4;
+    if (lq > 64 || (lq & (lq - 1)) != 0) return false;
+    if (G.K > KMAX_WIN) return false;
+    if ((uintptr_t)x % 16 || (uintptr_t)gout % 16) return false;
+    const long x_bytes = (long)G.n * G.h * G.w * G.c * 4;
+    if (x_bytes >= (1L << 31) - 64) return false;
+    int lq_log = 0;
+    while ((1 << lq_log) < lq) ++lq_log;
+    const int ip_max = 512 / lq;   // items per pass with 512 threads
+    int tr, threads;
+    if (G.wo <= ip_max) {          // one pass per step of tr output rows
+        tr = std::max(1, std::min(ip_max / G.wo, G.ho));
+        threads = (tr * G.wo * lq + 63) / 64 * 64;
+    } else {                       // one output row per step, several passes
+        tr = 1;
+        threads = 512;
+    }
+    const int ipass = threads / lq;
+    const long row_bytes = (long)G.w * G.d * 8;
+    int hy = -1, aw = 0;
+    for (int h = 8; h >= 2; --h) {
+        const int awh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 * h + 3;
+        if ((long)awh * row_bytes + 256 <= lds_limit) {
+            hy = h;
+            aw = awh;
+            break;
+        }
+    }
+    if (hy < 0) return false;
+    const long units = (long)G.n * G.g;
+    int chunks = (int)std::max(1L, ((long)num_cus + units - 1) / units);
+    chunks = std::min(chunks, (G.ho + tr - 1) / tr);
+    int chunk_rows = (G.ho + chunks - 1) / chunks;
+    chunk_rows = (chunk_rows + tr - 1) / tr * tr;
+    chunks = (G.ho + chunk_rows - 1) / chunk_rows;
+    if (units * chunks >= (1L << 31)) return false;
+    bc->lq_log = lq_log;
+    bc->ip = ipass;
+    bc->tr = tr;
+    bc->hy = hy;
+    bc->aw = aw;
+    bc->chunk_rows = chunk_rows;
+    bc->chunks = chunks;
+    bc->nwg = (int)(units * chunks);
+    bc->threads = threads;
+    bc->lds_bytes = (int)(aw * row_bytes);
+    bc->x_bytes = (uint32_t)x_bytes;
+    return true;
+}
+
+hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, const float* x, const float* off,
+                                   const float* mask, const float* gout, float* gx, float* goff, float* gmask,
+                                   hipStream_t s)
+{
+    const dim3 grid(bc.nwg), block(bc.threads);
+#define DCN_BWIN(KHV, KWV, SM)                                                                                   \
+    {                                                                                                           \
+        auto* fn = dcn_bwd_win<KHV, KWV, SM>;                                                                   \
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,          \
+                                           bc.lds_bytes);                                                       \
+        if (e != hipSuccess) return e;                                                                          \
+        fn<<<grid, block, bc.lds_bytes, s>>>(G, bc, x, off, mask, gout, gx, goff, gmask);                        \
+    }
+    const bool k33 = G.kh == 3 && G.kw == 3;
+    if (k33 && G.softmax) DCN_BWIN(3, 3, true)
+    else if (k33) DCN_BWIN(3, 3, false)
+    else if (G.softmax) DCN_BWIN(0, 0, true)
+    else DCN_BWIN(0, 0, false)
+#undef DCN_BWIN
+    return hipGetLastError();
+}
+
+}  // namespace dcn

@@ -205,11 +205,14 @@ def test_invalid_call_leaves_output_untouched(sds):
 # ---------------------------------------------------------------- backward
 
 
-def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=TOL["f32"], **geom):
+def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=TOL["f32"], offset=("normal", 1.5), gscale=1.0,
+              **geom):
     kern = geom.get("kernel", 3)
     K = kern * kern if isinstance(kern, int) else kern[0] * kern[1]
     ho, wo = oracle.dcn_out_size(h, w, kern, geom.get("stride", 1), geom.get("pad", 1), geom.get("dil", 1))
-    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, dtype="f32", seed=seed, grad=True)
+    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, offset=offset, dtype="f32", seed=seed, grad=True)
+    if gscale != 1.0:
+        d["grad_out"] = synth.store(d["grad_out"] * np.float32(gscale), "f32")
     x, off, mask, go = (to_dev(d[k], "f32") for k in ("x", "offset", "mask", "grad_out"))
     say(name, "softmax=%d" % softmax, (n, h, w, c, g), geom)
     gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=g, softmax=softmax, **geom)
@@ -224,6 +227,21 @@ def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=TOL["f32"], **geom)
 def test_backward_stage1_full(sds, softmax):
     """DCNv3 and DCNv4 backward, f32, N=64 H=W=56 C=64 G=4, grad_out N(0,1)."""
     check_bwd(sds, "bwd-stage1", 64, 56, 56, 64, 4, softmax)
+
+
+@pytest.mark.parametrize("softmax", [True, False])
+def test_backward_wide_offsets(sds, softmax):
+    """Offsets N(0, 6): many corners land outside the rows a workgroup keeps
+    on chip and take the direct path into grad_x."""
+    check_bwd(sds, "bwd-wide", 8, 56, 56, 64, 4, softmax, seed=31, offset=("normal", 6.0))
+
+
+@pytest.mark.parametrize("gscale", [1e-30, 1e-12, 1e12, 1e30])
+def test_backward_gradient_scales(sds, gscale):
+    """Output gradients scaled far from 1: the on-chip sums pick their scale
+    from the data, or step aside when it is out of their range."""
+    check_bwd(sds, "bwd-scale", 4, 20, 24, 32, 2, False, seed=37, gscale=gscale)
+    check_bwd(sds, "bwd-scale", 4, 20, 24, 32, 2, True, seed=37, gscale=gscale)
 
 
 @pytest.mark.parametrize("softmax", [True, False])
