@@ -49,9 +49,8 @@ __device__ __forceinline__ float lane_sum(float v, int width)
 // 64-bit integer.
 __device__ __forceinline__ unsigned long long to_fixed(float t)
 {
-    const float fl = floorf(t);
-    const uint32_t hi = (uint32_t)(int)fl;
-    const uint32_t lo = (uint32_t)fminf((t - fl) * 4294967296.0f, 4294967040.0f);
+    const uint32_t hi = (uint32_t)(int)floorf(t);
+    const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(t) * 4294967296.0f);   // fract < 1 - 2^-24
     return ((unsigned long long)hi << 32) | lo;
 }
 
@@ -77,6 +76,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
     const int r_end = min(G.ho, r_begin + bc.chunk_rows);
     if (r_begin >= r_end) return;
     const int D = G.d, C = G.c, W = G.w, H = G.h;
+    const int d_log = bc.lq_log + 2;                 // D = 4 * lanes per item, a power of two
     const int rowe = W * D;                          // elements of one window row
     const int wlo0 = r_begin * G.sh - G.ph - bc.hy - 1;
     const int lq = 1 << bc.lq_log;
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
     const long img = (long)n * H * W * C;
     const int items_step = bc.tr * G.wo;
     const int nsteps = (r_end - r_begin + bc.tr - 1) / bc.tr;
+    int base_slot = 0;                               // ring slot of the window's first row
     for (int s = 0; s < nsteps; ++s) {
         const int r_s = r_begin + s * bc.tr;
         const int lo = wlo0 + s * bc.tr * G.sh;       // first row of this step's window
@@ -220,10 +221,12 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                                 const int yc = y0 + (q >> 1), xc = x0 + (q & 1);
                                 const float mw = m[k] * w4[q];
                                 if (fixed && yc >= lo && yc < lo + bc.aw) {
-                                    unsigned long long* dst =
-                                        acc + ((yc - wlo0) % bc.aw) * rowe + xc * D + 4 * c4;
+                                    int slot = base_slot + (yc - lo);
+                                    slot -= slot >= bc.aw ? bc.aw : 0;
+                                    unsigned long long* dst = acc + slot * rowe + (xc << d_log) + 4 * c4;
+                                    const float mws = mw * tscale;
 #pragma unroll
-                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, to_fixed(mw * gc[j] * tscale));
+                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, to_fixed(mws * gc[j]));
                                 } else {
                                     float* dst = gx + img + ((long)yc * W + xc) * C + (long)g * D + 4 * c4;
 #pragma unroll
@@ -256,20 +259,25 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
         // grad_x; their slots are cleared for the rows that enter.
         if (gx) {
             const int nflush = s + 1 < nsteps ? bc.tr * G.sh : bc.aw;
-            for (int i = tid; i < nflush * rowe; i += nthr) {
-                const int rr = i / rowe, el = i - rr * rowe;
+            for (int rr = 0; rr < nflush; ++rr) {
                 const int y = lo + rr;
-                unsigned long long* a = acc + ((y - wlo0) % bc.aw) * rowe + el;
-                const unsigned long long q = *a;
-                if (q != 0ull) {
-                    *a = 0ull;
-                    const float v = (float)(int)(uint32_t)(q >> 32) * s_hi + (float)(uint32_t)q * s_lo;
-                    const int xc = el / D, c = el - xc * D;
-                    atomicAdd(gx + img + ((long)y * W + xc) * C + (long)g * D + c, v);
+                int slot = base_slot + rr;
+                slot -= slot >= bc.aw ? bc.aw : 0;
+                unsigned long long* arow = acc + slot * rowe;
+                float* grow = gx + img + (long)y * W * C + (long)g * D;
+                for (int el = tid; el < rowe; el += nthr) {
+                    const unsigned long long q = arow[el];
+                    if (q != 0ull) {
+                        arow[el] = 0ull;
+                        const float v = (float)(int)(uint32_t)(q >> 32) * s_hi + (float)(uint32_t)q * s_lo;
+                        atomicAdd(grow + (long)(el >> d_log) * C + (el & (D - 1)), v);
+                    }
                 }
             }
             __syncthreads();
         }
+        base_slot += bc.tr * G.sh;
+        while (base_slot >= bc.aw) base_slot -= bc.aw;
     }
 }
 
