@@ -54,7 +54,9 @@ __device__ __forceinline__ unsigned long long to_fixed(float t)
     return ((unsigned long long)hi << 32) | lo;
 }
 
-template <int KH, int KW, bool SOFTMAX>
+// NV = 16-byte vectors (4 channels each) per lane; a (pixel, group) item has
+// D / (4 NV) lanes.
+template <int KH, int KW, bool SOFTMAX, int NV>
 __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const float* __restrict__ x,
                                                    const float* __restrict__ off, const float* __restrict__ mask,
                                                    const float* __restrict__ gout, float* __restrict__ gx,
@@ -76,8 +78,13 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
     const int r_end = min(G.ho, r_begin + bc.chunk_rows);
     if (r_begin >= r_end) return;
     const int D = G.d, C = G.c, W = G.w, H = G.h;
-    const int d_log = bc.lq_log + 2;                 // D = 4 * lanes per item, a power of two
-    const int rowe = W * D;                          // elements of one window row
+    constexpr int CPL = 4 * NV;                      // channels per lane
+    const int d_log = bc.lq_log + 2 + (NV == 2);     // D = CPL * lanes per item, a power of two
+    // A window row holds W pixels of D sums at a stride of D + 1 words: the
+    // odd stride spreads a wave's atomics over the LDS banks (with a
+    // power-of-two stride all of them would fall on a few).
+    const int pstr = D + 1;
+    const int rowe = W * pstr;                       // 8-byte words of one window row
     const int wlo0 = r_begin * G.sh - G.ph - bc.hy - 1;
     const int lq = 1 << bc.lq_log;
     const int li = tid >> bc.lq_log, c4 = tid & (lq - 1);
@@ -85,24 +92,35 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
     // ---- the bound S of this workgroup, and whether every input is finite
     float part = 0.f;
     int bad = 0;
+    // Same lane layout as the main pass: lane (item, chunk) reads its CPL
+    // channels of grad_out with 16-byte loads and every lq-th logit.
     const int nitems = (r_end - r_begin) * G.wo;
-    for (int it = tid; it < nitems; it += nthr) {
+    for (int it0 = 0; it0 < nitems; it0 += bc.ip) {
+        const int it = it0 + li;
+        if (it >= nitems) continue;   // whole items only: the reductions below stay within one item
         const long pix = ((long)n * G.ho + r_begin + it / G.wo) * G.wo + it % G.wo;
         const long item = pix * G.g + g;
         float ms = 0.f;
-        for (int k = 0; k < K; ++k) {
+        for (int k = c4; k < K; k += lq) {
             const float v = mask[item * K + k];
             ms += fabsf(v);
             bad |= !(fabsf(v) <= 3.0e38f);
         }
-        if (SOFTMAX) ms = 1.f;
         float gm = 0.f;
-        for (int c = 0; c < D; ++c) {
-            const float v = gout[pix * C + (long)g * D + c];
-            gm = fmaxf(gm, fabsf(v));
-            bad |= !(fabsf(v) <= 3.0e38f);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + CPL * c4 + 4 * v);
+            const float a4[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gm = fmaxf(gm, fabsf(a4[j]));
+                bad |= !(fabsf(a4[j]) <= 3.0e38f);
+            }
         }
-        part += ms * gm;
+        ms = lane_sum(ms, lq);
+        for (int o = 1; o < lq; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+        if (SOFTMAX) ms = 1.f;
+        if (c4 == 0) part += ms * gm;
     }
     part = lane_sum(part, 64);
     for (int o = 1; o < 64; o <<= 1) bad |= __shfl_xor(bad, o, 64);
@@ -169,70 +187,49 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                     m[k] *= inv;
                 }
             }
-            const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + 4 * c4);
-            const float gc[4] = {g4.x, g4.y, g4.z, g4.w};
+            float gc[CPL];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + CPL * c4 + 4 * v);
+                gc[4 * v] = g4.x;
+                gc[4 * v + 1] = g4.y;
+                gc[4 * v + 2] = g4.z;
+                gc[4 * v + 3] = g4.w;
+            }
             const float* ob = off + item * K * 2;
             const int bx = wo * G.sw - G.pw, by = r * G.sh - G.ph;
             float sdm = 0.f;
-#pragma unroll
-            for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
-                if (!KF && k >= K) break;
-                const int kx = k / kh, ky = k - kx * kh;
-                const float tx = G.scale * ob[2 * k], ty = G.scale * ob[2 * k + 1];
+            // One tap's channel sums, its writes of grad_offset, and its
+            // scatter into grad_x (LDS window or global), given its corners.
+            auto tap_finish = [&](int k, float a, float b, int x0, int y0, const uint32_t* o4, const float* X00,
+                                  const float* X01, const float* X10, const float* X11) {
                 float sm = 0.f, sdx = 0.f, sdy = 0.f;
-                if (coord_ok(tx) && coord_ok(ty)) {
-                    const float fx = floorf(tx), fy = floorf(ty);
-                    const float a = tx - fx, b = ty - fy;
-                    const int x0 = bx + kx * G.dw + (int)fx;
-                    const int y0 = by + ky * G.dh + (int)fy;
-                    if (x0 >= -1 && x0 < W && y0 >= -1 && y0 < H) {
-                        const bool cx0 = x0 >= 0, cx1 = x0 + 1 < W, cy0 = y0 >= 0, cy1 = y0 + 1 < H;
-                        // element offsets of corner (y0, x0), channel 4*c4, and the buffer byte offsets
-                        const long e00 = img + ((long)y0 * W + x0) * C + (long)g * D + 4 * c4;
-                        const uint32_t b00 = (uint32_t)(e00 * 4);
-                        const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
-                        const u32x4 q00 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy0 && cx0) ? b00 : OOB, 0, 0);
-                        const u32x4 q01 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy0 && cx1) ? b00 + bC : OOB, 0, 0);
-                        const u32x4 q10 = __builtin_amdgcn_raw_buffer_load_b128(xr, (cy1 && cx0) ? b00 + bR : OOB, 0, 0);
-                        const u32x4 q11 =
-                            __builtin_amdgcn_raw_buffer_load_b128(xr, (cy1 && cx1) ? b00 + bR + bC : OOB, 0, 0);
-                        const float X00[4] = {__uint_as_float(q00.x), __uint_as_float(q00.y), __uint_as_float(q00.z),
-                                              __uint_as_float(q00.w)};
-                        const float X01[4] = {__uint_as_float(q01.x), __uint_as_float(q01.y), __uint_as_float(q01.z),
-                                              __uint_as_float(q01.w)};
-                        const float X10[4] = {__uint_as_float(q10.x), __uint_as_float(q10.y), __uint_as_float(q10.z),
-                                              __uint_as_float(q10.w)};
-                        const float X11[4] = {__uint_as_float(q11.x), __uint_as_float(q11.y), __uint_as_float(q11.z),
-                                              __uint_as_float(q11.w)};
-                        const float wa = 1.f - a, wb = 1.f - b;
-                        const float w4[4] = {wa * wb, a * wb, wa * b, a * b};
+                const float wa = 1.f - a, wb = 1.f - b;
+                const float w4[4] = {wa * wb, a * wb, wa * b, a * b};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float v = w4[0] * X00[j] + w4[1] * X01[j] + w4[2] * X10[j] + w4[3] * X11[j];
-                            sm = fmaf(gc[j], v, sm);
-                            sdx = fmaf(gc[j], wb * (X01[j] - X00[j]) + b * (X11[j] - X10[j]), sdx);
-                            sdy = fmaf(gc[j], wa * (X10[j] - X00[j]) + a * (X11[j] - X01[j]), sdy);
-                        }
-                        if (gx) {
-                            const bool cin[4] = {cy0 && cx0, cy0 && cx1, cy1 && cx0, cy1 && cx1};
+                for (int j = 0; j < CPL; ++j) {
+                    const float v = w4[0] * X00[j] + w4[1] * X01[j] + w4[2] * X10[j] + w4[3] * X11[j];
+                    sm = fmaf(gc[j], v, sm);
+                    sdx = fmaf(gc[j], wb * (X01[j] - X00[j]) + b * (X11[j] - X10[j]), sdx);
+                    sdy = fmaf(gc[j], wa * (X10[j] - X00[j]) + a * (X11[j] - X01[j]), sdy);
+                }
+                if (gx) {
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                if (!cin[q]) continue;
-                                const int yc = y0 + (q >> 1), xc = x0 + (q & 1);
-                                const float mw = m[k] * w4[q];
-                                if (fixed && yc >= lo && yc < lo + bc.aw) {
-                                    int slot = base_slot + (yc - lo);
-                                    slot -= slot >= bc.aw ? bc.aw : 0;
-                                    unsigned long long* dst = acc + slot * rowe + (xc << d_log) + 4 * c4;
-                                    const float mws = mw * tscale;
+                    for (int q = 0; q < 4; ++q) {
+                        if (o4[q] == OOB) continue;   // corner outside the image
+                        const int yc = y0 + (q >> 1), xc = x0 + (q & 1);
+                        const float mw = m[k] * w4[q];
+                        if (fixed && yc >= lo && yc < lo + bc.aw) {
+                            int slot = base_slot + (yc - lo);
+                            slot -= slot >= bc.aw ? bc.aw : 0;
+                            unsigned long long* dst = acc + slot * rowe + xc * pstr + CPL * c4;
+                            const float mws = mw * tscale;
 #pragma unroll
-                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, to_fixed(mws * gc[j]));
-                                } else {
-                                    float* dst = gx + img + ((long)yc * W + xc) * C + (long)g * D + 4 * c4;
+                            for (int j = 0; j < CPL; ++j) atomicAdd(dst + j, to_fixed(mws * gc[j]));
+                        } else {
+                            float* dst = gx + img + ((long)yc * W + xc) * C + (long)g * D + CPL * c4;
 #pragma unroll
-                                    for (int j = 0; j < 4; ++j) atomicAdd(dst + j, mw * gc[j]);
-                                }
-                            }
+                            for (int j = 0; j < CPL; ++j) atomicAdd(dst + j, mw * gc[j]);
                         }
                     }
                 }
@@ -245,6 +242,108 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                     goff[(item * K + k) * 2 + 0] = G.scale * m[k] * sdx;
                     goff[(item * K + k) * 2 + 1] = G.scale * m[k] * sdy;
                 }
+            };
+            if constexpr (KF > 0) {
+                // Geometry of every tap first, branch-free: a corner outside the
+                // image gets an offset past the end of the buffer (it reads zero
+                // and is not scattered); offsets beyond +-2^24 (or not finite)
+                // are clamped there, which puts every corner outside.
+                const float lim = 16777216.0f;
+                uint32_t o4[KF][4];
+                float fa[KF], fb[KF];
+                int xk[KF], yk[KF];
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    const int kx = k / KH, ky = k - kx * KH;
+                    const float tx = fminf(fmaxf(G.scale * ob[2 * k], -lim), lim);
+                    const float ty = fminf(fmaxf(G.scale * ob[2 * k + 1], -lim), lim);
+                    const float fx = floorf(tx), fy = floorf(ty);
+                    fa[k] = tx - fx;
+                    fb[k] = ty - fy;
+                    const int x0 = bx + kx * G.dw + (int)fx, y0 = by + ky * G.dh + (int)fy;
+                    xk[k] = x0;
+                    yk[k] = y0;
+                    const bool cx0 = (unsigned)x0 < (unsigned)W, cx1 = (unsigned)(x0 + 1) < (unsigned)W;
+                    const bool cy0 = (unsigned)y0 < (unsigned)H, cy1 = (unsigned)(y0 + 1) < (unsigned)H;
+                    const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * 4);
+                    const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
+                    o4[k][0] = (cy0 && cx0) ? b00 : OOB;
+                    o4[k][1] = (cy0 && cx1) ? b00 + bC : OOB;
+                    o4[k][2] = (cy1 && cx0) ? b00 + bR : OOB;
+                    o4[k][3] = (cy1 && cx1) ? b00 + bR + bC : OOB;
+                }
+                // The corners of tap k+1 are in flight while tap k is summed.
+                u32x4 buf[2][4][NV];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        buf[0][q][v] = __builtin_amdgcn_raw_buffer_load_b128(xr, o4[0][q] + 16u * v, 0, 0);
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    if (k + 1 < KF) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+#pragma unroll
+                            for (int v = 0; v < NV; ++v)
+                                buf[(k + 1) & 1][q][v] =
+                                    __builtin_amdgcn_raw_buffer_load_b128(xr, o4[k + 1][q] + 16u * v, 0, 0);
+                    }
+                    float X[4][CPL];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) {
+                            const u32x4 u = buf[k & 1][q][v];
+                            X[q][4 * v] = __uint_as_float(u.x);
+                            X[q][4 * v + 1] = __uint_as_float(u.y);
+                            X[q][4 * v + 2] = __uint_as_float(u.z);
+                            X[q][4 * v + 3] = __uint_as_float(u.w);
+                        }
+                    tap_finish(k, fa[k], fb[k], xk[k], yk[k], o4[k], X[0], X[1], X[2], X[3]);
+                }
+            } else {
+#pragma unroll
+            for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
+                if (!KF && k >= K) break;
+                const int kx = k / kh, ky = k - kx * kh;
+                const float tx = G.scale * ob[2 * k], ty = G.scale * ob[2 * k + 1];
+                float a = 0.f, b = 0.f;
+                int x0 = -2, y0 = -2;
+                uint32_t o4[4] = {OOB, OOB, OOB, OOB};
+                float X[4][CPL];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) X[q][j] = 0.f;
+                if (coord_ok(tx) && coord_ok(ty)) {
+                    const float fx = floorf(tx), fy = floorf(ty);
+                    a = tx - fx;
+                    b = ty - fy;
+                    x0 = bx + kx * G.dw + (int)fx;
+                    y0 = by + ky * G.dh + (int)fy;
+                    if (x0 >= -1 && x0 < W && y0 >= -1 && y0 < H) {
+                        const bool cx0 = x0 >= 0, cx1 = x0 + 1 < W, cy0 = y0 >= 0, cy1 = y0 + 1 < H;
+                        const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * 4);
+                        const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
+                        o4[0] = (cy0 && cx0) ? b00 : OOB;
+                        o4[1] = (cy0 && cx1) ? b00 + bC : OOB;
+                        o4[2] = (cy1 && cx0) ? b00 + bR : OOB;
+                        o4[3] = (cy1 && cx1) ? b00 + bR + bC : OOB;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+#pragma unroll
+                            for (int v = 0; v < NV; ++v) {
+                                const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(xr, o4[q] + 16u * v, 0, 0);
+                                X[q][4 * v] = __uint_as_float(u.x);
+                                X[q][4 * v + 1] = __uint_as_float(u.y);
+                                X[q][4 * v + 2] = __uint_as_float(u.z);
+                                X[q][4 * v + 3] = __uint_as_float(u.w);
+                            }
+                    }
+                }
+                tap_finish(k, a, b, x0, y0, o4, X[0], X[1], X[2], X[3]);
+            }
             }
             if (c4 == 0 && gmask) {
 #pragma unroll
@@ -265,12 +364,13 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                 slot -= slot >= bc.aw ? bc.aw : 0;
                 unsigned long long* arow = acc + slot * rowe;
                 float* grow = gx + img + (long)y * W * C + (long)g * D;
-                for (int el = tid; el < rowe; el += nthr) {
-                    const unsigned long long q = arow[el];
+                for (int el = tid; el < W * D; el += nthr) {
+                    const int xc = el >> d_log, c = el & (D - 1);
+                    const unsigned long long q = arow[xc * pstr + c];
                     if (q != 0ull) {
-                        arow[el] = 0ull;
+                        arow[xc * pstr + c] = 0ull;
                         const float v = (float)(int)(uint32_t)(q >> 32) * s_hi + (float)(uint32_t)q * s_lo;
-                        atomicAdd(grow + (long)(el >> d_log) * C + (el & (D - 1)), v);
+                        atomicAdd(grow + (long)xc * C + c, v);
                     }
                 }
             }
@@ -286,7 +386,8 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
 bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit, int num_cus, BwdWinCfg* bc)
 {
     if (G.d % 4 != 0) return false;
-    const int lq = G.d / 4;
+    const int nv = G.d % 8 == 0 ? 2 : 1;   // 8 channels per lane when D allows
+    const int lq = G.d / (4 * nv);
     if (lq > 64 || (lq & (lq - 1)) != 0) return false;
     if (G.K > KMAX_WIN) return false;
     if ((uintptr_t)x % 16 || (uintptr_t)gout % 16) return false;
@@ -304,7 +405,7 @@ bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit,
         threads = 512;
     }
     const int ipass = threads / lq;
-    const long row_bytes = (long)G.w * G.d * 8;
+    const long row_bytes = (long)G.w * (G.d + 1) * 8;   // padded pixel stride
     int hy = -1, aw = 0;
     for (int h = 8; h >= 2; --h) {
         const int awh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 * h + 3;
@@ -323,6 +424,7 @@ bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit,
     chunks = (G.ho + chunk_rows - 1) / chunk_rows;
     if (units * chunks >= (1L << 31)) return false;
     bc->lq_log = lq_log;
+    bc->nv = nv;
     bc->ip = ipass;
     bc->tr = tr;
     bc->hy = hy;
@@ -343,7 +445,7 @@ hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, const flo
     const dim3 grid(bc.nwg), block(bc.threads);
 #define DCN_BWIN(KHV, KWV, SM)                                                                                   \
     {                                                                                                           \
-        auto* fn = dcn_bwd_win<KHV, KWV, SM>;                                                                   \
+        auto* fn = bc.nv == 2 ? dcn_bwd_win<KHV, KWV, SM, 2> : dcn_bwd_win<KHV, KWV, SM, 1>;                    \
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,          \
                                            bc.lds_bytes);                                                       \
         if (e != hipSuccess) return e;                                                                          \

@@ -9,7 +9,8 @@
 namespace dcn {
 
 struct BwdWinCfg {
-    int lq_log;       // log2 of the lanes per item (4 channels per lane)
+    int lq_log;       // log2 of the lanes per item
+    int nv;           // 16-byte vectors per lane (4 * nv channels per lane)
     int ip;           // items per pass (threads / lanes per item)
     int tr;           // output rows per step
     int hy;           // halo rows above and below a step's footprint kept in the window
