@@ -1,5 +1,5 @@
-// DCN forward for f16/bf16, LDS sliding window of horizontally paired cells,
-// for gfx950.
+// DCN forward for f16, LDS sliding window of horizontally paired cells, for
+// gfx950.
 //
 // Same operator as dcn_forward.hip ("DCNv4: Unbounded Weights", "Why Is
 // Sampling Just 9 Points Still Slow?": y_g(p0) = sum_k m_gk x_g(p0 + p_k +
@@ -13,11 +13,12 @@
 // a tap is (1-b)[(1-a) X(y0,x0) + a X(y0,x0+1)] + b[(1-a) X(y0+1,x0) +
 // a X(y0+1,x0+1)].  Each ring row holds, for every column x in [-1, W-1] and
 // channel c, the 32-bit pair (X(x, c), X(x+1, c)) of 16-bit values (zero
-// outside the map), so one tap of one channel is two v_dot2c_f32_{f16,bf16}
-// against the packed weight pairs ((1-a)(1-b)m, a(1-b)m) and ((1-a)bm, abm)
-// instead of four multiply-adds: products and sums are fp32; the weights are
-// rounded to the storage type (relative error 2^-11 for f16, 2^-9 for bf16)
-// before the products.
+// outside the map), so one tap of one channel is two v_dot2c_f32_f16 against
+// the packed weight pairs ((1-a)(1-b)m, a(1-b)m) and ((1-a)bm, abm) instead
+// of four multiply-adds: products and sums are fp32; the weights are rounded
+// to f16 (relative error 2^-11) before the products.  (The same scheme in
+// bf16 would round the weights to 2^-9 and spend most of the f16/bf16 error
+// budget, so bf16 stays on the plain ring kernel.)
 //
 // A row is NQ planes of PS bytes (both compile-time): plane q holds the
 // 16-byte chunk q (channels 4q..4q+3) of every (cell, group).  A wave's
@@ -46,7 +47,6 @@ constexpr int INIT_IT = 4;              // rounds of cell conversion for the fir
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 
 // Packed weight pairs and the two-term dot product, per storage type.
@@ -60,17 +60,6 @@ template <> struct Pair<DT_F16> {
     static __device__ __forceinline__ float dot(uint32_t x, uint32_t w, float acc)
     {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, x), __builtin_bit_cast(h2_t, w), acc, false);
-    }
-};
-template <> struct Pair<DT_BF16> {
-    static __device__ __forceinline__ uint32_t pack(float lo, float hi)
-    {
-        const f2_t v = {lo, hi};
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2_t));
-    }
-    static __device__ __forceinline__ float dot(uint32_t x, uint32_t w, float acc)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, x), __builtin_bit_cast(b2_t, w), acc, false);
     }
 };
 
@@ -510,19 +499,17 @@ hipError_t launch_dcn_forward_pair(const Geom& G, const RingCfg& rc, int dtype, 
     switch (dtype * 2 + (G.softmax ? 1 : 0)) {
         case DT_F16 * 2 + 0: return launch_pair_typed<DT_F16, false>(G, rc, x, off, mask, out, s);
         case DT_F16 * 2 + 1: return launch_pair_typed<DT_F16, true>(G, rc, x, off, mask, out, s);
-        case DT_BF16 * 2 + 0: return launch_pair_typed<DT_BF16, false>(G, rc, x, off, mask, out, s);
-        case DT_BF16 * 2 + 1: return launch_pair_typed<DT_BF16, true>(G, rc, x, off, mask, out, s);
     }
     return hipErrorInvalidValue;
 }
 
 // Choose the group set, rows per step, halo and chunking of the paired-cell
-// kernel for geometry G, or return false when it does not apply (f16/bf16,
-// 3x3, D of 8 or 16, 16-byte aligned tensors).
+// kernel for geometry G, or return false when it does not apply (f16, 3x3,
+// D of 8 or 16, 16-byte aligned tensors).
 bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
                int lds_limit, int num_cus, RingCfg* rc)
 {
-    if (dtype != DT_F16 && dtype != DT_BF16) return false;
+    if (dtype != DT_F16) return false;
     if (G.kh != 3 || G.kw != 3) return false;
     if (G.d != 8 && G.d != 16) return false;
     if ((uintptr_t)x % 16 || (uintptr_t)off % 16 || (uintptr_t)mask % 16 || (uintptr_t)out % 16) return false;

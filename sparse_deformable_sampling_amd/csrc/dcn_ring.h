@@ -38,7 +38,7 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
 hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
                                    const void* mask, void* out, hipStream_t s);
 
-// The paired-cell variant for f16/bf16 (dcn_forward_pair.hip): same
+// The paired-cell variant for f16 (dcn_forward_pair.hip): same
 // configuration fields, with pb = bytes of one paired cell of the group set
 // and row_iters = cell-conversion tasks per thread per step.
 bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,

@@ -38,6 +38,7 @@ def check_fwd(sds, name, n, h, w, c, g, dtype, softmax, offset=("normal", 1.5), 
     got = run_fwd(sds, d, dtype, g, softmax, **geom)
     ref = oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, softmax=softmax, dtype=dtype, **geom)
     err = rel_err(got, ref)
+    say("  err", name, dtype, "%.3e" % err)
     assert err <= TOL[dtype], (name, dtype, softmax, err)
     return err
 
