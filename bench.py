@@ -288,6 +288,36 @@ def cpu_baseline(seconds):
                       "as exact doubles) through the single-threaded C oracle, %.1f s" % (runs, el)}
 
 
+def cpu_baseline_threads(seconds, max_threads=16):
+    """The same unmodified oracle, batch-sharded one image per task over the
+    host's cores (a thread pool: the oracle's C call releases the GIL)."""
+    import concurrent.futures as cf
+    import oracle
+    from sparse_deformable_sampling_amd import synth
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, max_threads))
+    n, h, w, c, g = STAGES["stage1"]
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f16", seed=1)
+    one = lambda i: oracle.dcn_forward(d["x"][i:i + 1], d["offset"][i:i + 1], d["mask"][i:i + 1], group=g,
+                                       dtype="f16")
+    one(0)
+    runs, t0 = 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as pool:
+        while True:
+            list(pool.map(one, range(n)))
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    units = runs * n * h * w * c * 9
+    return {"value": round(units / el / 1e9, 4), "unit": "Gtaps*ch/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full batch(es) of the headline workload, one image per task on %d threads, %.1f s"
+                      % (runs, threads, el)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -363,6 +393,7 @@ def main():
                      "kernel": "dcn_fwd (f16, 3x3, DCNv4)", "kernel_us_mean": s["kernel_us_mean"],
                      "kernel_us_median": s["kernel_us_median"], "algorithmic_bytes_per_launch": s["min_bytes"]},
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": None if args.no_cpu_baseline else cpu_baseline_threads(args.cpu_seconds),
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
