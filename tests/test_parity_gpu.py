@@ -135,6 +135,16 @@ def test_tall_wide_and_short_maps(sds, dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, 0.5, 2.0, -1.25])
+def test_offset_scale(sds, dtype, scale):
+    """offset_scale multiplies every offset before it is added (0 turns the
+    op into a modulated sampling of the regular grid)."""
+    for softmax in (False, True):
+        check_fwd(sds, "offset-scale", 2, 14, 12, 32, 2, dtype, softmax, seed=61, offset_scale=scale)
+    check_fwd(sds, "offset-scale", 4, 56, 56, 64, 4, dtype, False, seed=62, offset_scale=scale)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("c,g", [(32, 2), (64, 4)])
 def test_integer_offsets_bit_exact(sds, dtype, c, g):
     """One-hot DCNv4 modulation and integer offsets copy pixels exactly, in
@@ -235,6 +245,13 @@ def test_backward_wide_offsets(sds, softmax):
     """Offsets N(0, 6): many corners land outside the rows a workgroup keeps
     on chip and take the direct path into grad_x."""
     check_bwd(sds, "bwd-wide", 8, 56, 56, 64, 4, softmax, seed=31, offset=("normal", 6.0))
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.5, 2.0, -1.25])
+def test_backward_offset_scale(sds, scale):
+    """grad_offset carries the factor offset_scale."""
+    check_bwd(sds, "bwd-oscale", 4, 20, 24, 32, 2, False, seed=67, offset_scale=scale)
+    check_bwd(sds, "bwd-oscale", 4, 20, 24, 32, 2, True, seed=67, offset_scale=scale)
 
 
 @pytest.mark.parametrize("gscale", [1e-30, 1e-12, 1e12, 1e30])
