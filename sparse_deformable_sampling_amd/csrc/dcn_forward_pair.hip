@@ -30,9 +30,12 @@
 // The pairs cannot come straight from the buffer-to-LDS path, so each thread
 // loads 16-byte runs of two neighbouring pixels into registers while a step
 // computes, interleaves them with v_perm_b32 at the end of the step and
-// writes the cells of the rows the next step adds.  Offsets and masks of the
-// next step travel buffer-to-LDS as in the plain ring kernel; samples whose
-// rows fall outside the window are read from global memory in a tail pass.
+// writes the cells of the rows the next step adds.  Each lane also loads the
+// offsets and modulation of its item of the next step straight into
+// registers, so the whole LDS budget goes to the ring: at 16 channels per
+// group that is what lets two groups share a workgroup on 56-pixel rows.
+// Samples whose rows fall outside the window are read from global memory in
+// a tail pass.
 #include "dcn_device.h"
 #include "dcn_ring.h"
 
@@ -42,10 +45,8 @@ namespace {
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past any accepted tensor: reads as zero
 constexpr int CV_IT = 4;                // cell-conversion tasks per thread per step
-constexpr int ST_IT = 4;                // per-thread 16-byte chunks of one step's offsets (and of its mask)
 constexpr int INIT_IT = 4;              // rounds of cell conversion for the first window
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 
@@ -82,17 +83,6 @@ __device__ __forceinline__ void fma8(float* acc, float w, u32x4 r)
     }
 }
 
-// One wave copies `bytes` (a multiple of 16) of a buffer into LDS at `dst`,
-// 1 KB per instruction: lane l of the wave lands at dst + c + 16*l.
-__device__ __forceinline__ void wave_copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t src, unsigned char* dst,
-                                                 uint32_t bytes, int wave, int nwaves, int lane)
-{
-    for (uint32_t c = (uint32_t)wave * 1024u; c < bytes; c += (uint32_t)nwaves * 1024u) {
-        const uint32_t o = c + 16u * lane;
-        if (o < bytes) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + c), 16, src + o, 0, 0, 0);
-    }
-}
-
 // The 8 paired dwords of channels 8h..8h+7 of one cell from the 16-byte runs
 // of those channels at pixel x (lo) and pixel x + 1 (hi).
 __device__ __forceinline__ void interleave(u32x4 lo, u32x4 hi, u32x4& c0, u32x4& c1)
@@ -123,7 +113,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     constexpr int HPC = D / 8;               // conversion tasks (8 channels each) per cell of one group
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
-    unsigned char* stage = lds + rc.ring_bytes;
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -190,52 +179,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         }
     };
 
-    // Offsets and mask of one step.  With every group in the workgroup the
-    // step's items are contiguous and are staged with aligned 16-byte loads;
-    // otherwise each pixel contributes one aligned run per tensor of cpo
-    // (offsets) and cpm (mask) chunks.
-    const uint32_t GK2 = (uint32_t)G.g * K2B, GKM = (uint32_t)G.g * KMB;
-    auto first_pixel = [&](int s) { return (uint32_t)(n * G.ho + r_begin + s * rc.tr) * G.wo; };
-    auto step_pixels = [&](int s) { return (uint32_t)min(rc.tr, r_end - (r_begin + s * rc.tr)) * G.wo; };
-    // Per-thread staging runs, the same every step: pixel and chunk of the
-    // offsets run and of the mask run this thread copies in iteration i.
-    uint32_t st_o[ST_IT], st_m[ST_IT];   // (pixel << 6) | chunk
-    if (!rc.st_contig) {
-#pragma unroll
-        for (int i = 0; i < ST_IT; ++i) {
-            const uint32_t t = (uint32_t)(wave + i * nwaves) * 64u + lane;
-            const uint32_t p = t / rc.cpo, pm = t / rc.cpm;
-            st_o[i] = (p << 6) | (t - p * rc.cpo);
-            st_m[i] = (pm << 6) | (t - pm * rc.cpm);
-        }
-    }
-    auto load_stage = [&](int s) {
-        const uint32_t P0 = first_pixel(s), np = step_pixels(s);
-        if (rc.st_contig) {
-            const uint32_t ob = P0 * GK2, oe = (P0 + np) * GK2, mb = P0 * GKM, me = (P0 + np) * GKM;
-            const uint32_t o_lo = ob & ~15u, m_lo = mb & ~15u;
-            const uint32_t o_len = ((oe + 15u) & ~15u) - o_lo, m_len = ((me + 15u) & ~15u) - m_lo;
-            wave_copy_to_lds(orr, o_lo, stage, o_len, wave, nwaves, lane);
-            wave_copy_to_lds(mr, m_lo, stage + rc.stage_o_bytes, m_len, wave, nwaves, lane);
-        } else {
-#pragma unroll
-            for (int i = 0; i < ST_IT; ++i) {
-                const uint32_t c = (uint32_t)(wave + i * nwaves) * 1024u;
-                const uint32_t p = st_o[i] >> 6, j = st_o[i] & 63u;
-                if (p < np)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_ptr_t)(stage + c), 16,
-                                                             (((P0 + p) * GK2 + g0 * K2B) & ~15u) + 16u * j, 0, 0, 0);
-                const uint32_t pm = st_m[i] >> 6, jm = st_m[i] & 63u;
-                if (pm < np)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_ptr_t)(stage + rc.stage_o_bytes + c), 16,
-                                                             (((P0 + pm) * GKM + g0 * KMB) & ~15u) + 16u * jm, 0, 0, 0);
-            }
-        }
+    // This lane's item within every step: row rl of the step, column c, group gl of the set.
+    const int items_row = G.wo * rc.gs;
+    const int rl = tid / items_row;
+    const int rem = tid - rl * items_row;
+    const int c = rem / rc.gs, gl = rem - c * rc.gs;
+    const int g = g0 + gl;
+
+    // Offsets and mask of this lane's item in a step, loaded into registers
+    // one step ahead: the 9 dwords of its offset pairs and the 5 dwords that
+    // hold its 9 modulation scalars (a run of 16-bit values that starts at
+    // byte 0 or 2 of its first dword).
+    uint32_t po[KF], pmr[5], psh = 0;
+    auto load_offsets = [&](int s) {
+        const int rr = r_begin + s * rc.tr + rl;
+        const bool v = rl < rc.tr && rr < r_end;
+        const uint32_t item = ((uint32_t)(n * G.ho + rr) * G.wo + c) * G.g + g;
+        const uint32_t ob = v ? item * K2B : OOB;
+        const uint32_t mb = v ? (item * KMB) & ~3u : OOB;
+        psh = ((item * KMB) & 3u) * 8u;
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(orr, ob, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(orr, ob + 16u, 0, 0);
+        po[0] = a.x; po[1] = a.y; po[2] = a.z; po[3] = a.w;
+        po[4] = b.x; po[5] = b.y; po[6] = b.z; po[7] = b.w;
+        po[8] = __builtin_amdgcn_raw_buffer_load_b32(orr, ob + 32u, 0, 0);
+        const u32x4 mq = __builtin_amdgcn_raw_buffer_load_b128(mr, mb, 0, 0);
+        pmr[0] = mq.x; pmr[1] = mq.y; pmr[2] = mq.z; pmr[3] = mq.w;
+        pmr[4] = __builtin_amdgcn_raw_buffer_load_b32(mr, mb + 16u, 0, 0);
     };
 
     // ---- the first window: rows lo0 .. lo0 + nw - 1 in slots 0 .. nw - 1
     // (all of its loads in flight at once: INIT_IT rounds of adv rows cover it)
-    load_stage(0);
+    load_offsets(0);
     {
         u32x4 in_lo[INIT_IT][CV_IT], in_hi[INIT_IT][CV_IT];
 #pragma unroll
@@ -266,12 +241,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // This lane's item within every step: row rl of the step, column c, group gl of the set.
-    const int items_row = G.wo * rc.gs;
-    const int rl = tid / items_row;
-    const int rem = tid - rl * items_row;
-    const int c = rem / rc.gs, gl = rem - c * rc.gs;
-    const int g = g0 + gl;
     const uint32_t gbyte = 16u * gl;
     const float lim = 16777216.0f;
     // Cell column (x0 + 1) and window row of each tap's top-left corner before the offset.
@@ -290,37 +259,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const int slot_lo = (s * adv) % rc.R;
         const bool more = s + 1 < nsteps;
 
-        // ---- offsets and mask of this lane's item, out of the staging area
+        // ---- offsets and mask of this lane's item, then the next step's loads
         float dx[KF], dy[KF], m[KF];
         {
-            const uint32_t P0 = first_pixel(s);
-            const uint32_t pl = (uint32_t)(live ? rl : 0) * G.wo + c;    // pixel within the step
-            uint32_t ob, mb;
-            if (rc.st_contig) {
-                const uint32_t o_lo = (P0 * GK2) & ~15u, m_lo = (P0 * GKM) & ~15u;
-                ob = (P0 + pl) * GK2 + gl * K2B - o_lo;
-                mb = rc.stage_o_bytes + (P0 + pl) * GKM + gl * KMB - m_lo;
-            } else {
-                const uint32_t so = (P0 + pl) * GK2 + g0 * K2B, sm = (P0 + pl) * GKM + g0 * KMB;
-                ob = pl * rc.cpo * 16u + (so & 15u) + gl * K2B;
-                mb = rc.stage_o_bytes + pl * rc.cpm * 16u + (sm & 15u) + gl * KMB;
-            }
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
-                const uint32_t p = *reinterpret_cast<const uint32_t*>(stage + ob + 4u * k);
-                dx[k] = h2f<DT>(p & 0xffffu);
-                dy[k] = h2f<DT>(p >> 16);
-                m[k] = h2f<DT>(*reinterpret_cast<const uint16_t*>(stage + mb + 2u * k));
+                dx[k] = h2f<DT>(po[k] & 0xffffu);
+                dy[k] = h2f<DT>(po[k] >> 16);
             }
+            uint32_t mw[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) mw[i] = __builtin_amdgcn_alignbit(i < 4 ? pmr[i + 1] : 0u, pmr[i], psh);
+#pragma unroll
+            for (int k = 0; k < KF; ++k) m[k] = h2f<DT>((k & 1) ? mw[k >> 1] >> 16 : mw[k >> 1] & 0xffffu);
         }
-        __syncthreads();   // the staging area is free for the next step
-
-        // ---- the next step's rows (into registers) and staging data (to LDS)
         if (more) {
+            load_offsets(s + 1);
 #pragma unroll
             for (int i = 0; i < CV_IT; ++i)
                 if (cv_row[i] >= 0) cv_load(i, lo + rc.nw + cv_row[i]);
-            load_stage(s + 1);
         }
 
         float acc[D];
@@ -517,7 +474,6 @@ bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const v
     const long x_bytes = (long)G.n * G.h * G.w * G.c * es;
     const long off_bytes = (long)G.items * G.K * 2 * es, mask_bytes = (long)G.items * G.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
-    const int K2B = G.K * 2 * es, KMB = G.K * es;
     const int HPC = G.d / 8;
 
     const int HY_MIN = 3, HY_MAX = 8;
@@ -539,31 +495,12 @@ bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const v
         const long tasks_row = (long)(G.w + 1) * gs * HPC;
         const int cv_iters = (int)((adv * tasks_row + threads - 1) / threads);
         if (cv_iters > 4) continue;   // CV_IT
-        const int np = tr * G.wo;
-        const int nwaves = threads / 64;
-        int stage_o, stage_m, st_contig, cpo = 0, cpm = 0;
-        if (gs == G.g) {
-            st_contig = 1;
-            stage_o = (np * G.g * K2B + 15) / 16 * 16 + 16;
-            stage_m = (np * G.g * KMB + 15) / 16 * 16 + 16;
-        } else {
-            st_contig = 0;
-            auto gcd16 = [](int v) { int gdiv = 16; while (v % gdiv) gdiv >>= 1; return gdiv; };
-            cpo = (gs * K2B + (16 - gcd16(K2B)) + 15) / 16;
-            cpm = (gs * KMB + (16 - gcd16(KMB)) + 15) / 16;
-            stage_o = np * cpo * 16;
-            stage_m = np * cpm * 16;
-            const long iters = ((long)np * std::max(cpo, cpm) + 63) / 64;
-            if ((iters + nwaves - 1) / nwaves > 4) continue;   // ST_IT
-            if (cpo >= 64 || cpm >= 64) continue;              // packed run index
-        }
-        const int stage_bytes = stage_o + stage_m;
         int hy = -1, nw = 0, R = 0;
         for (int h = HY_MAX; h >= HY_MIN; --h) {
             const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
             const int Rh = nwh + adv;
             if (nwh > 4 * adv) continue;   // INIT_IT rounds fill the first window
-            if ((long)(Rh + 1) * pitch + stage_bytes <= lds_limit) {
+            if ((long)(Rh + 1) * pitch <= lds_limit) {
                 hy = h;
                 nw = nwh;
                 R = Rh;
@@ -593,12 +530,12 @@ bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const v
         rc->nwg = (int)(units * chunks);
         rc->threads = threads;
         rc->row_iters = cv_iters;   // conversion tasks per thread per step
-        rc->st_contig = st_contig;
-        rc->cpo = cpo;
-        rc->cpm = cpm;
-        rc->stage_o_bytes = stage_o;
+        rc->st_contig = 0;   // no staging area: offsets and mask go to registers
+        rc->cpo = 0;
+        rc->cpm = 0;
+        rc->stage_o_bytes = 0;
         rc->ring_bytes = (int)((R + 1) * pitch);
-        rc->lds_bytes = rc->ring_bytes + stage_bytes;
+        rc->lds_bytes = rc->ring_bytes;
         // Buffer loads range-check each dword; see plan_ring.
         rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
         rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);

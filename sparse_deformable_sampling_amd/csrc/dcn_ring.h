@@ -39,8 +39,10 @@ hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, 
                                    const void* mask, void* out, hipStream_t s);
 
 // The paired-cell variant for f16 (dcn_forward_pair.hip): same
-// configuration fields, with pb = bytes of one paired cell of the group set
-// and row_iters = cell-conversion tasks per thread per step.
+// configuration fields, with pb = bytes of one paired cell of the group set,
+// row_iters = cell-conversion tasks per thread per step and no staging area
+// (each lane loads its offsets and mask into registers; lds_bytes =
+// ring_bytes).
 bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
                int lds_limit, int num_cus, RingCfg* rc);
 
