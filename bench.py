@@ -129,7 +129,7 @@ MSDA_SHAPES = [(100, 134), (50, 67), (25, 34), (13, 17)]
 def msda_runner(torch, seed=1):
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, q, heads, dh, pts = 8, 17821, 8, 32, 4
-    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed)
+    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed, ref="cells")
     min_bytes = 4 * (d["value"].size + d["loc"].size + d["attn"].size + n * q * heads * dh)
     desc = B.MsdaDesc(n, q, heads, dh, len(MSDA_SHAPES), pts, 1, B.DCN_F32)
     shapes = (ctypes.c_int32 * 8)(*[v for hw in MSDA_SHAPES for v in hw])
@@ -151,7 +151,7 @@ def msda_runner(torch, seed=1):
 def msda_bwd_runner(torch, seed=1):
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, q, heads, dh, pts = 8, 17821, 8, 32, 4
-    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed)
+    d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed, ref="cells")
     g = np.random.default_rng(seed + 1000).standard_normal((n, q, heads, dh)).astype(np.float32)
     # value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written once
     min_bytes = 4 * (2 * (d["value"].size + d["loc"].size + d["attn"].size) + g.size)

@@ -569,9 +569,11 @@ void device_limits(int* lds_limit, int* num_cus)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (!__atomic_load_n(&ready[dev], __ATOMIC_ACQUIRE)) {
+        // On a failed query keep conservative defaults: the planners then
+        // size for 64 KB of LDS, which every gfx9 part provides.
         int lds = 65536, cus = 256;
-        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) lds = 65536;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
         cached_lds[dev] = lds;
         cached_cus[dev] = cus;
         __atomic_store_n(&ready[dev], true, __ATOMIC_RELEASE);

@@ -76,15 +76,31 @@ def dcn_inputs(n, h, w, c, group, out_hw, taps=9, offset=("normal", 1.5), dtype=
     return out
 
 
-def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype="f32", seed=1):
+def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype="f32", seed=1, ref="uniform"):
     """Value ~ N(0,1) [n,S,heads,head_dim] with S = sum H_l*W_l; per query a
-    reference point ~ U(0,1)^2; each sampling location is that point plus
+    reference point; each sampling location is that point plus
     N(0, offset_std) divided by the level's (W_l, H_l); attention logits
-    ~ N(0,1) [n,len_q,heads,L,points]."""
+    ~ N(0,1) [n,len_q,heads,L,points].
+
+    ref="uniform": reference points ~ U(0,1)^2, independent per query.
+    ref="cells": the encoder's queries, one per cell of the flattened maps
+    (level-major, row-major, so len_q must be S), each referring to its own
+    cell centre ((x + 1/2)/W_l, (y + 1/2)/H_l) (valid ratios of 1)."""
     L = len(shapes)
     S = int(sum(int(hh) * int(ww) for hh, ww in shapes))
     value = store(normal((n, S, heads, head_dim), 1.0, seed, VALUE), dtype)
-    ref = uniform((n, len_q, 1, 1, 1, 2), 0.0, 1.0, seed, REF)
+    if ref == "uniform":
+        ref = uniform((n, len_q, 1, 1, 1, 2), 0.0, 1.0, seed, REF)
+    elif ref == "cells":
+        if len_q != S:
+            raise ValueError("ref='cells' needs one query per cell (len_q == %d)" % S)
+        cen = []
+        for hh, ww in shapes:
+            yy, xx = np.meshgrid(np.arange(hh, dtype=np.float64), np.arange(ww, dtype=np.float64), indexing="ij")
+            cen.append(np.stack([(xx.ravel() + 0.5) / ww, (yy.ravel() + 0.5) / hh], axis=-1))
+        ref = np.broadcast_to(np.concatenate(cen).astype(np.float32).reshape(1, S, 1, 1, 1, 2), (n, S, 1, 1, 1, 2))
+    else:
+        raise ValueError("ref must be 'uniform' or 'cells'")
     dev = normal((n, len_q, heads, L, points, 2), offset_std, seed, MSDA_OFFSET)
     size = np.array([[ww, hh] for hh, ww in shapes], np.float32).reshape(1, 1, 1, L, 1, 2)
     loc = (ref + dev / size).astype(np.float32)

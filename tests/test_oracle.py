@@ -482,3 +482,23 @@ def test_bf16_bits_convert_exactly():
     # nearest-even rounding of the stored generator values
     r = synth.f32_to_bf16_bits(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9], np.float32))
     assert list(r) == [0x3F80, 0x3F82, 0x3F80]
+
+
+def test_msda_encoder_reference_points_are_cell_centres():
+    """The encoder recipe: one query per cell in level-major, row-major
+    order, each referring to its own cell centre on every level; zero offset
+    spread then samples exactly there, and the oracle returns that cell."""
+    shapes = [(2, 3), (1, 2)]
+    d = synth.msda_inputs(1, shapes, 8, 1, 2, 1, offset_std=0.0, ref="cells")
+    loc = d["loc"][0, :, 0, :, 0, :]
+    want = [(1 / 6, 1 / 4), (1 / 2, 1 / 4), (5 / 6, 1 / 4), (1 / 6, 3 / 4), (1 / 2, 3 / 4), (5 / 6, 3 / 4),
+            (1 / 4, 1 / 2), (3 / 4, 1 / 2)]
+    for lev in range(2):
+        np.testing.assert_allclose(loc[:, lev, :], np.array(want), rtol=0, atol=1e-7)
+    # one level, raw weight 1: query q samples its own cell centre and reads value[q] (up to the
+    # f32 rounding of the centre coordinates, e.g. 1/6, which moves the sample by ~1e-7 cell)
+    d0 = synth.msda_inputs(1, [(2, 3)], 6, 1, 2, 1, offset_std=0.0, ref="cells")
+    got = oracle.msda_forward(d0["value"], [(2, 3)], d0["loc"], np.ones_like(d0["attn"]), softmax=False)
+    np.testing.assert_allclose(got[0, :, 0, :], d0["value"][0, :, 0, :].astype(np.float64), rtol=0, atol=1e-6)
+    with pytest.raises(ValueError):
+        synth.msda_inputs(1, shapes, 7, 1, 2, 1, ref="cells")

@@ -346,8 +346,8 @@ def test_backward_partial_outputs(sds):
 ENCODER_SHAPES = [(100, 134), (50, 67), (25, 34), (13, 17)]
 
 
-def check_msda(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0):
-    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed)
+def check_msda(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0, ref="uniform"):
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed, ref=ref)
     v, loc, attn = (to_dev(d[k], "f32") for k in ("value", "loc", "attn"))
     say(name, (n, shapes, q, heads, dh, points), softmax)
     got = to_host(sds.msda_forward(v, shapes, loc, attn, softmax=softmax))
@@ -357,10 +357,12 @@ def check_msda(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1,
     return err
 
 
-def test_msda_encoder_full(sds):
+@pytest.mark.parametrize("ref", ["cells", "uniform"])
+def test_msda_encoder_full(sds, ref):
     """Batch 8, 4 levels (100x134 .. 13x17), all 17821 positions as queries,
-    8 heads x 32, 4 points per level, joint softmax over 16."""
-    check_msda(sds, "msda-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4)
+    8 heads x 32, 4 points per level, joint softmax over 16; reference points
+    at the queries' own cell centres (the encoder) or uniform at random."""
+    check_msda(sds, "msda-encoder-" + ref, 8, ENCODER_SHAPES, 17821, 8, 32, 4, ref=ref)
 
 
 @pytest.mark.parametrize("dh", [1, 3, 4, 8, 32, 64, 36])
@@ -402,9 +404,9 @@ def test_msda_levels_points(sds, shapes, points):
 MSDA_BWD_TOL = (1e-4, TOL["f32"], TOL["f32"])
 
 
-def check_msda_bwd(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0):
+def check_msda_bwd(sds, name, n, shapes, q, heads, dh, points, softmax=True, seed=1, offset_std=2.0, ref="uniform"):
     import torch
-    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed)
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed, ref=ref)
     g = synth.store(np.random.default_rng(seed + 1000).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
     v, loc, attn, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
     say(name, (n, shapes, q, heads, dh, points), softmax)
@@ -416,11 +418,12 @@ def check_msda_bwd(sds, name, n, shapes, q, heads, dh, points, softmax=True, see
     return errs
 
 
-@pytest.mark.parametrize("softmax", [True, False])
-def test_msda_backward_encoder_full(sds, softmax):
+@pytest.mark.parametrize("softmax,ref", [(True, "cells"), (False, "cells"), (True, "uniform")])
+def test_msda_backward_encoder_full(sds, softmax, ref):
     """Batch 8, 4 levels (100x134 .. 13x17), all 17821 positions as queries,
-    8 heads x 32, 4 points per level."""
-    check_msda_bwd(sds, "msda-bwd-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4, softmax=softmax)
+    8 heads x 32, 4 points per level; reference points at the queries' own
+    cell centres (the encoder) or uniform at random."""
+    check_msda_bwd(sds, "msda-bwd-encoder-" + ref, 8, ENCODER_SHAPES, 17821, 8, 32, 4, softmax=softmax, ref=ref)
 
 
 @pytest.mark.parametrize("n,shapes,q,heads,dh,points", [
