@@ -222,8 +222,8 @@ COPY_CALIB_BYTES = 256 << 20
 
 # Source files that make up the headline kernel; a recorded traffic figure
 # is reported only while their hash matches the one recorded with it.
-HEADLINE_KERNEL_SOURCES = ["dcn_forward_pair.hip", "dcn_ring.h", "dcn_device.h", "dcn_launch.h"]
-HEADLINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dcn_fwd_pair_f16_stage1_traffic.txt")
+HEADLINE_KERNEL_SOURCES = ["dcn_forward_ring.hip", "dcn_ring.h", "dcn_device.h", "dcn_launch.h"]
+HEADLINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dcn_fwd_ring_f16_stage1_traffic.txt")
 
 
 def kernel_source_hash(files=HEADLINE_KERNEL_SOURCES):

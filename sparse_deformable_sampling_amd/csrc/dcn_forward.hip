@@ -296,21 +296,10 @@ hipError_t launch_dcn_forward(const Geom& G, int dtype, const void* x, const voi
 {
     int lds_limit, num_cus;
     device_limits(&lds_limit, &num_cus);
-    // Kernel choice.  The paired-cell kernel (dcn_forward_pair.hip, f16 only)
-    // halves the multiply-add instructions but doubles the LDS bytes of a
-    // row, so it often holds only one channel group per workgroup; its global
-    // reads and writes then touch one 32-byte slice of every pixel's 128-byte
-    // line, and the vector memory pipeline's per-line cost eats the saving.
-    // It is taken when it keeps at least two groups per workgroup in a single
-    // wave of workgroups.
-    RingCfg rc;
-    const bool pair_ok = plan_pair(G, dtype, x, off, mask, out, lds_limit, num_cus, &rc);
-    if (pair_ok && rc.gs >= 2 && rc.nwg <= num_cus)
-        return launch_dcn_forward_pair(G, rc, dtype, x, off, mask, out, s);
+    // The LDS sliding-window kernel where it applies, else the direct gathers.
     RingCfg rr;
     if (plan_ring(G, dtype, x, off, mask, out, lds_limit, num_cus, &rr))
         return launch_dcn_forward_ring(G, rr, dtype, x, off, mask, out, s);
-    if (pair_ok) return launch_dcn_forward_pair(G, rc, dtype, x, off, mask, out, s);
     switch (dtype * 2 + (G.softmax ? 1 : 0)) {
         case DT_F32 * 2 + 0: return launch_typed<DT_F32, false>(G, x, off, mask, out, s);
         case DT_F32 * 2 + 1: return launch_typed<DT_F32, true>(G, x, off, mask, out, s);

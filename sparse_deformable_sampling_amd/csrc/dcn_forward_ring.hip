@@ -18,7 +18,9 @@
 //     3x3 footprint of its output rows plus HY halo rows above and below for
 //     the learned offsets;
 //   - while a step computes, buffer-to-LDS loads bring in the rows the next
-//     step adds and the next step's offsets and mask, with no VGPR round trip;
+//     step adds, with no VGPR round trip, and each lane loads the offsets
+//     and mask of its next item into registers (no LDS staging area, so the
+//     whole LDS goes to the ring);
 //   - a sample whose two rows fall outside the window (|dy| > HY) is given
 //     zero weight in the LDS pass and read with global loads in a tail pass by
 //     the lanes that need it.
@@ -34,7 +36,6 @@ namespace {
 
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past any accepted tensor: reads as zero
 constexpr int ROW_IT = 4;               // per-thread 16-byte chunks of one input row
-constexpr int ST_IT = 8;                // per-thread 16-byte chunks of one step's offsets (and of its mask)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -72,17 +73,6 @@ __device__ __forceinline__ float h2f(uint32_t h16)
     return __uint_as_float(h16 << 16);
 }
 
-// One wave copies `bytes` (a multiple of 16) of a buffer into LDS at `dst`,
-// 1 KB per instruction: lane l of the wave lands at dst + c + 16*l.
-__device__ __forceinline__ void wave_copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t src, unsigned char* dst,
-                                                 uint32_t bytes, int wave, int nwaves, int lane)
-{
-    for (uint32_t c = (uint32_t)wave * 1024u; c < bytes; c += (uint32_t)nwaves * 1024u) {
-        const uint32_t o = c + 16u * lane;
-        if (o < bytes) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + c), 16, src + o, 0, 0, 0);
-    }
-}
-
 template <int DT, int KH, int KW, bool SOFTMAX, int NCH>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dcn_fwd_ring(
     Geom G, RingCfg rc, const typename Elem<DT>::T* __restrict__ x, const typename Elem<DT>::T* __restrict__ off,
@@ -97,7 +87,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     static_assert(KF > 0, "ring kernel is instantiated for fixed kernels");
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
-    unsigned char* stage = lds + rc.ring_bytes;
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -152,34 +141,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         }
     };
 
-    // Offsets and mask of one step.  With every group in the workgroup the
-    // step's items are contiguous and are staged with aligned 16-byte loads;
-    // otherwise each pixel contributes one aligned run per tensor of cpo
-    // (offsets) and cpm (mask) chunks.
-    const uint32_t GK2 = (uint32_t)G.g * K2B, GKM = (uint32_t)G.g * KMB;
-    auto first_pixel = [&](int s) { return (uint32_t)(n * G.ho + r_begin + s * rc.tr) * G.wo; };
-    auto step_pixels = [&](int s) { return (uint32_t)min(rc.tr, r_end - (r_begin + s * rc.tr)) * G.wo; };
-    auto load_stage = [&](int s) {
-        const uint32_t P0 = first_pixel(s), np = step_pixels(s);
-        if (rc.st_contig) {
-            const uint32_t ob = P0 * GK2, oe = (P0 + np) * GK2, mb = P0 * GKM, me = (P0 + np) * GKM;
-            const uint32_t o_lo = ob & ~15u, m_lo = mb & ~15u;
-            const uint32_t o_len = ((oe + 15u) & ~15u) - o_lo, m_len = ((me + 15u) & ~15u) - m_lo;
-            wave_copy_to_lds(orr, o_lo, stage, o_len, wave, nwaves, lane);
-            wave_copy_to_lds(mr, m_lo, stage + rc.stage_o_bytes, m_len, wave, nwaves, lane);
-        } else {
+    // This lane's item within every step: row rl of the step, column c, group gl of the set.
+    const int items_row = G.wo * rc.gs;
+    const int rl = tid / items_row;
+    const int rem = tid - rl * items_row;
+    const int c = rem / rc.gs, gl = rem - c * rc.gs;
+    const int g = g0 + gl;
+
+    // Offsets and mask of this lane's item in a step, loaded into registers
+    // one step ahead (no LDS staging, so the whole LDS goes to the ring):
+    // the item's KF offset pairs and the dwords that hold its KF modulation
+    // scalars.  16-bit scalars form a run that starts at byte 0 or 2 of its
+    // first dword, re-aligned with a funnel shift.
+    constexpr int OW = (int)(K2B / 4);            // offset dwords per item
+    constexpr int MW = ES == 4 ? KF : KF / 2 + 1; // mask dwords loaded per item
+    uint32_t po[OW], pmr[MW], psh = 0;
+    auto load_offsets = [&](int s) {
+        const int rr = r_begin + s * rc.tr + rl;
+        const bool v = rl < rc.tr && rr < r_end;
+        const uint32_t item = ((uint32_t)(n * G.ho + rr) * G.wo + c) * G.g + g;
+        const uint32_t ob = v ? item * K2B : OOB;
+        const uint32_t mb = v ? (item * KMB) & ~3u : OOB;
+        psh = ((item * KMB) & 3u) * 8u;
 #pragma unroll
-            for (int i = 0; i < ST_IT; ++i) {
-                const uint32_t c = (uint32_t)(wave + i * nwaves) * 1024u;
-                const uint32_t t = c / 16u + lane;
-                const uint32_t p = t / rc.cpo, j = t - p * rc.cpo;
-                if (t < np * rc.cpo)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_ptr_t)(stage + c), 16,
-                                                             (((P0 + p) * GK2 + g0 * K2B) & ~15u) + 16u * j, 0, 0, 0);
-                const uint32_t pm = t / rc.cpm, jm = t - pm * rc.cpm;
-                if (t < np * rc.cpm)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_ptr_t)(stage + rc.stage_o_bytes + c), 16,
-                                                             (((P0 + pm) * GKM + g0 * KMB) & ~15u) + 16u * jm, 0, 0, 0);
+        for (int i = 0; i < OW; i += 4) {
+            if (i + 4 <= OW) {
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(orr, ob + 4u * i, 0, 0);
+                po[i] = a.x; po[i + 1] = a.y; po[i + 2] = a.z; po[i + 3] = a.w;
+            } else {
+#pragma unroll
+                for (int j = i; j < OW; ++j) po[j] = __builtin_amdgcn_raw_buffer_load_b32(orr, ob + 4u * j, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MW; i += 4) {
+            if (i + 4 <= MW) {
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(mr, mb + 4u * i, 0, 0);
+                pmr[i] = a.x; pmr[i + 1] = a.y; pmr[i + 2] = a.z; pmr[i + 3] = a.w;
+            } else {
+#pragma unroll
+                for (int j = i; j < MW; ++j) pmr[j] = __builtin_amdgcn_raw_buffer_load_b32(mr, mb + 4u * j, 0, 0);
             }
         }
     };
@@ -194,21 +195,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         }
     }
     for (int rr = 0; rr < rc.nw; ++rr) load_row(lo0 + rr);
-    load_stage(0);
+    load_offsets(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // This lane's item within every step: row rl of the step, column c, group gl of the set.
-    const int items_row = G.wo * rc.gs;
-    const int rl = tid / items_row;
-    const int rem = tid - rl * items_row;
-    const int c = rem / rc.gs, gl = rem - c * rc.gs;
-    const int g = g0 + gl;
     const uint32_t gbyte = (uint32_t)gl * gsize;
     const float lim = 16777216.0f;
-    uint32_t qoff[NCH];   // byte offset of the chunk held in accumulator slot q
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) qoff[q] = NCH == 2 ? 16u * ((uint32_t)(q + c) & 1u) : 16u * q;
     // Window-relative row and LDS column of each tap's top-left corner before
     // the offset (they do not change from step to step).
     int bxk[KW], byk[KH];
@@ -224,42 +216,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const int lo = lo0 + s * adv;
         const int slot_lo = (s * adv) % rc.R;
 
-        // ---- offsets and mask of this lane's item, out of the staging area
+        // ---- offsets and mask of this lane's item, then the next step's loads
         float dx[KF], dy[KF], m[KF];
-        {
-            const uint32_t P0 = first_pixel(s);
-            const uint32_t pl = (uint32_t)(live ? rl : 0) * G.wo + c;    // pixel within the step
-            uint32_t ob, mb;
-            if (rc.st_contig) {
-                const uint32_t o_lo = (P0 * GK2) & ~15u, m_lo = (P0 * GKM) & ~15u;
-                ob = (P0 + pl) * GK2 + gl * K2B - o_lo;
-                mb = rc.stage_o_bytes + (P0 + pl) * GKM + gl * KMB - m_lo;
-            } else {
-                const uint32_t so = (P0 + pl) * GK2 + g0 * K2B, sm = (P0 + pl) * GKM + g0 * KMB;
-                ob = pl * rc.cpo * 16u + (so & 15u) + gl * K2B;
-                mb = rc.stage_o_bytes + pl * rc.cpm * 16u + (sm & 15u) + gl * KMB;
-            }
+        if constexpr (ES == 4) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
-                if constexpr (ES == 4) {
-                    const float2 d = *reinterpret_cast<const float2*>(stage + ob + 8u * k);
-                    dx[k] = d.x;
-                    dy[k] = d.y;
-                    m[k] = *reinterpret_cast<const float*>(stage + mb + 4u * k);
-                } else {
-                    const uint32_t p = *reinterpret_cast<const uint32_t*>(stage + ob + 4u * k);
-                    dx[k] = h2f<DT>(p & 0xffffu);
-                    dy[k] = h2f<DT>(p >> 16);
-                    m[k] = h2f<DT>(*reinterpret_cast<const uint16_t*>(stage + mb + 2u * k));
-                }
+                dx[k] = __uint_as_float(po[2 * k]);
+                dy[k] = __uint_as_float(po[2 * k + 1]);
+                m[k] = __uint_as_float(pmr[k]);
+            }
+        } else {
+            uint32_t mw[MW];
+#pragma unroll
+            for (int i = 0; i < MW; ++i) mw[i] = __builtin_amdgcn_alignbit(i + 1 < MW ? pmr[i + 1] : 0u, pmr[i], psh);
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                dx[k] = h2f<DT>(po[k] & 0xffffu);
+                dy[k] = h2f<DT>(po[k] >> 16);
+                m[k] = h2f<DT>((k & 1) ? mw[k >> 1] >> 16 : mw[k >> 1] & 0xffffu);
             }
         }
-        __syncthreads();   // the staging area is free for the next step
 
-        // ---- the next step's new rows and staging data go straight to LDS
+        // ---- the next step's new rows go straight to LDS, its offsets to registers
         if (s + 1 < nsteps) {
+            load_offsets(s + 1);
             for (int rr = 0; rr < adv; ++rr) load_row(lo + rc.nw + rr);
-            load_stage(s + 1);
         }
 
         if (live) {
@@ -311,38 +292,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
             // Reads of tap k+1 are in flight while tap k accumulates (with four
             // chunks per corner the two taps' data would not fit in registers,
-            // so each tap's reads are issued just before its math).  With two
-            // chunks per corner, slot q holds chunk (q + column) % 2, so that
-            // neighbouring lanes read different 16-byte bank groups in the same
-            // instruction; the stores undo the rotation.
+            // so each tap's reads are issued just before its math).  Chunk q of
+            // a corner sits 16*q bytes past its first, an immediate offset of
+            // the read.  (Rotating the chunk order between neighbouring lanes
+            // spreads a read over more LDS bank groups, but its address
+            // arithmetic cost more than the conflicts it saved.)
             constexpr bool PIPE = NCH <= 2;
             const uint32_t o01 = (uint32_t)rc.pb, o10 = (uint32_t)rc.pitch, o11 = (uint32_t)(rc.pitch + rc.pb);
             u32x4 cur[4 * NCH], nxt[PIPE ? 4 * NCH : 1];
 #pragma unroll
             for (int q = 0; q < NCH; ++q) {
-                cur[4 * q + 0] = lds_ld16(ring, A[0] + qoff[q]);
-                cur[4 * q + 1] = lds_ld16(ring, A[0] + o01 + qoff[q]);
-                cur[4 * q + 2] = lds_ld16(ring, A[0] + o10 + qoff[q]);
-                cur[4 * q + 3] = lds_ld16(ring, A[0] + o11 + qoff[q]);
+                cur[4 * q + 0] = lds_ld16(ring, A[0] + 16u * q);
+                cur[4 * q + 1] = lds_ld16(ring, A[0] + o01 + 16u * q);
+                cur[4 * q + 2] = lds_ld16(ring, A[0] + o10 + 16u * q);
+                cur[4 * q + 3] = lds_ld16(ring, A[0] + o11 + 16u * q);
             }
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
                 if (!PIPE && k > 0) {
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
-                        cur[4 * q + 0] = lds_ld16(ring, A[k] + qoff[q]);
-                        cur[4 * q + 1] = lds_ld16(ring, A[k] + o01 + qoff[q]);
-                        cur[4 * q + 2] = lds_ld16(ring, A[k] + o10 + qoff[q]);
-                        cur[4 * q + 3] = lds_ld16(ring, A[k] + o11 + qoff[q]);
+                        cur[4 * q + 0] = lds_ld16(ring, A[k] + 16u * q);
+                        cur[4 * q + 1] = lds_ld16(ring, A[k] + o01 + 16u * q);
+                        cur[4 * q + 2] = lds_ld16(ring, A[k] + o10 + 16u * q);
+                        cur[4 * q + 3] = lds_ld16(ring, A[k] + o11 + 16u * q);
                     }
                 }
                 if (PIPE && k + 1 < KF) {
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
-                        nxt[4 * q + 0] = lds_ld16(ring, A[k + 1] + qoff[q]);
-                        nxt[4 * q + 1] = lds_ld16(ring, A[k + 1] + o01 + qoff[q]);
-                        nxt[4 * q + 2] = lds_ld16(ring, A[k + 1] + o10 + qoff[q]);
-                        nxt[4 * q + 3] = lds_ld16(ring, A[k + 1] + o11 + qoff[q]);
+                        nxt[4 * q + 0] = lds_ld16(ring, A[k + 1] + 16u * q);
+                        nxt[4 * q + 1] = lds_ld16(ring, A[k + 1] + o01 + 16u * q);
+                        nxt[4 * q + 2] = lds_ld16(ring, A[k + 1] + o10 + 16u * q);
+                        nxt[4 * q + 3] = lds_ld16(ring, A[k + 1] + o11 + 16u * q);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);   // keep the next tap's reads ahead of this tap's math
@@ -399,7 +381,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                     const float ma = mk * (1.f - a), mb = mk * a;
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
-                        const uint32_t qo = qoff[q];   // chunk held in slot q
+                        const uint32_t qo = 16u * q;
                         fma16<DT>(acc + q * V, ma * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o00 + qo, 0, 0));
                         fma16<DT>(acc + q * V, mb * (1.f - b), __builtin_amdgcn_raw_buffer_load_b128(xr, o01g + qo, 0, 0));
                         fma16<DT>(acc + q * V, ma * b, __builtin_amdgcn_raw_buffer_load_b128(xr, o10g + qo, 0, 0));
@@ -409,7 +391,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             }
             T* op = out + (((long)(n * G.ho + r) * G.wo + c) * G.c + (long)g * G.d);
 #pragma unroll
-            for (int q = 0; q < NCH; ++q) store_vec<DT>(op + qoff[q] / ES, acc + q * V);
+            for (int q = 0; q < NCH; ++q) store_vec<DT>(op + q * V, acc + q * V);
         }
 
         __builtin_amdgcn_s_waitcnt(0);   // this wave's buffer-to-LDS loads have landed
@@ -472,7 +454,6 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
     const long x_bytes = (long)G.n * G.h * G.w * G.c * es;
     const long off_bytes = (long)G.items * G.K * 2 * es, mask_bytes = (long)G.items * G.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
-    const int K2B = G.K * 2 * es, KMB = G.K * es;
 
     // Try group sets from all groups down; take the first that keeps a halo of
     // at least HY_MIN rows in LDS with one workgroup per CU.
@@ -491,30 +472,12 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
         const int nwaves = threads / 64;
         const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
         if (row_iters > 4) continue;   // ROW_IT
-        const int np = tr * G.wo;      // pixels per step
-        int stage_o, stage_m, st_contig, cpo = 0, cpm = 0;
-        if (gs == G.g) {
-            st_contig = 1;
-            stage_o = (np * G.g * K2B + 15) / 16 * 16 + 16;
-            stage_m = (np * G.g * KMB + 15) / 16 * 16 + 16;
-        } else {
-            st_contig = 0;
-            // a run starts at a multiple of gcd(item bytes, 16) within its 16-byte line
-            auto gcd16 = [](int v) { int gdiv = 16; while (v % gdiv) gdiv >>= 1; return gdiv; };
-            cpo = (gs * K2B + (16 - gcd16(K2B)) + 15) / 16;
-            cpm = (gs * KMB + (16 - gcd16(KMB)) + 15) / 16;
-            stage_o = np * cpo * 16;
-            stage_m = np * cpm * 16;
-            const long iters = ((long)np * std::max(cpo, cpm) + 63) / 64;
-            if ((iters + nwaves - 1) / nwaves > 8) continue;   // ST_IT
-        }
-        const int stage_bytes = stage_o + stage_m;
         const int adv = tr * G.sh;
         int hy = -1, nw = 0, R = 0;
         for (int h = HY_MAX; h >= HY_MIN; --h) {
             const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
             const int Rh = nwh + adv;
-            if ((long)(Rh + 1) * pitch + stage_bytes <= lds_limit) {
+            if ((long)(Rh + 1) * pitch <= lds_limit) {
                 hy = h;
                 nw = nwh;
                 R = Rh;
@@ -544,12 +507,8 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
         rc->nwg = (int)(units * chunks);
         rc->threads = threads;
         rc->row_iters = row_iters;
-        rc->st_contig = st_contig;
-        rc->cpo = cpo;
-        rc->cpm = cpm;
-        rc->stage_o_bytes = stage_o;
         rc->ring_bytes = (int)((R + 1) * pitch);
-        rc->lds_bytes = rc->ring_bytes + stage_bytes;
+        rc->lds_bytes = rc->ring_bytes;   // offsets and mask go to registers, not LDS
         // Buffer loads range-check each dword: a dword that straddles num_records
         // reads as zero.  Rounding the extents up to whole dwords keeps the last
         // values of an odd-length 16-bit tensor readable; the extra bytes share

@@ -23,11 +23,8 @@ struct RingCfg {
     int nwg;          // workgroups
     int threads;      // threads per workgroup (one item per thread per step)
     int row_iters;    // 1 KB copy instructions per wave for one input row
-    int st_contig;    // 1: offsets/mask of a step are one contiguous run (gs == groups)
-    int cpo, cpm;     // otherwise: 16-byte chunks staged per pixel for offsets and for mask
-    int stage_o_bytes;  // bytes of the offsets part of the staging area
     int ring_bytes;   // (R + 1) * pitch
-    int lds_bytes;    // ring + staging of one step's offsets and mask
+    int lds_bytes;    // the ring (each lane loads its offsets and mask into registers)
     uint32_t x_bytes, off_bytes, mask_bytes;   // buffer extents, rounded up to whole dwords
 };
 
@@ -36,17 +33,6 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
                int lds_limit, int num_cus, RingCfg* rc);
 
 hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
-                                   const void* mask, void* out, hipStream_t s);
-
-// The paired-cell variant for f16 (dcn_forward_pair.hip): same
-// configuration fields, with pb = bytes of one paired cell of the group set,
-// row_iters = cell-conversion tasks per thread per step and no staging area
-// (each lane loads its offsets and mask into registers; lds_bytes =
-// ring_bytes).
-bool plan_pair(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
-               int lds_limit, int num_cus, RingCfg* rc);
-
-hipError_t launch_dcn_forward_pair(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
                                    const void* mask, void* out, hipStream_t s);
 
 // Per-device properties cached on first use (LDS bytes per workgroup, CU count).
