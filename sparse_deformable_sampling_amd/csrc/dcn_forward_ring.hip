@@ -27,6 +27,10 @@
 // Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
 // accumulation; 16-byte vector stores, one writer per output element.
+// WMAX is the workgroup's wave count bound: 16 (four waves per SIMD, <=128
+// VGPRs) where a corner is at most 32 bytes, the next tap's geometry then
+// being computed while its reads land; 8 otherwise, with the geometry of all
+// taps computed first and the next tap's reads in flight during the math.
 #include "dcn_device.h"
 #include "dcn_ring.h"
 
@@ -73,8 +77,8 @@ __device__ __forceinline__ float h2f(uint32_t h16)
     return __uint_as_float(h16 << 16);
 }
 
-template <int DT, int KH, int KW, bool SOFTMAX, int NCH>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void dcn_fwd_ring(
+template <int DT, int KH, int KW, bool SOFTMAX, int NCH, int WMAX>
+__global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX / 4, WMAX / 4))) void dcn_fwd_ring(
     Geom G, RingCfg rc, const typename Elem<DT>::T* __restrict__ x, const typename Elem<DT>::T* __restrict__ off,
     const typename Elem<DT>::T* __restrict__ mask, typename Elem<DT>::T* __restrict__ out)
 {
@@ -261,13 +265,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             float acc[NCH * V];
 #pragma unroll
             for (int q = 0; q < NCH * V; ++q) acc[q] = 0.f;
-            // Geometry of all taps first: the LDS address of the top-left
-            // corner (the others are +pb, +pitch, +pitch+pb) and four weights.
-            uint32_t A[KF];
-            float W00[KF], W01[KF], W10[KF], W11[KF];
+            const uint32_t o01 = (uint32_t)rc.pb, o10 = (uint32_t)rc.pitch, o11 = (uint32_t)(rc.pitch + rc.pb);
             uint32_t fb = 0;
-#pragma unroll
-            for (int k = 0; k < KF; ++k) {
+            // Tap k's geometry: the LDS address of its top-left corner (the
+            // others are +pb, +pitch, +pitch+pb) and its four weights.
+            auto geo = [&](int k, uint32_t& Ak, float& w00, float& w01, float& w10, float& w11) {
                 const int kx = k / KH, ky = k - (k / KH) * KH;
                 const float tx = fminf(fmaxf(G.scale * dx[k], -lim), lim);
                 const float ty = fminf(fmaxf(G.scale * dy[k], -lim), lim);
@@ -282,63 +284,91 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                 uint32_t s0 = (uint32_t)(slot_lo + yi);
                 s0 = min(s0, s0 - (uint32_t)rc.R);                  // wrap once
                 const uint32_t addr = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
-                A[k] = use ? addr : 0u;
+                Ak = use ? addr : 0u;
                 const float mm = use ? m[k] : 0.f;
                 const float ma = mm * (1.f - a), mb = mm * a;
-                W00[k] = ma * (1.f - b);
-                W01[k] = mb * (1.f - b);
-                W10[k] = ma * b;
-                W11[k] = mb * b;
-            }
-            // Reads of tap k+1 are in flight while tap k accumulates (with four
-            // chunks per corner the two taps' data would not fit in registers,
-            // so each tap's reads are issued just before its math).  Chunk q of
-            // a corner sits 16*q bytes past its first, an immediate offset of
-            // the read.  (Rotating the chunk order between neighbouring lanes
-            // spreads a read over more LDS bank groups, but its address
-            // arithmetic cost more than the conflicts it saved.)
-            constexpr bool PIPE = NCH <= 2;
-            const uint32_t o01 = (uint32_t)rc.pb, o10 = (uint32_t)rc.pitch, o11 = (uint32_t)(rc.pitch + rc.pb);
-            u32x4 cur[4 * NCH], nxt[PIPE ? 4 * NCH : 1];
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                cur[4 * q + 0] = lds_ld16(ring, A[0] + 16u * q);
-                cur[4 * q + 1] = lds_ld16(ring, A[0] + o01 + 16u * q);
-                cur[4 * q + 2] = lds_ld16(ring, A[0] + o10 + 16u * q);
-                cur[4 * q + 3] = lds_ld16(ring, A[0] + o11 + 16u * q);
-            }
-#pragma unroll
-            for (int k = 0; k < KF; ++k) {
-                if (!PIPE && k > 0) {
-#pragma unroll
-                    for (int q = 0; q < NCH; ++q) {
-                        cur[4 * q + 0] = lds_ld16(ring, A[k] + 16u * q);
-                        cur[4 * q + 1] = lds_ld16(ring, A[k] + o01 + 16u * q);
-                        cur[4 * q + 2] = lds_ld16(ring, A[k] + o10 + 16u * q);
-                        cur[4 * q + 3] = lds_ld16(ring, A[k] + o11 + 16u * q);
-                    }
-                }
-                if (PIPE && k + 1 < KF) {
-#pragma unroll
-                    for (int q = 0; q < NCH; ++q) {
-                        nxt[4 * q + 0] = lds_ld16(ring, A[k + 1] + 16u * q);
-                        nxt[4 * q + 1] = lds_ld16(ring, A[k + 1] + o01 + 16u * q);
-                        nxt[4 * q + 2] = lds_ld16(ring, A[k + 1] + o10 + 16u * q);
-                        nxt[4 * q + 3] = lds_ld16(ring, A[k + 1] + o11 + 16u * q);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);   // keep the next tap's reads ahead of this tap's math
+                w00 = ma * (1.f - b);
+                w01 = mb * (1.f - b);
+                w10 = ma * b;
+                w11 = mb * b;
+            };
+            // The four corners' addresses are pointers into the ring, so that
+            // the 16-byte chunk offsets fold into the reads' immediate offsets.
+            auto issue = [&](uint32_t Ak, u32x4* d) {
+                const unsigned char* p00 = ring + Ak;
+                const unsigned char* p01 = p00 + o01;
+                const unsigned char* p10 = p00 + o10;
+                const unsigned char* p11 = p00 + o11;
 #pragma unroll
                 for (int q = 0; q < NCH; ++q) {
-                    fma16<DT>(acc + q * V, W00[k], cur[4 * q + 0]);
-                    fma16<DT>(acc + q * V, W01[k], cur[4 * q + 1]);
-                    fma16<DT>(acc + q * V, W10[k], cur[4 * q + 2]);
-                    fma16<DT>(acc + q * V, W11[k], cur[4 * q + 3]);
+                    d[4 * q + 0] = *reinterpret_cast<const u32x4*>(p00 + 16 * q);
+                    d[4 * q + 1] = *reinterpret_cast<const u32x4*>(p01 + 16 * q);
+                    d[4 * q + 2] = *reinterpret_cast<const u32x4*>(p10 + 16 * q);
+                    d[4 * q + 3] = *reinterpret_cast<const u32x4*>(p11 + 16 * q);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                if (PIPE && k + 1 < KF) {
+            };
+            if constexpr (WMAX == 16) {
+                // Four waves per SIMD hide the LDS latency, so registers go to
+                // occupancy: one tap's data in flight, the next tap's geometry
+                // computed while it lands.
+                uint32_t Ac;
+                float c00, c01, c10, c11;
+                geo(0, Ac, c00, c01, c10, c11);
+                u32x4 cur[4 * NCH];
+                issue(Ac, cur);
 #pragma unroll
-                    for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[PIPE ? q : 0];
+                for (int k = 0; k < KF; ++k) {
+                    uint32_t An = 0;
+                    float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
+                    if (k + 1 < KF) geo(k + 1, An, n00, n01, n10, n11);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        fma16<DT>(acc + q * V, c00, cur[4 * q + 0]);
+                        fma16<DT>(acc + q * V, c01, cur[4 * q + 1]);
+                        fma16<DT>(acc + q * V, c10, cur[4 * q + 2]);
+                        fma16<DT>(acc + q * V, c11, cur[4 * q + 3]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (k + 1 < KF) {
+                        issue(An, cur);
+                        c00 = n00; c01 = n01; c10 = n10; c11 = n11;
+                    }
+                }
+            } else {
+                // Geometry of all taps first: the LDS address of the top-left
+                // corner (the others are +pb, +pitch, +pitch+pb) and four weights.
+                uint32_t A[KF];
+                float W00[KF], W01[KF], W10[KF], W11[KF];
+#pragma unroll
+                for (int k = 0; k < KF; ++k) geo(k, A[k], W00[k], W01[k], W10[k], W11[k]);
+                // Reads of tap k+1 are in flight while tap k accumulates (with four
+                // chunks per corner the two taps' data would not fit in registers,
+                // so each tap's reads are issued just before its math).  Chunk q of
+                // a corner sits 16*q bytes past its first, an immediate offset of
+                // the read.  (Rotating the chunk order between neighbouring lanes
+                // spreads a read over more LDS bank groups, but its address
+                // arithmetic cost more than the conflicts it saved.)
+                constexpr bool PIPE = NCH <= 2;
+                u32x4 cur[4 * NCH], nxt[PIPE ? 4 * NCH : 1];
+                issue(A[0], cur);
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    if (!PIPE && k > 0) issue(A[k], cur);
+                    if (PIPE && k + 1 < KF) issue(A[k + 1], nxt);
+                    __builtin_amdgcn_sched_barrier(0);   // keep the next tap's reads ahead of this tap's math
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        fma16<DT>(acc + q * V, W00[k], cur[4 * q + 0]);
+                        fma16<DT>(acc + q * V, W01[k], cur[4 * q + 1]);
+                        fma16<DT>(acc + q * V, W10[k], cur[4 * q + 2]);
+                        fma16<DT>(acc + q * V, W11[k], cur[4 * q + 3]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (PIPE && k + 1 < KF) {
+#pragma unroll
+                        for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[PIPE ? q : 0];
+                    }
                 }
             }
             // Tail: samples outside the window that may touch the image, read
@@ -406,19 +436,21 @@ hipError_t launch_ring_typed(const Geom& G, const RingCfg& rc, const void* x, co
     using T = typename Elem<DT>::T;
     const int nch = G.d * (int)sizeof(T) / 16;
     const dim3 grid(rc.nwg), block(rc.threads);
-#define DCN_RING_CASE(NCHV)                                                                                   \
-    case NCHV: {                                                                                              \
-        auto* fn = dcn_fwd_ring<DT, 3, 3, SOFTMAX, NCHV>;                                                     \
+#define DCN_RING_CASE(NCHV, WM)                                                                               \
+    case NCHV * 100 + WM: {                                                                                   \
+        auto* fn = dcn_fwd_ring<DT, 3, 3, SOFTMAX, NCHV, WM>;                                                 \
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,        \
                                            rc.lds_bytes);                                                     \
         if (e != hipSuccess) return e;                                                                        \
         fn<<<grid, block, rc.lds_bytes, s>>>(G, rc, (const T*)x, (const T*)off, (const T*)mask, (T*)out);      \
         break;                                                                                                \
     }
-    switch (nch) {
-        DCN_RING_CASE(1)
-        DCN_RING_CASE(2)
-        DCN_RING_CASE(4)
+    switch (nch * 100 + (rc.threads > 512 ? 16 : 8)) {
+        DCN_RING_CASE(1, 8)
+        DCN_RING_CASE(2, 8)
+        DCN_RING_CASE(4, 8)
+        DCN_RING_CASE(1, 16)
+        DCN_RING_CASE(2, 16)
         default: return hipErrorInvalidValue;
     }
 #undef DCN_RING_CASE
@@ -455,70 +487,79 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
     const long off_bytes = (long)G.items * G.K * 2 * es, mask_bytes = (long)G.items * G.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
 
-    // Try group sets from all groups down; take the first that keeps a halo of
-    // at least HY_MIN rows in LDS with one workgroup per CU.
+    // For a target number of items per step, try group sets from all groups
+    // down; take the first that keeps a halo of at least HY_MIN rows in LDS
+    // with one workgroup per CU.
     const int HY_MIN = 4, HY_MAX = 8;
-    for (int gs = G.g; gs >= 1; --gs) {
-        if (G.g % gs) continue;
-        const int items_row = G.wo * gs;
-        if (items_row > 512) continue;
-        int tr = (448 + items_row - 1) / items_row;
-        tr = std::max(1, std::min(tr, std::min(512 / items_row, G.ho)));
-        const int items_step = tr * items_row;
-        const int threads = (items_step + 63) / 64 * 64;
-        const int pb = gs * G.d * es;
-        const int cpp = pb / 16;
-        const long pitch = (long)(G.w + 2) * pb + 80;   // 5 bank groups of skew: nearby rows spread over the banks
-        const int nwaves = threads / 64;
-        const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
-        if (row_iters > 4) continue;   // ROW_IT
-        const int adv = tr * G.sh;
-        int hy = -1, nw = 0, R = 0;
-        for (int h = HY_MAX; h >= HY_MIN; --h) {
-            const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
-            const int Rh = nwh + adv;
-            if ((long)(Rh + 1) * pitch <= lds_limit) {
-                hy = h;
-                nw = nwh;
-                R = Rh;
-                break;
+    auto try_plan = [&](int target) -> bool {
+        const int max_thr = target > 448 ? 1024 : 512;
+        for (int gs = G.g; gs >= 1; --gs) {
+            if (G.g % gs) continue;
+            const int items_row = G.wo * gs;
+            if (items_row > max_thr) continue;
+            int tr = (target + items_row - 1) / items_row;
+            tr = std::max(1, std::min(tr, std::min(max_thr / items_row, G.ho)));
+            const int items_step = tr * items_row;
+            const int threads = (items_step + 63) / 64 * 64;
+            const int pb = gs * G.d * es;
+            const int cpp = pb / 16;
+            const long pitch = (long)(G.w + 2) * pb + 80;   // 5 bank groups of skew: nearby rows spread over the banks
+            const int nwaves = threads / 64;
+            const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
+            if (row_iters > 4) continue;   // ROW_IT
+            const int adv = tr * G.sh;
+            int hy = -1, nw = 0, R = 0;
+            for (int h = HY_MAX; h >= HY_MIN; --h) {
+                const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
+                const int Rh = nwh + adv;
+                if ((long)(Rh + 1) * pitch <= lds_limit) {
+                    hy = h;
+                    nw = nwh;
+                    R = Rh;
+                    break;
+                }
             }
+            if (hy < 0) continue;
+            const int gsets = G.g / gs;
+            const long units = (long)G.n * gsets;
+            int chunks = (int)std::max(1L, ((long)num_cus + units - 1) / units);
+            chunks = std::min(chunks, (G.ho + tr - 1) / tr);
+            int chunk_rows = (G.ho + chunks - 1) / chunks;
+            // A chunk need not be a whole number of steps (its last step may be
+            // partial): rounding it up would leave the last chunk short.
+            chunks = (G.ho + chunk_rows - 1) / chunk_rows;
+            if (units * chunks >= (1L << 31)) continue;
+            rc->gs = gs;
+            rc->gsets = gsets;
+            rc->pb = pb;
+            rc->cpp = cpp;
+            rc->pitch = (int)pitch;
+            rc->R = R;
+            rc->nw = nw;
+            rc->hy = hy;
+            rc->tr = tr;
+            rc->chunk_rows = chunk_rows;
+            rc->chunks = chunks;
+            rc->nwg = (int)(units * chunks);
+            rc->threads = threads;
+            rc->row_iters = row_iters;
+            rc->ring_bytes = (int)((R + 1) * pitch);
+            rc->lds_bytes = rc->ring_bytes;   // offsets and mask go to registers, not LDS
+            // Buffer loads range-check each dword: a dword that straddles num_records
+            // reads as zero.  Rounding the extents up to whole dwords keeps the last
+            // values of an odd-length 16-bit tensor readable; the extra bytes share
+            // a dword (and so a page) with valid data and are never used.
+            rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
+            rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
+            rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
+            return true;
         }
-        if (hy < 0) continue;
-        const int gsets = G.g / gs;
-        const long units = (long)G.n * gsets;
-        int chunks = (int)std::max(1L, ((long)num_cus + units - 1) / units);
-        chunks = std::min(chunks, (G.ho + tr - 1) / tr);
-        int chunk_rows = (G.ho + chunks - 1) / chunks;
-        chunk_rows = (chunk_rows + tr - 1) / tr * tr;
-        chunks = (G.ho + chunk_rows - 1) / chunk_rows;
-        if (units * chunks >= (1L << 31)) continue;
-        rc->gs = gs;
-        rc->gsets = gsets;
-        rc->pb = pb;
-        rc->cpp = cpp;
-        rc->pitch = (int)pitch;
-        rc->R = R;
-        rc->nw = nw;
-        rc->hy = hy;
-        rc->tr = tr;
-        rc->chunk_rows = chunk_rows;
-        rc->chunks = chunks;
-        rc->nwg = (int)(units * chunks);
-        rc->threads = threads;
-        rc->row_iters = row_iters;
-        rc->ring_bytes = (int)((R + 1) * pitch);
-        rc->lds_bytes = rc->ring_bytes;   // offsets and mask go to registers, not LDS
-        // Buffer loads range-check each dword: a dword that straddles num_records
-        // reads as zero.  Rounding the extents up to whole dwords keeps the last
-        // values of an odd-length 16-bit tensor readable; the extra bytes share
-        // a dword (and so a page) with valid data and are never used.
-        rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
-        rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
-        rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
-        return true;
-    }
-    return false;
+        return false;
+    };
+    // With at most 32 bytes per corner, a 1024-thread workgroup (four waves
+    // per SIMD, a tap's data in <=128 VGPRs) hides the LDS latency better;
+    // try that first.
+    return (nch <= 2 && try_plan(896)) || try_plan(448);
 }
 
 void device_limits(int* lds_limit, int* num_cus)
