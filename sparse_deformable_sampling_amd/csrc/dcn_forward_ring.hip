@@ -220,8 +220,12 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         const int lo = lo0 + s * adv;
         const int slot_lo = (s * adv) % rc.R;
 
-        // ---- offsets and mask of this lane's item, then the next step's loads
+        // ---- offsets and mask of this lane's item, then the next step's loads.
+        // 16-bit offset pairs stay packed (pc) until a tap's geometry needs
+        // them, which keeps 9 registers free while the next step's loads are
+        // in flight.
         float dx[KF], dy[KF], m[KF];
+        uint32_t pc[KF];
         if constexpr (ES == 4) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
@@ -235,8 +239,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             for (int i = 0; i < MW; ++i) mw[i] = __builtin_amdgcn_alignbit(i + 1 < MW ? pmr[i + 1] : 0u, pmr[i], psh);
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
-                dx[k] = h2f<DT>(po[k] & 0xffffu);
-                dy[k] = h2f<DT>(po[k] >> 16);
+                pc[k] = po[k];
                 m[k] = h2f<DT>((k & 1) ? mw[k >> 1] >> 16 : mw[k >> 1] & 0xffffu);
             }
         }
@@ -271,8 +274,16 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             // others are +pb, +pitch, +pitch+pb) and its four weights.
             auto geo = [&](int k, uint32_t& Ak, float& w00, float& w01, float& w10, float& w11) {
                 const int kx = k / KH, ky = k - (k / KH) * KH;
-                const float tx = fminf(fmaxf(G.scale * dx[k], -lim), lim);
-                const float ty = fminf(fmaxf(G.scale * dy[k], -lim), lim);
+                float dxk, dyk;
+                if constexpr (ES == 4) {
+                    dxk = dx[k];
+                    dyk = dy[k];
+                } else {
+                    dxk = h2f<DT>(pc[k] & 0xffffu);
+                    dyk = h2f<DT>(pc[k] >> 16);
+                }
+                const float tx = fminf(fmaxf(G.scale * dxk, -lim), lim);
+                const float ty = fminf(fmaxf(G.scale * dyk, -lim), lim);
                 const float fx = floorf(tx), fy = floorf(ty);
                 const float a = tx - fx, b = ty - fy;
                 const int xs = bxk[kx] + (int)fx;                   // LDS column of the left corners
@@ -429,32 +440,39 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     }
 }
 
+template <int DT, bool SOFTMAX, int NCHV, int WM>
+hipError_t launch_one(const Geom& G, const RingCfg& rc, const void* x, const void* off, const void* mask, void* out,
+                      hipStream_t s)
+{
+    using T = typename Elem<DT>::T;
+    auto* fn = dcn_fwd_ring<DT, 3, 3, SOFTMAX, NCHV, WM>;
+    const hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, rc.lds_bytes);
+    if (e != hipSuccess) return e;
+    fn<<<dim3(rc.nwg), dim3(rc.threads), rc.lds_bytes, s>>>(G, rc, (const T*)x, (const T*)off, (const T*)mask,
+                                                             (T*)out);
+    return hipGetLastError();
+}
+
 template <int DT, bool SOFTMAX>
 hipError_t launch_ring_typed(const Geom& G, const RingCfg& rc, const void* x, const void* off, const void* mask,
                              void* out, hipStream_t s)
 {
     using T = typename Elem<DT>::T;
     const int nch = G.d * (int)sizeof(T) / 16;
-    const dim3 grid(rc.nwg), block(rc.threads);
-#define DCN_RING_CASE(NCHV, WM)                                                                               \
-    case NCHV * 100 + WM: {                                                                                   \
-        auto* fn = dcn_fwd_ring<DT, 3, 3, SOFTMAX, NCHV, WM>;                                                 \
-        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,        \
-                                           rc.lds_bytes);                                                     \
-        if (e != hipSuccess) return e;                                                                        \
-        fn<<<grid, block, rc.lds_bytes, s>>>(G, rc, (const T*)x, (const T*)off, (const T*)mask, (T*)out);      \
-        break;                                                                                                \
+    const bool wide = rc.threads > 512;
+    // 1024-thread workgroups are planned only where nch * es <= 4 (f16/bf16
+    // with D <= 16, f32 with D = 4), so no f32 two-chunk one is built.
+    if (wide && nch == 1) return launch_one<DT, SOFTMAX, 1, 16>(G, rc, x, off, mask, out, s);
+    if constexpr (DT != DT_F32) {
+        if (wide && nch == 2) return launch_one<DT, SOFTMAX, 2, 16>(G, rc, x, off, mask, out, s);
     }
-    switch (nch * 100 + (rc.threads > 512 ? 16 : 8)) {
-        DCN_RING_CASE(1, 8)
-        DCN_RING_CASE(2, 8)
-        DCN_RING_CASE(4, 8)
-        DCN_RING_CASE(1, 16)
-        DCN_RING_CASE(2, 16)
-        default: return hipErrorInvalidValue;
+    if (wide) return hipErrorInvalidValue;
+    switch (nch) {
+        case 1: return launch_one<DT, SOFTMAX, 1, 8>(G, rc, x, off, mask, out, s);
+        case 2: return launch_one<DT, SOFTMAX, 2, 8>(G, rc, x, off, mask, out, s);
+        case 4: return launch_one<DT, SOFTMAX, 4, 8>(G, rc, x, off, mask, out, s);
     }
-#undef DCN_RING_CASE
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -556,10 +574,10 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
         }
         return false;
     };
-    // With at most 32 bytes per corner, a 1024-thread workgroup (four waves
-    // per SIMD, a tap's data in <=128 VGPRs) hides the LDS latency better;
-    // try that first.
-    return (nch <= 2 && try_plan(896)) || try_plan(448);
+    // Where a tap's data and the prefetched offsets fit in 128 VGPRs (nch * es
+    // <= 4: f16/bf16 with D <= 16, f32 with D = 4), a 1024-thread workgroup
+    // (four waves per SIMD) hides the LDS latency better; try that first.
+    return (nch * es <= 4 && try_plan(896)) || try_plan(448);
 }
 
 void device_limits(int* lds_limit, int* num_cus)
