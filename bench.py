@@ -101,23 +101,33 @@ def dcn_fwd_runner(torch, stage, dtype, softmax, seed=1):
     return r
 
 
-def dcn_bwd_runner(torch, softmax, seed=1):
+def dcn_bwd_runner(torch, softmax, seed=1, stage="stage1", dtype="f32"):
+    """DCN backward through dcn_backward_ws (an fp32 grad_x workspace for
+    f16/bf16, none for f32).  min_bytes counts the tensors the op reads (x,
+    offset, mask, grad_out) and writes (grad_x, grad_offset, grad_mask) once,
+    in their own dtype; the workspace's fp32 traffic is not algorithmic."""
     from sparse_deformable_sampling_amd import _binding as B, synth
-    n, h, w, c, g = STAGES["stage1"]
-    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=seed, grad=True)
+    n, h, w, c, g = STAGES[stage]
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype=dtype, seed=seed, grad=True)
+    es = ES[dtype]
     elems = 2 * (d["x"].size + d["offset"].size + d["mask"].size) + d["grad_out"].size
-    min_bytes = elems * 4
-    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, softmax, B.DCN_F32)
-    base = [upload(torch, d[k], "f32") for k in ("x", "offset", "mask", "grad_out")]
+    min_bytes = elems * es
+    code = {"f32": B.DCN_F32, "f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, softmax, code)
+    nbytes = ctypes.c_size_t(0)
+    B.check(B.lib().dcn_backward_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    base = [upload(torch, d[k], dtype) for k in ("x", "offset", "mask", "grad_out")]
     stream = torch.cuda.current_stream()
     args, keep = [], []
     for i in range(n_sets(min_bytes)):
         ins = [t.clone() for t in base] if i else base
         outs = [torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])]
-        keep += ins + outs
+        ws = torch.empty(((nbytes.value + 3) // 4,), dtype=torch.float32, device="cuda") if nbytes.value else None
+        keep += ins + outs + [ws]
         args.append((ctypes.byref(desc),) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + outs) +
-                    (ctypes.c_void_p(stream.cuda_stream),))
-    r = Runner("%s_bwd_stage1_f32" % ("dcnv3" if softmax else "dcnv4"), args, B.lib().dcn_backward,
+                    (ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), ctypes.c_size_t(nbytes.value),
+                     ctypes.c_void_p(stream.cuda_stream)))
+    r = Runner("%s_bwd_%s_%s" % ("dcnv3" if softmax else "dcnv4", stage, dtype), args, B.lib().dcn_backward_ws,
                n * h * w * c * 9, min_bytes, stream)
     r.keep = keep
     return r
@@ -339,7 +349,8 @@ def main():
         elif name.startswith("msda"):
             r = msda_runner(torch)
         elif "_bwd_" in name:
-            r = dcn_bwd_runner(torch, name.startswith("dcnv3"))
+            parts = name.split("_")   # dcnv4_bwd_stage1_f32
+            r = dcn_bwd_runner(torch, name.startswith("dcnv3"), stage=parts[2], dtype=parts[3])
         else:
             parts = name.split("_")   # dcnv4_fwd_stage1_f16
             r = dcn_fwd_runner(torch, parts[2], parts[3], parts[0] == "dcnv3")
@@ -364,8 +375,10 @@ def main():
             secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
-        for softmax in (True, False):
-            r = dcn_bwd_runner(torch, softmax)
+        bwd_jobs = [(True, "stage1", "f32"), (False, "stage1", "f32"), (False, "stage1", "f16"),
+                    (False, "stage1", "bf16"), (False, "stage2", "f16"), (False, "stage3", "f16")]
+        for softmax, stage, dt in bwd_jobs:
+            r = dcn_bwd_runner(torch, softmax, stage=stage, dtype=dt)
             secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r

@@ -65,6 +65,7 @@
 #ifndef LIBDCN_DCN_H
 #define LIBDCN_DCN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -109,18 +110,37 @@ dcn_status dcn_output_size(const dcn_desc* desc, int32_t* h_out, int32_t* w_out)
 dcn_status dcn_forward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
                        void* out, void* stream);
 
-/* Gradients of dcn_forward given grad_out ([n][ho][wo][c]).  grad_x
- * ([n][h][w][c]) is OVERWRITTEN: zero-filled on `stream`, then accumulated
- * with fp32 atomics, so its low bits depend on the order of the atomics.
- * grad_offset and grad_mask (same layouts as offset and mask) are overwritten;
- * with softmax=1 grad_mask is the gradient with respect to the logits passed
- * in `mask`.  Any of grad_x, grad_offset, grad_mask may be NULL to skip it.
- * desc->dtype must be DCN_F32 (otherwise DCN_ERR_UNSUPPORTED).  At a sample
- * coordinate that is exactly an integer the derivative of the cell above the
- * floor (the right-hand derivative) is returned. */
+/* Gradients of dcn_forward given grad_out ([n][ho][wo][c]).  All tensors are
+ * in desc->dtype (f32, f16 or bf16); arithmetic is fp32.  grad_x
+ * ([n][h][w][c]) is OVERWRITTEN: its fp32 sums are zero-filled on `stream`,
+ * then accumulated partly with fp32 atomics, so their low bits depend on the
+ * order of the atomics.  grad_offset and grad_mask (same layouts as offset and
+ * mask) are overwritten; with softmax=1 grad_mask is the gradient with respect
+ * to the logits passed in `mask`.  f16/bf16 results are rounded once, to
+ * nearest even.  Any of grad_x, grad_offset, grad_mask may be NULL to skip
+ * it.  At a sample coordinate that is exactly an integer the derivative of the
+ * cell above the floor (the right-hand derivative) is returned.
+ * An f16/bf16 backward that computes grad_x sums it in an fp32 buffer the
+ * caller provides: use dcn_backward_ws.  dcn_backward is dcn_backward_ws with
+ * no workspace, so for f16/bf16 with grad_x it returns DCN_ERR_INVALID. */
 dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
                         const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
                         void* stream);
+
+/* Bytes of device workspace dcn_backward_ws needs for `desc` when grad_x is
+ * computed: 4*n*h*w*c for f16/bf16 (the fp32 sums of grad_x), 0 for f32.
+ * Half-precision backward is the DCNv4 training case ("DCNv4: Unbounded
+ * Weights", "2. Move Less Data on the GPU": half precision halves the bytes
+ * moved). */
+dcn_status dcn_backward_workspace_size(const dcn_desc* desc, size_t* bytes);
+
+/* dcn_backward with a caller-owned device workspace (4-byte aligned, at least
+ * dcn_backward_workspace_size bytes; may be NULL when that size is 0 or
+ * grad_x is NULL).  Its contents on entry do not matter and are clobbered;
+ * calls that share a workspace must not overlap in time. */
+dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                           const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Multi-scale deformable attention sampling core (see above).
  * spatial_shapes: HOST array [levels][2] = (H_l, W_l), each >= 1.

@@ -98,7 +98,8 @@ def dcn_forward(x, offset, mask, group, kernel=3, stride=1, pad=1, dil=1, offset
 
 def dcn_backward(x, offset, mask, grad_out, group, kernel=3, stride=1, pad=1, dil=1, offset_scale=1.0,
                  softmax=False, need_x=True, need_offset=True, need_mask=True):
-    """(grad_x, grad_offset, grad_mask) of dcn_forward; an output not needed is None."""
+    """(grad_x, grad_offset, grad_mask) of dcn_forward; an output not needed is None.
+    f16/bf16 tensors: grad_x is summed in an fp32 workspace allocated here."""
     dev = _check_tensors(x, offset, mask, grad_out)
     desc, oshape = _desc_for(x, offset, mask, group, kernel, stride, pad, dil, offset_scale, softmax)
     if tuple(grad_out.shape) != oshape:
@@ -107,8 +108,13 @@ def dcn_backward(x, offset, mask, grad_out, group, kernel=3, stride=1, pad=1, di
     gx = torch.empty_like(x) if need_x else None
     go = torch.empty_like(offset) if need_offset else None
     gm = torch.empty_like(mask) if need_mask else None
-    _b.check(_b.lib().dcn_backward(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out),
-                                   _ptr(gx), _ptr(go), _ptr(gm), _stream(dev)))
+    nbytes = ctypes.c_size_t(0)
+    _b.check(_b.lib().dcn_backward_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    ws = torch.empty(((nbytes.value + 3) // 4,), dtype=torch.float32, device=dev) if (need_x and nbytes.value) \
+        else None
+    _b.check(_b.lib().dcn_backward_ws(ctypes.byref(desc), _ptr(x), _ptr(offset), _ptr(mask), _ptr(grad_out),
+                                      _ptr(gx), _ptr(go), _ptr(gm), _ptr(ws), nbytes.value if ws is not None else 0,
+                                      _stream(dev)))
     return gx, go, gm
 
 

@@ -29,8 +29,8 @@ class MsdaDesc(ctypes.Structure):
                 ("n", "len_q", "heads", "head_dim", "levels", "points", "softmax", "dtype")]
 
 
-EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_backward", "dcn_status_str",
-           "dcn_last_error")
+EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "dcn_backward_workspace_size", "dcn_backward_ws",
+           "msda_forward", "msda_backward", "dcn_status_str", "dcn_last_error")
 
 _lib = None
 
@@ -52,6 +52,10 @@ def lib():
     L.dcn_forward.restype = ctypes.c_int
     L.dcn_backward.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]
     L.dcn_backward.restype = ctypes.c_int
+    L.dcn_backward_workspace_size.argtypes = [ctypes.POINTER(DcnDesc), ctypes.POINTER(ctypes.c_size_t)]
+    L.dcn_backward_workspace_size.restype = ctypes.c_int
+    L.dcn_backward_ws.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.dcn_backward_ws.restype = ctypes.c_int
     L.msda_forward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp]
     L.msda_forward.restype = ctypes.c_int
     L.msda_backward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,

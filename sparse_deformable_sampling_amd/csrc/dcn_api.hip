@@ -125,8 +125,16 @@ dcn_status dcn_forward(const dcn_desc* desc, const void* x, const void* offset, 
     return hip_status(dcn::launch_dcn_forward(G, desc->dtype, x, offset, mask, out, (hipStream_t)stream));
 }
 
-dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
-                        const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask, void* stream)
+// Bytes of fp32 workspace a backward of this geometry and dtype needs for
+// its grad_x sums (0 for f32, where grad_x itself holds them).
+static int64_t backward_ws_bytes(const dcn_desc* d)
+{
+    return d->dtype == DCN_F32 ? 0 : (int64_t)d->n * d->h * d->w * d->c * 4;
+}
+
+static dcn_status backward_impl(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                                void* workspace, size_t workspace_bytes, void* stream)
 {
     dcn::Geom G;
     dcn_status st = make_geom(desc, &G);
@@ -138,11 +146,43 @@ dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset,
     if (grad_x && (uintptr_t)grad_x % es) return fail(DCN_ERR_UNSUPPORTED, "grad_x is not aligned");
     if (grad_offset && (uintptr_t)grad_offset % es) return fail(DCN_ERR_UNSUPPORTED, "grad_offset is not aligned");
     if (grad_mask && (uintptr_t)grad_mask % es) return fail(DCN_ERR_UNSUPPORTED, "grad_mask is not aligned");
-    if (desc->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "dcn_backward supports f32 only");
+    const int64_t need = grad_x ? backward_ws_bytes(desc) : 0;
+    if (need > 0) {
+        if (!workspace)
+            return fail(DCN_ERR_INVALID, "an f16/bf16 backward with grad_x needs an fp32 workspace of %lld bytes "
+                        "(dcn_backward_ws)", (long long)need);
+        if ((int64_t)workspace_bytes < need)
+            return fail(DCN_ERR_INVALID, "workspace has %zu bytes, %lld needed", workspace_bytes, (long long)need);
+        if ((uintptr_t)workspace % 4) return fail(DCN_ERR_UNSUPPORTED, "workspace is not aligned to 4 bytes");
+    }
     if (!grad_x && !grad_offset && !grad_mask) return ok();
-    return hip_status(dcn::launch_dcn_backward(G, (const float*)x, (const float*)offset, (const float*)mask,
-                                               (const float*)grad_out, (float*)grad_x, (float*)grad_offset,
-                                               (float*)grad_mask, (hipStream_t)stream));
+    return hip_status(dcn::launch_dcn_backward(G, desc->dtype, x, offset, mask, grad_out, grad_x, grad_offset,
+                                               grad_mask, need > 0 ? (float*)workspace : nullptr,
+                                               (hipStream_t)stream));
+}
+
+dcn_status dcn_backward(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                        const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask, void* stream)
+{
+    return backward_impl(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, nullptr, 0, stream);
+}
+
+dcn_status dcn_backward_workspace_size(const dcn_desc* desc, size_t* bytes)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    if (!bytes) return fail(DCN_ERR_INVALID, "bytes is NULL");
+    *bytes = (size_t)backward_ws_bytes(desc);
+    return ok();
+}
+
+dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                           const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    return backward_impl(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, workspace,
+                         workspace_bytes, stream);
 }
 
 // Validation shared by the MSDA entry points; fills G on success.

@@ -1,4 +1,5 @@
-// DCN backward with grad_x accumulated on chip, for gfx950 (fp32).
+// DCN backward with grad_x accumulated on chip, for gfx950 (f32, f16, bf16
+// storage; fp32 arithmetic, and grad_x summed in fp32).
 //
 // The gradients are those of dcn_backward.hip (the derivative of y_g(p0) =
 // sum_k m_gk x_g(p0 + p_k + dp_gk), "DCNv4: Unbounded Weights", "Why Is
@@ -27,6 +28,9 @@
 // Non-finite inputs, or an S outside [2^-60, 2^60), turn the fixed-point path
 // off for that workgroup (every contribution then takes the fp32 atomic).
 // Integer sums do not depend on the order of the additions.
+// With f16/bf16 storage the inputs are widened to fp32 as they are read,
+// grad_offset and grad_mask are rounded once (to nearest even) as they are
+// stored, and grad_x is summed into an fp32 buffer that the caller converts.
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -54,14 +58,77 @@ __device__ __forceinline__ unsigned long long to_fixed(float t)
     return ((unsigned long long)hi << 32) | lo;
 }
 
-// NV = 16-byte vectors (4 channels each) per lane; a (pixel, group) item has
-// D / (4 NV) lanes.
-template <int KH, int KW, bool SOFTMAX, int NV>
-__global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const float* __restrict__ x,
-                                                   const float* __restrict__ off, const float* __restrict__ mask,
-                                                   const float* __restrict__ gout, float* __restrict__ gx,
-                                                   float* __restrict__ goff, float* __restrict__ gmask)
+// Widen N consecutive storage-type values (N * sizeof(T) a multiple of 8
+// bytes, 8-byte aligned) to fp32.
+template <int DT, int N>
+__device__ __forceinline__ void load_n(const typename Elem<DT>::T* p, float* v)
 {
+    constexpr int RW = N * (int)sizeof(typename Elem<DT>::T) / 4;   // dwords
+    uint32_t w[RW];
+    if constexpr (RW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < RW / 4; ++i) {
+            const u32x4 r = reinterpret_cast<const u32x4*>(p)[i];
+            w[4 * i] = r.x; w[4 * i + 1] = r.y; w[4 * i + 2] = r.z; w[4 * i + 3] = r.w;
+        }
+    } else {
+        static_assert(RW == 2, "8 or a multiple of 16 bytes");
+        const uint2 r = *reinterpret_cast<const uint2*>(p);
+        w[0] = r.x; w[1] = r.y;
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if constexpr (DT == DT_F32) v[j] = __uint_as_float(w[j]);
+        else if constexpr (DT == DT_F16)
+            v[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? w[j >> 1] >> 16 : w[j >> 1] & 0xffffu));
+        else v[j] = __uint_as_float((j & 1) ? w[j >> 1] & 0xffff0000u : w[j >> 1] << 16);
+    }
+}
+
+// The RW dwords holding a lane's CPL channels of one corner, widened to fp32.
+template <int DT, int CPL>
+__device__ __forceinline__ void widen(const uint32_t* w, float* v)
+{
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        if constexpr (DT == DT_F32) v[j] = __uint_as_float(w[j]);
+        else if constexpr (DT == DT_F16)
+            v[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? w[j >> 1] >> 16 : w[j >> 1] & 0xffffu));
+        else v[j] = __uint_as_float((j & 1) ? w[j >> 1] & 0xffff0000u : w[j >> 1] << 16);
+    }
+}
+
+// Buffer loads of RW dwords at byte offset o (an offset past the buffer reads zero).
+template <int RW>
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rs, uint32_t o, uint32_t* w)
+{
+    if constexpr (RW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < RW / 4; ++i) {
+            const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * i, 0, 0);
+            w[4 * i] = r.x; w[4 * i + 1] = r.y; w[4 * i + 2] = r.z; w[4 * i + 3] = r.w;
+        }
+    } else {
+        static_assert(RW == 2, "8 or a multiple of 16 bytes");
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 r = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+        w[0] = r.x; w[1] = r.y;
+    }
+}
+
+// DT = storage type of x, offset, mask, grad_out, grad_offset and grad_mask
+// (grad_x is fp32).  NV: a lane holds 4 NV channels; a (pixel, group) item
+// has D / (4 NV) lanes.
+template <int DT, int KH, int KW, bool SOFTMAX, int NV>
+__global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const typename Elem<DT>::T* __restrict__ x,
+                                                   const typename Elem<DT>::T* __restrict__ off,
+                                                   const typename Elem<DT>::T* __restrict__ mask,
+                                                   const typename Elem<DT>::T* __restrict__ gout,
+                                                   float* __restrict__ gx, typename Elem<DT>::T* __restrict__ goff,
+                                                   typename Elem<DT>::T* __restrict__ gmask)
+{
+    using T = typename Elem<DT>::T;
+    constexpr int ES = (int)sizeof(T);
     constexpr int KF = KH * KW;
     extern __shared__ unsigned long long acc[];   // [aw][w][d] fixed-point sums
     __shared__ float red_s[16];
@@ -79,6 +146,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
     if (r_begin >= r_end) return;
     const int D = G.d, C = G.c, W = G.w, H = G.h;
     constexpr int CPL = 4 * NV;                      // channels per lane
+    constexpr int RW = CPL * ES / 4;                 // dwords of a lane's channels of one corner
     const int d_log = bc.lq_log + 2 + (NV == 2);     // D = CPL * lanes per item, a power of two
     // A window row holds W pixels of D sums at a stride of D + 1 words: the
     // odd stride spreads a wave's atomics over the LDS banks (with a
@@ -102,19 +170,18 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
         const long item = pix * G.g + g;
         float ms = 0.f;
         for (int k = c4; k < K; k += lq) {
-            const float v = mask[item * K + k];
+            const float v = to_f32(mask[item * K + k]);
             ms += fabsf(v);
             bad |= !(fabsf(v) <= 3.0e38f);
         }
         float gm = 0.f;
+        {
+            float a[CPL];
+            load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, a);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + CPL * c4 + 4 * v);
-            const float a4[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gm = fmaxf(gm, fabsf(a4[j]));
-                bad |= !(fabsf(a4[j]) <= 3.0e38f);
+            for (int j = 0; j < CPL; ++j) {
+                gm = fmaxf(gm, fabsf(a[j]));
+                bad |= !(fabsf(a[j]) <= 3.0e38f);
             }
         }
         ms = lane_sum(ms, lq);
@@ -164,7 +231,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
 #pragma unroll
             for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
                 if (!KF && k >= K) break;
-                m[k] = mask[item * K + k];
+                m[k] = to_f32(mask[item * K + k]);
             }
             if constexpr (SOFTMAX) {
                 float mx = m[0];
@@ -188,15 +255,8 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                 }
             }
             float gc[CPL];
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const float4 g4 = *reinterpret_cast<const float4*>(gout + pix * C + (long)g * D + CPL * c4 + 4 * v);
-                gc[4 * v] = g4.x;
-                gc[4 * v + 1] = g4.y;
-                gc[4 * v + 2] = g4.z;
-                gc[4 * v + 3] = g4.w;
-            }
-            const float* ob = off + item * K * 2;
+            load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, gc);
+            const T* ob = off + item * K * 2;
             const int bx = wo * G.sw - G.pw, by = r * G.sh - G.ph;
             float sdm = 0.f;
             // One tap's channel sums, its writes of grad_offset, and its
@@ -239,8 +299,8 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                 dm[k] = sm;
                 sdm += m[k] * sm;
                 if (c4 == 0 && goff) {
-                    goff[(item * K + k) * 2 + 0] = G.scale * m[k] * sdx;
-                    goff[(item * K + k) * 2 + 1] = G.scale * m[k] * sdy;
+                    goff[(item * K + k) * 2 + 0] = from_f32<DT>(G.scale * m[k] * sdx);
+                    goff[(item * K + k) * 2 + 1] = from_f32<DT>(G.scale * m[k] * sdy);
                 }
             };
             if constexpr (KF > 0) {
@@ -255,51 +315,39 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
                     const int kx = k / KH, ky = k - kx * KH;
-                    const float tx = fminf(fmaxf(G.scale * ob[2 * k], -lim), lim);
-                    const float ty = fminf(fmaxf(G.scale * ob[2 * k + 1], -lim), lim);
+                    const float tx = fminf(fmaxf(G.scale * to_f32(ob[2 * k]), -lim), lim);
+                    const float ty = fminf(fmaxf(G.scale * to_f32(ob[2 * k + 1]), -lim), lim);
                     const float fx = floorf(tx), fy = floorf(ty);
                     fa[k] = tx - fx;
                     fb[k] = ty - fy;
                     const int x0 = bx + kx * G.dw + (int)fx, y0 = by + ky * G.dh + (int)fy;
                     xk[k] = x0;
                     yk[k] = y0;
-                    const bool cx0 = (unsigned)x0 < (unsigned)W, cx1 = (unsigned)(x0 + 1) < (unsigned)W;
+                    // A sample exactly on the edge px = -1 (or py = -1) is outside
+                    // the map, like any px <= -1: zero value and zero gradient.
+                    const bool edge = (x0 == -1 && fa[k] == 0.f) || (y0 == -1 && fb[k] == 0.f);
+                    const bool cx0 = (unsigned)x0 < (unsigned)W && !edge, cx1 = (unsigned)(x0 + 1) < (unsigned)W && !edge;
                     const bool cy0 = (unsigned)y0 < (unsigned)H, cy1 = (unsigned)(y0 + 1) < (unsigned)H;
-                    const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * 4);
-                    const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
+                    const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * ES);
+                    const uint32_t bC = (uint32_t)C * ES, bR = (uint32_t)W * C * ES;
                     o4[k][0] = (cy0 && cx0) ? b00 : OOB;
                     o4[k][1] = (cy0 && cx1) ? b00 + bC : OOB;
                     o4[k][2] = (cy1 && cx0) ? b00 + bR : OOB;
                     o4[k][3] = (cy1 && cx1) ? b00 + bR + bC : OOB;
                 }
                 // The corners of tap k+1 are in flight while tap k is summed.
-                u32x4 buf[2][4][NV];
+                uint32_t buf[2][4][RW];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int v = 0; v < NV; ++v)
-                        buf[0][q][v] = __builtin_amdgcn_raw_buffer_load_b128(xr, o4[0][q] + 16u * v, 0, 0);
+                for (int q = 0; q < 4; ++q) load_raw<RW>(xr, o4[0][q], buf[0][q]);
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
                     if (k + 1 < KF) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-#pragma unroll
-                            for (int v = 0; v < NV; ++v)
-                                buf[(k + 1) & 1][q][v] =
-                                    __builtin_amdgcn_raw_buffer_load_b128(xr, o4[k + 1][q] + 16u * v, 0, 0);
+                        for (int q = 0; q < 4; ++q) load_raw<RW>(xr, o4[k + 1][q], buf[(k + 1) & 1][q]);
                     }
                     float X[4][CPL];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            const u32x4 u = buf[k & 1][q][v];
-                            X[q][4 * v] = __uint_as_float(u.x);
-                            X[q][4 * v + 1] = __uint_as_float(u.y);
-                            X[q][4 * v + 2] = __uint_as_float(u.z);
-                            X[q][4 * v + 3] = __uint_as_float(u.w);
-                        }
+                    for (int q = 0; q < 4; ++q) widen<DT, CPL>(buf[k & 1][q], X[q]);
                     tap_finish(k, fa[k], fb[k], xk[k], yk[k], o4[k], X[0], X[1], X[2], X[3]);
                 }
             } else {
@@ -307,7 +355,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
             for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
                 if (!KF && k >= K) break;
                 const int kx = k / kh, ky = k - kx * kh;
-                const float tx = G.scale * ob[2 * k], ty = G.scale * ob[2 * k + 1];
+                const float tx = G.scale * to_f32(ob[2 * k]), ty = G.scale * to_f32(ob[2 * k + 1]);
                 float a = 0.f, b = 0.f;
                 int x0 = -2, y0 = -2;
                 uint32_t o4[4] = {OOB, OOB, OOB, OOB};
@@ -322,24 +370,21 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
                     b = ty - fy;
                     x0 = bx + kx * G.dw + (int)fx;
                     y0 = by + ky * G.dh + (int)fy;
-                    if (x0 >= -1 && x0 < W && y0 >= -1 && y0 < H) {
+                    // px <= -1 or py <= -1 (the edge included), px >= W, py >= H: outside
+                    if (x0 >= -1 && x0 < W && y0 >= -1 && y0 < H && !(x0 == -1 && a == 0.f) && !(y0 == -1 && b == 0.f)) {
                         const bool cx0 = x0 >= 0, cx1 = x0 + 1 < W, cy0 = y0 >= 0, cy1 = y0 + 1 < H;
-                        const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * 4);
-                        const uint32_t bC = (uint32_t)C * 4u, bR = (uint32_t)W * C * 4u;
+                        const uint32_t b00 = (uint32_t)((img + ((long)y0 * W + x0) * C + (long)g * D + CPL * c4) * ES);
+                        const uint32_t bC = (uint32_t)C * ES, bR = (uint32_t)W * C * ES;
                         o4[0] = (cy0 && cx0) ? b00 : OOB;
                         o4[1] = (cy0 && cx1) ? b00 + bC : OOB;
                         o4[2] = (cy1 && cx0) ? b00 + bR : OOB;
                         o4[3] = (cy1 && cx1) ? b00 + bR + bC : OOB;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-#pragma unroll
-                            for (int v = 0; v < NV; ++v) {
-                                const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(xr, o4[q] + 16u * v, 0, 0);
-                                X[q][4 * v] = __uint_as_float(u.x);
-                                X[q][4 * v + 1] = __uint_as_float(u.y);
-                                X[q][4 * v + 2] = __uint_as_float(u.z);
-                                X[q][4 * v + 3] = __uint_as_float(u.w);
-                            }
+                        for (int q = 0; q < 4; ++q) {
+                            uint32_t w[RW];
+                            load_raw<RW>(xr, o4[q], w);
+                            widen<DT, CPL>(w, X[q]);
+                        }
                     }
                 }
                 tap_finish(k, a, b, x0, y0, o4, X[0], X[1], X[2], X[3]);
@@ -349,7 +394,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
 #pragma unroll
                 for (int k = 0; k < (KF ? KF : KMAX_WIN); ++k) {
                     if (!KF && k >= K) break;
-                    gmask[item * K + k] = SOFTMAX ? m[k] * (dm[k] - sdm) : dm[k];
+                    gmask[item * K + k] = from_f32<DT>(SOFTMAX ? m[k] * (dm[k] - sdm) : dm[k]);
                 }
             }
         }
@@ -383,7 +428,8 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const f
 
 }  // namespace
 
-bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit, int num_cus, BwdWinCfg* bc)
+bool plan_bwd_win(const Geom& G, int dtype, const void* x, const void* gout, int lds_limit, int num_cus,
+                  BwdWinCfg* bc)
 {
     if (G.d % 4 != 0) return false;
     const int nv = G.d % 8 == 0 ? 2 : 1;   // 8 channels per lane when D allows
@@ -391,7 +437,7 @@ bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit,
     if (lq > 64 || (lq & (lq - 1)) != 0) return false;
     if (G.K > KMAX_WIN) return false;
     if ((uintptr_t)x % 16 || (uintptr_t)gout % 16) return false;
-    const long x_bytes = (long)G.n * G.h * G.w * G.c * 4;
+    const long x_bytes = (long)G.n * G.h * G.w * G.c * (dtype == DT_F32 ? 4 : 2);
     if (x_bytes >= (1L << 31) - 64) return false;
     int lq_log = 0;
     while ((1 << lq_log) < lq) ++lq_log;
@@ -438,18 +484,22 @@ bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit,
     return true;
 }
 
-hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, const float* x, const float* off,
-                                   const float* mask, const float* gout, float* gx, float* goff, float* gmask,
-                                   hipStream_t s)
+namespace {
+
+template <int DT>
+hipError_t launch_win_typed(const Geom& G, const BwdWinCfg& bc, const void* x, const void* off, const void* mask,
+                            const void* gout, float* gx, void* goff, void* gmask, hipStream_t s)
 {
+    using T = typename Elem<DT>::T;
     const dim3 grid(bc.nwg), block(bc.threads);
 #define DCN_BWIN(KHV, KWV, SM)                                                                                   \
     {                                                                                                           \
-        auto* fn = bc.nv == 2 ? dcn_bwd_win<KHV, KWV, SM, 2> : dcn_bwd_win<KHV, KWV, SM, 1>;                    \
+        auto* fn = bc.nv == 2 ? dcn_bwd_win<DT, KHV, KWV, SM, 2> : dcn_bwd_win<DT, KHV, KWV, SM, 1>;            \
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,          \
                                            bc.lds_bytes);                                                       \
         if (e != hipSuccess) return e;                                                                          \
-        fn<<<grid, block, bc.lds_bytes, s>>>(G, bc, x, off, mask, gout, gx, goff, gmask);                        \
+        fn<<<grid, block, bc.lds_bytes, s>>>(G, bc, (const T*)x, (const T*)off, (const T*)mask, (const T*)gout,  \
+                                             gx, (T*)goff, (T*)gmask);                                           \
     }
     const bool k33 = G.kh == 3 && G.kw == 3;
     if (k33 && G.softmax) DCN_BWIN(3, 3, true)
@@ -458,6 +508,20 @@ hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, const flo
     else DCN_BWIN(0, 0, false)
 #undef DCN_BWIN
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, int dtype, const void* x, const void* off,
+                                   const void* mask, const void* gout, float* gx, void* goff, void* gmask,
+                                   hipStream_t s)
+{
+    switch (dtype) {
+        case DT_F32: return launch_win_typed<DT_F32>(G, bc, x, off, mask, gout, gx, goff, gmask, s);
+        case DT_F16: return launch_win_typed<DT_F16>(G, bc, x, off, mask, gout, gx, goff, gmask, s);
+        case DT_BF16: return launch_win_typed<DT_BF16>(G, bc, x, off, mask, gout, gx, goff, gmask, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dcn

@@ -10,7 +10,7 @@ namespace dcn {
 
 struct BwdWinCfg {
     int lq_log;       // log2 of the lanes per item
-    int nv;           // 16-byte vectors per lane (4 * nv channels per lane)
+    int nv;           // 4 * nv channels per lane
     int ip;           // items per pass (threads / lanes per item)
     int tr;           // output rows per step
     int hy;           // halo rows above and below a step's footprint kept in the window
@@ -23,11 +23,14 @@ struct BwdWinCfg {
     uint32_t x_bytes; // bytes of x (buffer extent)
 };
 
-// Fill `bc` for geometry G; false if the windowed kernel does not apply.
-bool plan_bwd_win(const Geom& G, const void* x, const void* gout, int lds_limit, int num_cus, BwdWinCfg* bc);
+// Fill `bc` for geometry G and storage type dtype; false if the windowed
+// kernel does not apply.
+bool plan_bwd_win(const Geom& G, int dtype, const void* x, const void* gout, int lds_limit, int num_cus,
+                  BwdWinCfg* bc);
 
-hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, const float* x, const float* off,
-                                   const float* mask, const float* gout, float* gx, float* goff, float* gmask,
+// x, off, mask, gout, goff and gmask in the storage type; gx is fp32.
+hipError_t launch_dcn_backward_win(const Geom& G, const BwdWinCfg& bc, int dtype, const void* x, const void* off,
+                                   const void* mask, const void* gout, float* gx, void* goff, void* gmask,
                                    hipStream_t s);
 
 }  // namespace dcn

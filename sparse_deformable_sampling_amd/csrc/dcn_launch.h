@@ -31,8 +31,11 @@ struct MsdaGeom {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_dcn_forward(const Geom& g, int dtype, const void* x, const void* off, const void* mask,
                               void* out, hipStream_t s);
-hipError_t launch_dcn_backward(const Geom& g, const float* x, const float* off, const float* mask,
-                               const float* gout, float* gx, float* goff, float* gmask, hipStream_t s);
+// x, off, mask, gout, gx, goff, gmask in the storage type dtype.  grad_x is
+// summed in fp32: in gx itself for f32, else in ws (n*h*w*c floats, needed
+// only when gx is requested), which is then rounded into gx.
+hipError_t launch_dcn_backward(const Geom& g, int dtype, const void* x, const void* off, const void* mask,
+                               const void* gout, void* gx, void* goff, void* gmask, float* ws, hipStream_t s);
 hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
                                float* out, hipStream_t s);
 hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,

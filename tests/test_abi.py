@@ -104,18 +104,34 @@ def test_forward_rejects_misaligned_pointers():
     assert _call_forward(desc, (0x1001, 0x2000, 0x3000, 0x4000)) == B.DCN_ERR_UNSUPPORTED
 
 
-def test_backward_rejects_half_precision_and_nulls():
+def test_backward_workspace_and_nulls():
+    """f16/bf16 backward with grad_x sums in a caller-provided fp32 workspace:
+    its size is 4*n*h*w*c (0 for f32); a missing, short or misaligned one is
+    rejected before any launch."""
     L = B.lib()
     vp = ctypes.c_void_p
+    nbytes = ctypes.c_size_t(123)
+    for dt, want in ((B.DCN_F16, 4 * 8 * 8 * 16), (B.DCN_BF16, 4 * 8 * 8 * 16), (B.DCN_F32, 0)):
+        desc = B.make_desc(1, 8, 8, 16, 2, dtype=dt)
+        assert L.dcn_backward_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)) == B.DCN_OK
+        assert nbytes.value == want
+    assert L.dcn_backward_workspace_size(ctypes.byref(desc), None) == B.DCN_ERR_INVALID
     desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_F16)
-    st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), None,
-                        None, None)
+    ins = (vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000))
+    st = L.dcn_backward(ctypes.byref(desc), *ins, vp(0x5000), None, None, None)
+    assert st == B.DCN_ERR_INVALID and b"workspace" in L.dcn_last_error()
+    st = L.dcn_backward_ws(ctypes.byref(desc), *ins, vp(0x5000), None, None, vp(0x6000), 4095, None)
+    assert st == B.DCN_ERR_INVALID
+    st = L.dcn_backward_ws(ctypes.byref(desc), *ins, vp(0x5000), None, None, vp(0x6002), 4096, None)
     assert st == B.DCN_ERR_UNSUPPORTED
     desc = B.make_desc(1, 8, 8, 16, 2)
     st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), None, vp(0x4000), vp(0x5000), None, None, None)
     assert st == B.DCN_ERR_INVALID
     # nothing requested: a valid no-op, no launch
-    st = L.dcn_backward(ctypes.byref(desc), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), None, None, None, None)
+    st = L.dcn_backward(ctypes.byref(desc), *ins, None, None, None, None)
+    assert st == B.DCN_OK
+    desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_BF16)
+    st = L.dcn_backward_ws(ctypes.byref(desc), *ins, None, None, None, None, 0, None)
     assert st == B.DCN_OK
 
 

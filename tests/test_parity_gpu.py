@@ -216,20 +216,22 @@ def test_invalid_call_leaves_output_untouched(sds):
 # ---------------------------------------------------------------- backward
 
 
-def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=TOL["f32"], offset=("normal", 1.5), gscale=1.0,
-              **geom):
+def check_bwd(sds, name, n, h, w, c, g, softmax, seed=1, tol=None, offset=("normal", 1.5), gscale=1.0,
+              dtype="f32", **geom):
+    tol = TOL[dtype] if tol is None else tol
     kern = geom.get("kernel", 3)
     K = kern * kern if isinstance(kern, int) else kern[0] * kern[1]
     ho, wo = oracle.dcn_out_size(h, w, kern, geom.get("stride", 1), geom.get("pad", 1), geom.get("dil", 1))
-    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, offset=offset, dtype="f32", seed=seed, grad=True)
+    d = synth.dcn_inputs(n, h, w, c, g, (ho, wo), taps=K, offset=offset, dtype=dtype, seed=seed, grad=True)
     if gscale != 1.0:
         d["grad_out"] = synth.store(d["grad_out"] * np.float32(gscale), "f32")
-    x, off, mask, go = (to_dev(d[k], "f32") for k in ("x", "offset", "mask", "grad_out"))
-    say(name, "softmax=%d" % softmax, (n, h, w, c, g), geom)
+    x, off, mask, go = (to_dev(d[k], dtype) for k in ("x", "offset", "mask", "grad_out"))
+    say(name, dtype, "softmax=%d" % softmax, (n, h, w, c, g), geom)
     gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=g, softmax=softmax, **geom)
     rx, roff, rm = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=g, softmax=softmax,
-                                       **geom)
+                                       dtype=dtype, **geom)
     errs = (rel_err(to_host(gx), rx), rel_err(to_host(goff), roff), rel_err(to_host(gm), rm))
+    say("  err", name, dtype, "%.3e %.3e %.3e" % errs)
     assert max(errs) <= tol, (name, softmax, errs)
     return errs
 
@@ -328,6 +330,80 @@ def test_backward_channel_splits(sds, c, g):
 def test_backward_geometries(sds, geom):
     for softmax in (False, True):
         check_bwd(sds, "bwd-geom", 2, 13, 10, 16, 2, softmax, seed=31, **geom)
+
+
+# ---------------------------------------------------------------- half-precision backward
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("softmax", [True, False])
+def test_backward_half_stage1_full(sds, dtype, softmax):
+    """f16/bf16 backward at N=64 H=W=56 C=64 G=4: inputs and grads in the
+    half type, fp32 arithmetic, grad_x summed in an fp32 workspace."""
+    check_bwd(sds, "bwd-half-stage1", 64, 56, 56, 64, 4, softmax, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("stage", ["stage2", "stage3"])
+def test_backward_half_stage2_stage3(sds, dtype, stage):
+    n, hw, c, g = {"stage2": (64, 28, 128, 8), "stage3": (64, 14, 320, 20)}[stage]
+    check_bwd(sds, "bwd-half-" + stage, n, hw, hw, c, g, False, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("c,g", [(16, 4), (12, 4), (15, 3), (32, 1), (8, 4), (48, 2), (2, 1)])
+def test_backward_half_channel_splits(sds, dtype, c, g):
+    """D = 4, 3, 5, 32, 2, 24, 2: the windowed kernel with 4 or 8 channels
+    per lane (8- and 16-byte gathers of 16-bit values), the lane-per-channel
+    and the generic fallbacks."""
+    for softmax in (False, True):
+        check_bwd(sds, "bwd-half-split", 2, 9, 11, c, g, softmax, seed=71, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_half_wide_offsets_and_geometries(sds, dtype):
+    check_bwd(sds, "bwd-half-wide", 4, 40, 44, 64, 4, True, seed=73, offset=("normal", 6.0), dtype=dtype)
+    check_bwd(sds, "bwd-half-geom", 2, 13, 10, 16, 2, False, seed=79, dtype=dtype,
+              kernel=(3, 2), stride=(2, 1), pad=(1, 2), dil=(1, 2))
+    check_bwd(sds, "bwd-half-oscale", 2, 12, 14, 32, 2, False, seed=83, dtype=dtype, offset_scale=-1.25)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_half_partial_outputs(sds, dtype):
+    """Without grad_x no workspace is used; grad_x alone still matches."""
+    d = synth.dcn_inputs(2, 9, 9, 16, 2, (9, 9), dtype=dtype, seed=89, grad=True)
+    x, off, mask, go = (to_dev(d[k], dtype) for k in ("x", "offset", "mask", "grad_out"))
+    say("bwd-half-partial", dtype)
+    rx, roff, rm = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=2, dtype=dtype)
+    gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=2, need_x=False)
+    assert gx is None and rel_err(to_host(goff), roff) <= TOL[dtype] and rel_err(to_host(gm), rm) <= TOL[dtype]
+    gx, goff, gm = sds.dcn_backward(x, off, mask, go, group=2, need_offset=False, need_mask=False)
+    assert goff is None and gm is None and rel_err(to_host(gx), rx) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_backward_samples_exactly_on_the_lower_edges(sds, dtype):
+    """Integer offsets that put samples exactly at px = -1 or py = -1: such a
+    sample is outside the map (zero value and zero gradient), while samples
+    at other integer coordinates take the right-hand derivative."""
+    n, h, w, c, g = 2, 7, 9, 16, 2
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=97, grad=True)
+    off = d["offset"].copy()                      # [n, ho, wo, g, 9, 2], tap k = kx*3 + ky
+    off[:, :, 0, :, 0:3, 0] = 0.0                 # wo = 0, kx = 0: px = -1 exactly
+    off[:, 0, :, :, 0::3, 1] = 0.0                # ho = 0, ky = 0: py = -1 exactly
+    off[:, :, 1, :, 0:3, 0] = -1.0                # wo = 1, kx = 0: px = -1 again
+    off[:, 3, :, :, 3:6, 0] = np.float32(2.0)     # an interior integer coordinate
+    d["offset"] = off
+    if dtype != "f32":
+        d = {k: synth.store(v.astype(np.float32), dtype) for k, v in d.items()}
+    x, o, m, go = (to_dev(d[k], dtype) for k in ("x", "offset", "mask", "grad_out"))
+    say("bwd-edges", dtype)
+    for softmax in (False, True):
+        gx, goff, gm = sds.dcn_backward(x, o, m, go, group=g, softmax=softmax)
+        rx, roff, rm = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=g,
+                                           softmax=softmax, dtype=dtype)
+        errs = (rel_err(to_host(gx), rx), rel_err(to_host(goff), roff), rel_err(to_host(gm), rm))
+        assert max(errs) <= TOL[dtype], (dtype, softmax, errs)
+        assert np.all(to_host(goff)[:, :, 0, :, 0:3, 0] == 0.0)
 
 
 def test_backward_partial_outputs(sds):
