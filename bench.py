@@ -158,6 +158,35 @@ def msda_runner(torch, seed=1):
     return r
 
 
+def msda_ref_runner(torch, seed=1):
+    """MSDA read with locations formed in the kernel: the encoder shape with
+    point references, per-image valid ratios and right/bottom padding.
+    min_bytes: value, offsets, attn and out once, plus the references,
+    ratios and the byte mask."""
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, q, heads, dh, pts = 8, 17821, 8, 32, 4
+    d = synth.msda_ref_inputs(n, MSDA_SHAPES, q, heads, dh, pts, ref_dims=2, padded=True, seed=seed)
+    min_bytes = 4 * (d["value"].size + d["offsets"].size + d["attn"].size + n * q * heads * dh +
+                     d["reference"].size + d["valid_ratios"].size) + d["padding_mask"].size
+    desc = B.MsdaDesc(n, q, heads, dh, len(MSDA_SHAPES), pts, 1, B.DCN_F32)
+    shapes = (ctypes.c_int32 * 8)(*[v for hw in MSDA_SHAPES for v in hw])
+    base = [upload(torch, d[k], "f32") for k in ("value", "reference", "valid_ratios", "offsets", "attn")]
+    base.append(torch.from_numpy(d["padding_mask"]).cuda())
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        ins = [t.clone() for t in base] if i else base
+        out = torch.empty((n, q, heads, dh), device="cuda")
+        keep += ins + [out]
+        v, ref, rat, off, att, pad = (ctypes.c_void_p(t.data_ptr()) for t in ins)
+        args.append((ctypes.byref(desc), shapes, ctypes.c_int32(2), v, ref, rat, off, att, pad,
+                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)))
+    r = Runner("msda_fwd_ref_encoder_f32", args, B.lib().msda_forward_ref, n * q * heads * dh * len(MSDA_SHAPES) * pts,
+               min_bytes, stream)
+    r.keep = keep
+    return r
+
+
 def msda_bwd_runner(torch, seed=1):
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, q, heads, dh, pts = 8, 17821, 8, 32, 4
@@ -346,6 +375,8 @@ def main():
             return copy_calib(torch, args.steps, args.warmup)
         if name.startswith("msda_bwd"):
             r = msda_bwd_runner(torch)
+        elif name.startswith("msda_fwd_ref"):
+            r = msda_ref_runner(torch)
         elif name.startswith("msda"):
             r = msda_runner(torch)
         elif "_bwd_" in name:
@@ -383,6 +414,9 @@ def main():
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
         r = msda_runner(torch)
+        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+        r = msda_ref_runner(torch)
         secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r

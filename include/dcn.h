@@ -148,6 +148,29 @@ dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offs
 dcn_status msda_forward(const msda_desc* desc, const int32_t* spatial_shapes, const void* value,
                         const void* loc, const void* attn, void* out, void* stream);
 
+/* msda_forward with the sampling locations formed in the kernel from
+ * references, valid ratios and offsets, and with padded value cells ("Deformable
+ * DETR: Learn Where to Read", "A reference links resolutions without equating
+ * their pixels", "A learned location can fall between cells" on box
+ * references, and "Math and tensor shapes"):
+ *   reference    [n][len_q][ref_dims], f32, in valid-image normalised
+ *                coordinates: (x, y) for ref_dims 2, (x, y, w, h) for 4;
+ *   valid_ratios [n][levels][2] = (valid W / W_l, valid H / H_l), f32, or NULL
+ *                for ratios of 1;
+ *   offsets      [n][len_q][heads][levels][points][2], f32 (the loc layout);
+ *   padding_mask [n][S] bytes, nonzero = padded value cell, or NULL.
+ * Sample (l, p) of a query with level ratios (r_w, r_h) is read at
+ *   ref_dims 2:  u = x r_w + dx / W_l,              v = y r_h + dy / H_l
+ *   ref_dims 4:  u = x r_w + (dx / points) w r_w / 2, v = y r_h + (dy / points) h r_h / 2
+ * (formed in fp64), then exactly as msda_forward reads loc = (u, v), except
+ * that a padded cell reads zero (the attention module zeroes projected values
+ * at masked positions).  attn, out and the other requirements are those of
+ * msda_forward; ref_dims other than 2 or 4 is DCN_ERR_INVALID. */
+dcn_status msda_forward_ref(const msda_desc* desc, const int32_t* spatial_shapes, int32_t ref_dims,
+                            const void* value, const void* reference, const void* valid_ratios,
+                            const void* offsets, const void* attn, const uint8_t* padding_mask, void* out,
+                            void* stream);
+
 /* Gradients of msda_forward given grad_out ([n][len_q][heads][head_dim]).
  * grad_value ([n][S][heads][head_dim]) is OVERWRITTEN: zero-filled on
  * `stream`, then accumulated with fp32 atomics, so its low bits depend on the

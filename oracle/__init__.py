@@ -165,6 +165,52 @@ def msda_forward(value, shapes, loc, attn, softmax=True, dtype=None, tent=False)
     return out
 
 
+def msda_locations(reference, offsets, shapes, valid_ratios=None):
+    """Sampling locations [n,q,heads,L,P,2] (float64) formed from references
+    and offsets.
+
+    "Deformable DETR: Learn Where to Read", "A reference links resolutions
+    without equating their pixels" and "Math and tensor shapes": a point
+    reference p (valid-image coordinates) maps into level l's padded frame as
+    p * r_l, and the offset is divided by the level's (W_l, H_l); for a box
+    reference (x, y, w, h) the offset term is instead (offset / P) * (w, h) *
+    r_l / 2, with P the points per level ("A learned location can fall between
+    cells", on box references).  r_l = (valid W / W_l, valid H / H_l) per
+    image; no clamping.
+    reference: [n,q,2] or [n,q,4]; offsets: [n,q,heads,L,P,2];
+    valid_ratios: [n,L,2] or None (ratios of 1)."""
+    ref = to_f64(reference)
+    off = to_f64(offsets)
+    n, Q, M, L, P, two = off.shape
+    assert two == 2 and ref.shape[:2] == (n, Q) and ref.shape[2] in (2, 4) and len(shapes) == L
+    ratios = np.ones((n, L, 2)) if valid_ratios is None else to_f64(valid_ratios)
+    loc = np.zeros(off.shape, np.float64)
+    for b in range(n):
+        for q in range(Q):
+            for l in range(L):
+                size = (shapes[l][1], shapes[l][0])          # (W_l, H_l)
+                for axis in range(2):
+                    centre = ref[b, q, axis] * ratios[b, l, axis]
+                    if ref.shape[2] == 4:
+                        shift = off[b, q, :, l, :, axis] / P * ref[b, q, axis + 2] * ratios[b, l, axis] * 0.5
+                    else:
+                        shift = off[b, q, :, l, :, axis] / size[axis]
+                    loc[b, q, :, l, :, axis] = centre + shift
+    return loc
+
+
+def msda_forward_ref(value, shapes, reference, offsets, attn, valid_ratios=None, padding_mask=None, softmax=True):
+    """msda_forward at the locations of msda_locations, after zeroing the
+    value cells marked in padding_mask [n,S] (the attention module zeroes
+    projected values at masked positions: "Deformable DETR...", "A reference
+    links resolutions without equating their pixels")."""
+    v64 = to_f64(value).copy()
+    if padding_mask is not None:
+        v64[np.asarray(padding_mask).astype(bool)] = 0.0
+    loc = msda_locations(reference, offsets, shapes, valid_ratios)
+    return msda_forward(v64, shapes, loc, attn, softmax=softmax)
+
+
 def msda_backward(value, shapes, loc, attn, grad_out, softmax=True, dtype=None):
     """(grad_value, grad_loc, grad_attn) of msda_forward in float64;
     grad_attn is with respect to the values passed in attn (the logits when

@@ -21,7 +21,8 @@ import ctypes
 
 from . import _binding as _b
 
-__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_backward", "DcnError"]
+__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_forward_ref", "msda_backward",
+           "DcnError"]
 
 DcnError = _b.DcnError
 
@@ -136,6 +137,40 @@ def msda_forward(value, spatial_shapes, loc, attn, softmax=True, out=None):
         out = _torch().empty((n, Q, M, Dh), dtype=value.dtype, device=dev)
     _b.check(_b.lib().msda_forward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn), _ptr(out),
                                    _stream(dev)))
+    return out
+
+
+def msda_forward_ref(value, spatial_shapes, reference, offsets, attn, valid_ratios=None, padding_mask=None,
+                     softmax=True, out=None):
+    """msda_forward with locations formed on the GPU from reference points
+    ([n, q, 2]) or boxes ([n, q, 4]), valid ratios ([n, L, 2] or None) and
+    offsets ([n, q, heads, L, P, 2]); padding_mask ([n, S] bool/uint8 or None)
+    marks value cells that read zero."""
+    dev = _check_tensors(value, reference, offsets, attn, *([] if valid_ratios is None else [valid_ratios]))
+    n, S, M, Dh = value.shape
+    if offsets.dim() != 6 or offsets.shape[-1] != 2:
+        raise ValueError("offsets must be [n, q, heads, L, P, 2]")
+    _, Q, M2, L, P, _ = offsets.shape
+    if offsets.shape[0] != n or M2 != M or tuple(attn.shape) != (n, Q, M, L, P) or len(spatial_shapes) != L:
+        raise ValueError("inconsistent value/offsets/attn/spatial_shapes")
+    if reference.dim() != 3 or tuple(reference.shape[:2]) != (n, Q) or reference.shape[2] not in (2, 4):
+        raise ValueError("reference must be [n, q, 2] or [n, q, 4]")
+    if valid_ratios is not None and tuple(valid_ratios.shape) != (n, L, 2):
+        raise ValueError("valid_ratios must be [n, L, 2]")
+    if padding_mask is not None:
+        torch = _torch()
+        if tuple(padding_mask.shape) != (n, S) or padding_mask.device != value.device:
+            raise ValueError("padding_mask must be [n, S] on value's device")
+        padding_mask = padding_mask.to(torch.uint8).contiguous()
+    shapes = (ctypes.c_int32 * (2 * L))(*[int(v) for hw in spatial_shapes for v in hw])
+    if sum(int(h) * int(w) for h, w in spatial_shapes) != S:
+        raise ValueError("sum of H_l*W_l must equal value.shape[1]")
+    desc = _b.MsdaDesc(n, Q, M, Dh, L, P, int(bool(softmax)), _dtype_code(value))
+    if out is None:
+        out = _torch().empty((n, Q, M, Dh), dtype=value.dtype, device=dev)
+    _b.check(_b.lib().msda_forward_ref(ctypes.byref(desc), shapes, int(reference.shape[2]), _ptr(value),
+                                       _ptr(reference), _ptr(valid_ratios), _ptr(offsets), _ptr(attn),
+                                       _ptr(padding_mask), _ptr(out), _stream(dev)))
     return out
 
 

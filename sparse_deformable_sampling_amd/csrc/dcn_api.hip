@@ -199,6 +199,7 @@ static dcn_status msda_geom(const msda_desc* d, const int32_t* shapes, dcn::Msda
         return fail(DCN_ERR_UNSUPPORTED, "at most %d levels are supported", dcn::MSDA_MAX_LEVELS);
     G.n = d->n; G.q = d->len_q; G.m = d->heads; G.dh = d->head_dim; G.L = d->levels; G.P = d->points;
     G.softmax = d->softmax;
+    G.half_inv_p = 0.5 / d->points;
     int64_t S = 0;
     for (int l = 0; l < d->levels; ++l) {
         const int32_t hl = shapes[2 * l], wl = shapes[2 * l + 1];
@@ -206,6 +207,8 @@ static dcn_status msda_geom(const msda_desc* d, const int32_t* shapes, dcn::Msda
             return fail(DCN_ERR_INVALID, "level %d has an invalid shape (%d, %d)", l, hl, wl);
         G.H[l] = hl;
         G.W[l] = wl;
+        G.inv_w[l] = 1.0 / wl;
+        G.inv_h[l] = 1.0 / hl;
         G.start[l] = (int)S;
         S += (int64_t)hl * wl;
         if (S >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
@@ -232,6 +235,28 @@ dcn_status msda_forward(const msda_desc* d, const int32_t* shapes, const void* v
         return st;
     return hip_status(dcn::launch_msda_forward(G, (const float*)value, (const float*)loc, (const float*)attn,
                                                (float*)out, (hipStream_t)stream));
+}
+
+dcn_status msda_forward_ref(const msda_desc* d, const int32_t* shapes, int32_t ref_dims, const void* value,
+                            const void* reference, const void* valid_ratios, const void* offsets, const void* attn,
+                            const uint8_t* padding_mask, void* out, void* stream)
+{
+    dcn::MsdaGeom G;
+    dcn_status st = msda_geom(d, shapes, G);
+    if (st) return st;
+    if (ref_dims != 2 && ref_dims != 4) return fail(DCN_ERR_INVALID, "ref_dims must be 2 or 4 (got %d)", ref_dims);
+    if (!value || !reference || !offsets || !attn || !out)
+        return fail(DCN_ERR_INVALID, "value, reference, offsets, attn and out must not be NULL");
+    if (d->dtype != DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "msda_forward_ref supports f32 only");
+    if ((int64_t)d->n * d->len_q * ref_dims >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
+    if ((st = check_ptr(value, "value", 4)) || (st = check_ptr(reference, "reference", 4)) ||
+        (st = check_ptr(offsets, "offsets", 4)) || (st = check_ptr(attn, "attn", 4)) || (st = check_ptr(out, "out", 4)))
+        return st;
+    if (valid_ratios && (uintptr_t)valid_ratios % 4) return fail(DCN_ERR_UNSUPPORTED, "valid_ratios is not aligned");
+    return hip_status(dcn::launch_msda_forward_ref(G, ref_dims, (const float*)value, (const float*)reference,
+                                                   (const float*)valid_ratios, (const float*)offsets,
+                                                   (const float*)attn, padding_mask, (float*)out,
+                                                   (hipStream_t)stream));
 }
 
 dcn_status msda_backward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,

@@ -26,6 +26,8 @@ struct MsdaGeom {
     int S;                          // sum of H_l * W_l
     int softmax;
     int H[MSDA_MAX_LEVELS], W[MSDA_MAX_LEVELS], start[MSDA_MAX_LEVELS];
+    double inv_w[MSDA_MAX_LEVELS], inv_h[MSDA_MAX_LEVELS];   // 1 / W_l, 1 / H_l
+    double half_inv_p;                                       // 0.5 / P
 };
 
 // Each returns hipSuccess or the launch error.
@@ -38,6 +40,12 @@ hipError_t launch_dcn_backward(const Geom& g, int dtype, const void* x, const vo
                                const void* gout, void* gx, void* goff, void* gmask, float* ws, hipStream_t s);
 hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
                                float* out, hipStream_t s);
+// Locations formed in the kernel from a point (ref_dims 2) or box (4)
+// reference per query, valid ratios [n][L][2] (or NULL: 1) and offsets laid
+// out like loc; pad [n][S] (or NULL) marks value cells that read zero.
+hipError_t launch_msda_forward_ref(const MsdaGeom& g, int ref_dims, const float* value, const float* ref,
+                                   const float* ratios, const float* offsets, const float* attn,
+                                   const uint8_t* pad, float* out, hipStream_t s);
 hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
                                 const float* gout, float* gvalue, float* gloc, float* gattn, hipStream_t s);
 

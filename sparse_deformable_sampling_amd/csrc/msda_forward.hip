@@ -10,6 +10,16 @@
 //    over all levels and points jointly; the head output is the weighted sum
 //    of the sampled head-dim vectors.
 //
+// Locations come either as given normalised (u, v) per sample, or are formed
+// here from a reference per query and an offset per sample ("Deformable
+// DETR...", "A reference links resolutions without equating their pixels" and
+// "Math and tensor shapes"), in fp64:
+//  - point reference (x, y):  u = x r_w + dx / W_l,  v = y r_h + dy / H_l;
+//  - box reference (x, y, w, h):  u = x r_w + (dx / P) w r_w / 2, likewise v;
+// with (r_w, r_h) the level's valid ratios of the image (1 when absent).  An
+// optional padding mask marks value cells as padded; they read zero, as the
+// attention module zeroes projected values at masked positions.
+//
 // Work item = one (image, query, head); a lane holds 4 consecutive channels
 // of the head (16-byte loads of the [n][S][heads][head_dim] value tensor) or,
 // for other head sizes, the whole head.  The pixel coordinate is formed in
@@ -30,20 +40,72 @@ struct Sample {
     bool any;
 };
 
-__device__ __forceinline__ Sample sample_geometry(const MsdaGeom& G, int l, float u, float v, float A, long img_head)
+// Where the sample locations come from.  REF = 0: `loc` holds (u, v) per
+// sample.  REF = 2 or 4: `loc` holds the per-sample offsets (same layout),
+// `ref` the per-query point or box, `ratio` [n][L][2] valid ratios (or NULL).
+// `pad` [n][S] marks padded value cells (or NULL).
+struct MsdaSrc {
+    const float* loc;
+    const float* ref;
+    const float* ratio;
+    const uint8_t* pad;
+};
+
+// Normalised location (u, v) of sample i (level l) of item (n, q, head), fp64.
+// `rat`, when given, holds image n's valid ratios per level (else they are
+// read from src.ratio).
+template <int REF>
+__device__ __forceinline__ void sample_uv(const MsdaGeom& G, const MsdaSrc& src, int n, int q, long item, int l, int i,
+                                          double& u, double& v, const float2* rat = nullptr)
+{
+    const int LP = G.L * G.P;
+    const float2 t = *reinterpret_cast<const float2*>(src.loc + (item * LP + i) * 2);
+    if constexpr (REF == 0) {
+        u = t.x;
+        v = t.y;
+    } else {
+        const float* r = src.ref + ((long)n * G.q + q) * REF;
+        double rw = 1.0, rh = 1.0;
+        if (rat) {
+            rw = rat[l].x;
+            rh = rat[l].y;
+        } else if (src.ratio) {
+            rw = src.ratio[((long)n * G.L + l) * 2];
+            rh = src.ratio[((long)n * G.L + l) * 2 + 1];
+        }
+        // Reciprocals instead of fp64 divisions: one extra rounding of 2^-53.
+        if constexpr (REF == 2) {
+            u = (double)r[0] * rw + (double)t.x * G.inv_w[l];
+            v = (double)r[1] * rh + (double)t.y * G.inv_h[l];
+        } else {
+            u = (double)r[0] * rw + (double)t.x * G.half_inv_p * (double)r[2] * rw;
+            v = (double)r[1] * rh + (double)t.y * G.half_inv_p * (double)r[3] * rh;
+        }
+    }
+}
+
+// Whether value cell `cell` (index within the image's S cells) of image n is padded.
+__device__ __forceinline__ bool padded(const MsdaSrc& src, const MsdaGeom& G, int n, long cell)
+{
+    return src.pad && src.pad[(long)n * G.S + cell] != 0;
+}
+
+__device__ __forceinline__ Sample sample_geometry(const MsdaGeom& G, const MsdaSrc& src, int n, int l, double u,
+                                                  double v, float A, long img_head)
 {
     Sample s;
     s.any = false;
     const int Hl = G.H[l], Wl = G.W[l];
-    const double x = (double)u * Wl - 0.5, y = (double)v * Hl - 0.5;
+    const double x = u * Wl - 0.5, y = v * Hl - 0.5;
     if (!(x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl)) return s;
     const double fx = floor(x), fy = floor(y);
     const float a = (float)(x - fx), b = (float)(y - fy);
     const int x0 = (int)fx, y0 = (int)fy;
-    s.c00 = y0 >= 0 && x0 >= 0;
-    s.c01 = y0 >= 0 && x0 + 1 < Wl;
-    s.c10 = y0 + 1 < Hl && x0 >= 0;
-    s.c11 = y0 + 1 < Hl && x0 + 1 < Wl;
+    const long cell = (long)G.start[l] + (long)y0 * Wl + x0;
+    s.c00 = y0 >= 0 && x0 >= 0 && !padded(src, G, n, cell);
+    s.c01 = y0 >= 0 && x0 + 1 < Wl && !padded(src, G, n, cell + 1);
+    s.c10 = y0 + 1 < Hl && x0 >= 0 && !padded(src, G, n, cell + Wl);
+    s.c11 = y0 + 1 < Hl && x0 + 1 < Wl && !padded(src, G, n, cell + Wl + 1);
     const float Aa = A * (1.f - a), Ab = A * a;
     s.w00 = Aa * (1.f - b);
     s.w01 = Ab * (1.f - b);
@@ -68,9 +130,8 @@ __device__ __forceinline__ void head_stats(const float* a, int LP, bool softmax,
 }
 
 // One lane per (image, query, head, 4 channels); P = head_dim / 4 lanes per item.
-template <bool SOFTMAX>
-__global__ __launch_bounds__(256) void msda_fwd_vec4(MsdaGeom G, const float* __restrict__ value,
-                                                     const float* __restrict__ loc,
+template <bool SOFTMAX, int REF>
+__global__ __launch_bounds__(256) void msda_fwd_vec4(MsdaGeom G, const float* __restrict__ value, MsdaSrc src,
                                                      const float* __restrict__ attn, float* __restrict__ out)
 {
     const int P4 = G.dh / 4;
@@ -81,9 +142,9 @@ __global__ __launch_bounds__(256) void msda_fwd_vec4(MsdaGeom G, const float* __
     const int chunk = (int)(t - item * P4);
     const int h = (int)(item % G.m);
     const int n = (int)(item / ((long)G.q * G.m));
+    const int q = (int)((item / G.m) % G.q);
     const int LP = G.L * G.P;
     const float* ai = attn + item * LP;
-    const float* li = loc + item * LP * 2;
     float mx, inv;
     head_stats(ai, LP, SOFTMAX, mx, inv);
     const long img_head = (long)n * G.S * G.m * G.dh + (long)h * G.dh + chunk * 4;
@@ -94,7 +155,9 @@ __global__ __launch_bounds__(256) void msda_fwd_vec4(MsdaGeom G, const float* __
         for (int p = 0; p < G.P; ++p) {
             const int i = l * G.P + p;
             const float A = SOFTMAX ? exp_nonpos(ai[i] - mx) * inv : ai[i];
-            const Sample s = sample_geometry(G, l, li[2 * i], li[2 * i + 1], A, img_head);
+            double u, vv;
+            sample_uv<REF>(G, src, n, q, item, l, i, u, vv);
+            const Sample s = sample_geometry(G, src, n, l, u, vv, A, img_head);
             if (!s.any) continue;
             float v[4];
             if (s.c00) {
@@ -139,14 +202,15 @@ __global__ __launch_bounds__(256) void msda_fwd_vec4(MsdaGeom G, const float* __
 constexpr uint32_t MS_OOB = 0x80000000u;
 constexpr int MS_REC_MAX = 1024;   // sample records per workgroup (32 KB)
 
-template <bool SOFTMAX>
+template <bool SOFTMAX, int REF>
 __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int LQlog, int QT, int tiles, int nwg,
                                                      uint32_t value_bytes, const float* __restrict__ value,
-                                                     const float* __restrict__ loc, const float* __restrict__ attn,
+                                                     MsdaSrc src, const float* __restrict__ attn,
                                                      float* __restrict__ out)
 {
     __shared__ u32x4 rec_o[MS_REC_MAX];
     __shared__ float4 rec_w[MS_REC_MAX];
+    __shared__ float2 rat[MSDA_MAX_LEVELS];   // this image's valid ratios (references only)
     const int nwg_pad = (nwg + 7) & ~7;
     const int b = blockIdx.x;
     const int L = (b & 7) * (nwg_pad >> 3) + (b >> 3);
@@ -158,14 +222,21 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
     const int q0 = tile * QT;
     const uint32_t unit = (uint32_t)G.m * G.dh * 4u;   // bytes from one value row to the next
 
+    if constexpr (REF != 0) {
+        if (tid < G.L)
+            rat[tid] = src.ratio ? make_float2(src.ratio[((long)n * G.L + tid) * 2], src.ratio[((long)n * G.L + tid) * 2 + 1])
+                                 : make_float2(1.f, 1.f);
+        __syncthreads();
+    }
+
     // ---- phase 1: sample records
     const int nsamp = QT << LPlog;
     for (int s = tid; s < nsamp; s += nthr) {
         const int qi = s >> LPlog, i = s & (LP - 1);
         const int q = q0 + qi;
         const bool valid = q < G.q;
-        const long item = ((long)n * G.q + (valid ? q : 0)) * G.m + h;
-        const float2 uv = *reinterpret_cast<const float2*>(loc + (item * LP + i) * 2);
+        const int qc = valid ? q : 0;
+        const long item = ((long)n * G.q + qc) * G.m + h;
         float A = attn[item * LP + i];
         if constexpr (SOFTMAX) {
             float mx = A;
@@ -179,7 +250,9 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
         const int Hl = G.H[l], Wl = G.W[l];
         u32x4 o = {MS_OOB, MS_OOB, MS_OOB, MS_OOB};
         float4 w = {0.f, 0.f, 0.f, 0.f};
-        const double x = (double)uv.x * Wl - 0.5, y = (double)uv.y * Hl - 0.5;
+        double u, v;
+        sample_uv<REF>(G, src, n, qc, item, l, i, u, v, rat);
+        const double x = u * Wl - 0.5, y = v * Hl - 0.5;
         if (valid && x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl) {
             const double fx = floor(x), fy = floor(y);
             const float a = (float)(x - fx), bb = (float)(y - fy);
@@ -192,10 +265,11 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
             const uint32_t base = (uint32_t)(row * G.m + h) * (uint32_t)(G.dh * 4);
             const uint32_t down = (uint32_t)Wl * unit;
             const bool cx0 = x0 >= 0, cx1 = x0 + 1 < Wl, cy0 = y0 >= 0, cy1 = y0 + 1 < Hl;
-            o.x = (cy0 && cx0) ? base : MS_OOB;
-            o.y = (cy0 && cx1) ? base + unit : MS_OOB;
-            o.z = (cy1 && cx0) ? base + down : MS_OOB;
-            o.w = (cy1 && cx1) ? base + down + unit : MS_OOB;
+            const long cell = (long)G.start[l] + (long)y0 * Wl + x0;
+            o.x = (cy0 && cx0 && !padded(src, G, n, cell)) ? base : MS_OOB;
+            o.y = (cy0 && cx1 && !padded(src, G, n, cell + 1)) ? base + unit : MS_OOB;
+            o.z = (cy1 && cx0 && !padded(src, G, n, cell + Wl)) ? base + down : MS_OOB;
+            o.w = (cy1 && cx1 && !padded(src, G, n, cell + Wl + 1)) ? base + down + unit : MS_OOB;
         }
         rec_o[s] = o;
         rec_w[s] = w;
@@ -234,9 +308,8 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
 }
 
 // Any head_dim: one lane per (image, query, head), channel loop.
-template <bool SOFTMAX>
-__global__ __launch_bounds__(256) void msda_fwd_generic(MsdaGeom G, const float* __restrict__ value,
-                                                        const float* __restrict__ loc,
+template <bool SOFTMAX, int REF>
+__global__ __launch_bounds__(256) void msda_fwd_generic(MsdaGeom G, const float* __restrict__ value, MsdaSrc src,
                                                         const float* __restrict__ attn, float* __restrict__ out)
 {
     const long item = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -244,9 +317,9 @@ __global__ __launch_bounds__(256) void msda_fwd_generic(MsdaGeom G, const float*
     if (item >= items) return;
     const int h = (int)(item % G.m);
     const int n = (int)(item / ((long)G.q * G.m));
+    const int q = (int)((item / G.m) % G.q);
     const int LP = G.L * G.P;
     const float* ai = attn + item * LP;
-    const float* li = loc + item * LP * 2;
     float mx, inv;
     head_stats(ai, LP, SOFTMAX, mx, inv);
     const long img_head = (long)n * G.S * G.m * G.dh + (long)h * G.dh;
@@ -258,7 +331,9 @@ __global__ __launch_bounds__(256) void msda_fwd_generic(MsdaGeom G, const float*
         for (int p = 0; p < G.P; ++p) {
             const int i = l * G.P + p;
             const float A = SOFTMAX ? exp_nonpos(ai[i] - mx) * inv : ai[i];
-            const Sample s = sample_geometry(G, l, li[2 * i], li[2 * i + 1], A, img_head);
+            double u, v;
+            sample_uv<REF>(G, src, n, q, item, l, i, u, v);
+            const Sample s = sample_geometry(G, src, n, l, u, v, A, img_head);
             if (!s.any) continue;
             for (int c = 0; c < G.dh; ++c) {
                 float acc = o[c];
@@ -274,11 +349,14 @@ __global__ __launch_bounds__(256) void msda_fwd_generic(MsdaGeom G, const float*
 
 }  // namespace
 
-hipError_t launch_msda_forward(const MsdaGeom& G, const float* value, const float* loc, const float* attn, float* out,
-                               hipStream_t s)
+namespace {
+
+template <int REF>
+hipError_t launch_src(const MsdaGeom& G, const float* value, const MsdaSrc& src, const float* attn, float* out,
+                      hipStream_t s)
 {
     const long items = (long)G.n * G.q * G.m;
-    const bool aligned = ((uintptr_t)value % 16 == 0) && ((uintptr_t)out % 16 == 0) && ((uintptr_t)loc % 8 == 0);
+    const bool aligned = ((uintptr_t)value % 16 == 0) && ((uintptr_t)out % 16 == 0) && ((uintptr_t)src.loc % 8 == 0);
     const dim3 block(256);
     const int LP = G.L * G.P, LQ = G.dh / 4;
     const long value_bytes = (long)G.n * G.S * G.m * G.dh * 4;
@@ -293,25 +371,42 @@ hipError_t launch_msda_forward(const MsdaGeom& G, const float* value, const floa
         if (nwg < (1L << 30)) {
             const dim3 grid((unsigned)((nwg + 7) & ~7L)), blk((unsigned)(QT * LQ));
             if (G.softmax)
-                msda_fwd_tile<true><<<grid, blk, 0, s>>>(G, LPlog, LQlog, QT, tiles, (int)nwg, (uint32_t)value_bytes,
-                                                         value, loc, attn, out);
+                msda_fwd_tile<true, REF><<<grid, blk, 0, s>>>(G, LPlog, LQlog, QT, tiles, (int)nwg,
+                                                              (uint32_t)value_bytes, value, src, attn, out);
             else
-                msda_fwd_tile<false><<<grid, blk, 0, s>>>(G, LPlog, LQlog, QT, tiles, (int)nwg, (uint32_t)value_bytes,
-                                                          value, loc, attn, out);
+                msda_fwd_tile<false, REF><<<grid, blk, 0, s>>>(G, LPlog, LQlog, QT, tiles, (int)nwg,
+                                                               (uint32_t)value_bytes, value, src, attn, out);
             return hipGetLastError();
         }
     }
     if (aligned && G.dh % 4 == 0) {
         const long lanes = items * (G.dh / 4);
         const dim3 grid((unsigned)((lanes + 255) / 256));
-        if (G.softmax) msda_fwd_vec4<true><<<grid, block, 0, s>>>(G, value, loc, attn, out);
-        else msda_fwd_vec4<false><<<grid, block, 0, s>>>(G, value, loc, attn, out);
+        if (G.softmax) msda_fwd_vec4<true, REF><<<grid, block, 0, s>>>(G, value, src, attn, out);
+        else msda_fwd_vec4<false, REF><<<grid, block, 0, s>>>(G, value, src, attn, out);
     } else {
         const dim3 grid((unsigned)((items + 255) / 256));
-        if (G.softmax) msda_fwd_generic<true><<<grid, block, 0, s>>>(G, value, loc, attn, out);
-        else msda_fwd_generic<false><<<grid, block, 0, s>>>(G, value, loc, attn, out);
+        if (G.softmax) msda_fwd_generic<true, REF><<<grid, block, 0, s>>>(G, value, src, attn, out);
+        else msda_fwd_generic<false, REF><<<grid, block, 0, s>>>(G, value, src, attn, out);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_msda_forward(const MsdaGeom& G, const float* value, const float* loc, const float* attn, float* out,
+                               hipStream_t s)
+{
+    const MsdaSrc src = {loc, nullptr, nullptr, nullptr};
+    return launch_src<0>(G, value, src, attn, out, s);
+}
+
+hipError_t launch_msda_forward_ref(const MsdaGeom& G, int ref_dims, const float* value, const float* ref,
+                                   const float* ratios, const float* offsets, const float* attn,
+                                   const uint8_t* pad, float* out, hipStream_t s)
+{
+    const MsdaSrc src = {offsets, ref, ratios, pad};
+    return ref_dims == 4 ? launch_src<4>(G, value, src, attn, out, s) : launch_src<2>(G, value, src, attn, out, s);
 }
 
 }  // namespace dcn

@@ -16,7 +16,7 @@ from __future__ import annotations
 import numpy as np
 
 # stream ids, one per tensor
-X, OFFSET, MASK, GRAD_OUT, VALUE, REF, MSDA_OFFSET, ATTN = 1, 2, 3, 4, 5, 6, 7, 8
+X, OFFSET, MASK, GRAD_OUT, VALUE, REF, MSDA_OFFSET, ATTN, VALID = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 DTYPES = ("f32", "f16", "bf16")
 
@@ -106,3 +106,45 @@ def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype
     loc = (ref + dev / size).astype(np.float32)
     attn = store(normal((n, len_q, heads, L, points), 1.0, seed, ATTN), dtype)
     return {"value": value, "loc": store(loc, dtype), "attn": attn}
+
+
+def msda_ref_inputs(n, shapes, len_q, heads, head_dim, points, ref_dims=2, offset_std=2.0, padded=True, seed=1):
+    """Inputs of the reference-based MSDA read (f32):
+    value ~ N(0,1) [n,S,heads,head_dim]; attn logits ~ N(0,1);
+    offsets ~ N(0, offset_std) [n,q,heads,L,P,2] (pixels for point references,
+    box-relative units for boxes, where +-P spans the box);
+    reference [n,q,ref_dims] in valid-image coordinates: points ~ U(0,1)^2,
+    boxes (x, y) ~ U(0,1)^2 with (w, h) ~ U(0.05, 0.5)^2.
+    padded=True: image b keeps a fraction f_b ~ U(0.6, 1) of every level's
+    width and height (at least one cell) at the top-left; the rest is
+    right/bottom padding, marked in padding_mask [n,S] (1 = padded), and
+    valid_ratios [n,L,2] = (valid W / W_l, valid H / H_l).  padded=False:
+    ratios of 1 and no mask."""
+    L = len(shapes)
+    S = int(sum(int(hh) * int(ww) for hh, ww in shapes))
+    value = normal((n, S, heads, head_dim), 1.0, seed, VALUE)
+    offsets = normal((n, len_q, heads, L, points, 2), offset_std, seed, MSDA_OFFSET)
+    attn = normal((n, len_q, heads, L, points), 1.0, seed, ATTN)
+    if ref_dims == 2:
+        reference = uniform((n, len_q, 2), 0.0, 1.0, seed, REF)
+    elif ref_dims == 4:
+        u = uniform((n, len_q, 4), 0.0, 1.0, seed, REF)
+        reference = np.concatenate([u[..., :2], 0.05 + 0.45 * u[..., 2:]], axis=-1).astype(np.float32)
+    else:
+        raise ValueError("ref_dims must be 2 or 4")
+    ratios = np.ones((n, L, 2), np.float32)
+    mask = np.zeros((n, S), np.uint8)
+    if padded:
+        frac = uniform((n,), 0.6, 1.0, seed, VALID)
+        start = 0
+        for l, (hh, ww) in enumerate(shapes):
+            for b in range(n):
+                wv = max(1, int(np.ceil(frac[b] * ww)))
+                hv = max(1, int(np.ceil(frac[b] * hh)))
+                ratios[b, l] = (wv / ww, hv / hh)
+                m = np.ones((hh, ww), np.uint8)
+                m[:hv, :wv] = 0
+                mask[b, start:start + hh * ww] = m.reshape(-1)
+            start += hh * ww
+    return {"value": value, "reference": np.ascontiguousarray(reference), "offsets": offsets, "attn": attn,
+            "valid_ratios": ratios if padded else None, "padding_mask": mask if padded else None}

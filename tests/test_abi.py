@@ -199,3 +199,25 @@ def test_torch_wrappers_refuse_cpu_tensors():
     mask = torch.zeros(1, 4, 4, 1, 9)
     with pytest.raises(RuntimeError, match="GPU"):
         sds.dcn_forward(x, off, mask, group=1)
+
+
+def test_msda_forward_ref_validation():
+    """ref_dims must be 2 or 4, the tensors must be given, f32 only; all
+    checked before any launch."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+    shapes = (ctypes.c_int32 * 4)(4, 5, 2, 3)
+    desc = B.MsdaDesc(1, 6, 2, 8, 2, 2, 1, B.DCN_F32)
+    good = (vp(0x1000), vp(0x2000), None, vp(0x3000), vp(0x4000), None, vp(0x5000))
+
+    def call(ref_dims, args):
+        return L.msda_forward_ref(ctypes.byref(desc), shapes, ref_dims, *args[:6], args[6], None)
+
+    assert call(3, good) == B.DCN_ERR_INVALID
+    assert call(2, (vp(0x1000), None) + good[2:]) == B.DCN_ERR_INVALID
+    assert call(4, good[:3] + (None,) + good[4:]) == B.DCN_ERR_INVALID
+    assert call(2, good[:6] + (None,)) == B.DCN_ERR_INVALID
+    assert call(2, (vp(0x1000), vp(0x2002)) + good[2:]) == B.DCN_ERR_UNSUPPORTED
+    assert call(2, good[:2] + (vp(0x2001),) + good[3:]) == B.DCN_ERR_UNSUPPORTED
+    desc.dtype = B.DCN_F16
+    assert call(2, good) == B.DCN_ERR_UNSUPPORTED

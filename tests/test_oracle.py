@@ -502,3 +502,69 @@ def test_msda_encoder_reference_points_are_cell_centres():
     np.testing.assert_allclose(got[0, :, 0, :], d0["value"][0, :, 0, :].astype(np.float64), rtol=0, atol=1e-6)
     with pytest.raises(ValueError):
         synth.msda_inputs(1, shapes, 7, 1, 2, 1, ref="cells")
+
+
+# ---------------------------------------------------------------- MSDA locations from references (NEXT-4)
+
+def test_msda_locations_meaning():
+    """Pins of the location formula by what it means, not by its arithmetic:
+    zero offsets leave the reference (times the valid ratio); a point offset
+    of one level width (in pixels) moves u by exactly 1 on a non-square level,
+    and a height moves v by 1; a box offset of +-P reaches the box's edges."""
+    shapes = [(4, 10), (3, 6)]          # (H, W), non-square
+    n, Q, M, L, P = 1, 2, 1, 2, 4
+    ratios = np.array([[[0.8, 0.5], [0.75, 1.0]]])
+    pts = np.array([[[0.25, 0.5], [0.9, 0.1]]])
+    zero = np.zeros((n, Q, M, L, P, 2))
+    loc = oracle.msda_locations(pts, zero, shapes, ratios)
+    for l in range(L):
+        np.testing.assert_allclose(loc[0, :, 0, l, 0], pts[0] * ratios[0, l], rtol=0, atol=1e-15)
+    step = zero.copy()
+    for l, (H, W) in enumerate(shapes):
+        step[0, :, 0, l, 0] = (W, 0.0)
+        step[0, :, 0, l, 1] = (0.0, H)
+    loc1 = oracle.msda_locations(pts, step, shapes, ratios)
+    np.testing.assert_allclose(loc1[0, :, 0, :, 0] - loc[0, :, 0, :, 0], [[[1, 0]] * L] * Q, atol=1e-12)
+    np.testing.assert_allclose(loc1[0, :, 0, :, 1] - loc[0, :, 0, :, 1], [[[0, 1]] * L] * Q, atol=1e-12)
+    boxes = np.array([[[0.5, 0.4, 0.2, 0.6], [0.3, 0.7, 0.4, 0.2]]])
+    edge = zero.copy()
+    edge[..., 0, 0] = P                 # point 0: +P along x -> right edge
+    edge[..., 1, 0] = -P                # point 1: -P along x -> left edge
+    edge[..., 2, 1] = P                 # point 2: +P along y -> bottom edge
+    locb = oracle.msda_locations(boxes, edge, shapes, ratios)
+    for q in range(Q):
+        x, y, w, h = boxes[0, q]
+        for l in range(L):
+            rw, rh = ratios[0, l]
+            np.testing.assert_allclose(locb[0, q, 0, l, 0], [(x + w / 2) * rw, y * rh], atol=1e-12)
+            np.testing.assert_allclose(locb[0, q, 0, l, 1], [(x - w / 2) * rw, y * rh], atol=1e-12)
+            np.testing.assert_allclose(locb[0, q, 0, l, 2], [x * rw, (y + h / 2) * rh], atol=1e-12)
+            np.testing.assert_allclose(locb[0, q, 0, l, 3], [x * rw, y * rh], atol=1e-12)
+
+
+def test_msda_forward_ref_valid_frame_and_padding():
+    """A valid-image cell centre, mapped through the valid ratio, is the padded
+    frame's cell centre and returns that cell; padded cells read zero."""
+    H, W, Hv, Wv = 5, 8, 4, 6                       # valid region: top-left 4 x 6
+    shapes = [(H, W)]
+    n, M, Dh = 1, 1, 3
+    S = H * W
+    rng = np.random.default_rng(7)
+    value = rng.standard_normal((n, S, M, Dh))
+    cells = [(j, i) for j in range(Hv) for i in range(Wv)]
+    Q = len(cells)
+    ref = np.array([[[(i + 0.5) / Wv, (j + 0.5) / Hv] for j, i in cells]])
+    ratios = np.array([[[Wv / W, Hv / H]]])
+    off = np.zeros((n, Q, M, 1, 1, 2))
+    attn = np.ones((n, Q, M, 1, 1))
+    out = oracle.msda_forward_ref(value, shapes, ref, off, attn, ratios, None, softmax=False)
+    want = np.array([value[0, j * W + i, 0] for j, i in cells])
+    np.testing.assert_allclose(out[0, :, 0], want, rtol=0, atol=1e-12)
+    pad = np.zeros((n, S), np.uint8)
+    pad[0, :] = 1
+    out = oracle.msda_forward_ref(value, shapes, ref, off, attn, ratios, pad, softmax=False)
+    assert np.all(out == 0.0)
+    pad[0, :] = 0
+    pad[0, [j * W + i for j in range(H) for i in range(W) if i >= Wv or j >= Hv]] = 1   # the padded border
+    out = oracle.msda_forward_ref(value, shapes, ref, off, attn, ratios, pad, softmax=False)
+    np.testing.assert_allclose(out[0, :, 0], want, rtol=0, atol=1e-12)

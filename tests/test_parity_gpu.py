@@ -467,6 +467,63 @@ def test_msda_levels_points(sds, shapes, points):
         check_msda(sds, "msda-lp", 2, shapes, 17, 2, 8, points, softmax=softmax, seed=43, offset_std=4.0)
 
 
+# ---------------------------------------------------------------- MSDA from references (NEXT-4)
+
+def check_msda_ref(sds, name, n, shapes, q, heads, dh, points, ref_dims, padded=True, softmax=True, seed=1):
+    import torch
+    d = synth.msda_ref_inputs(n, shapes, q, heads, dh, points, ref_dims=ref_dims, padded=padded, seed=seed)
+    v, ref, off, attn = (to_dev(d[k], "f32") for k in ("value", "reference", "offsets", "attn"))
+    ratios = to_dev(d["valid_ratios"], "f32") if padded else None
+    pad = torch.from_numpy(d["padding_mask"]).cuda() if padded else None
+    say(name, (n, shapes, q, heads, dh, points), "ref_dims=%d padded=%d softmax=%d" % (ref_dims, padded, softmax))
+    got = to_host(sds.msda_forward_ref(v, shapes, ref, off, attn, valid_ratios=ratios, padding_mask=pad,
+                                       softmax=softmax))
+    want = oracle.msda_forward_ref(d["value"], shapes, d["reference"], d["offsets"], d["attn"],
+                                   d["valid_ratios"], d["padding_mask"], softmax=softmax)
+    err = rel_err(got, want)
+    say("  err", name, "%.3e" % err)
+    assert err <= TOL["f32"], (name, err)
+
+
+def test_msda_ref_encoder_padded(sds):
+    """Encoder shape (batch 8, 4 levels 100x134 .. 13x17, 8 heads x 32,
+    4 points), point references, per-image valid ratios and padding."""
+    check_msda_ref(sds, "msda-ref-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4, 2)
+
+
+@pytest.mark.parametrize("padded", [True, False])
+@pytest.mark.parametrize("softmax", [True, False])
+def test_msda_ref_decoder_boxes(sds, padded, softmax):
+    """Decoder-like: 300 box references per image over the encoder levels."""
+    check_msda_ref(sds, "msda-ref-boxes", 4, ENCODER_SHAPES, 300, 8, 32, 4, 4, padded=padded, softmax=softmax,
+                   seed=61)
+
+
+@pytest.mark.parametrize("ref_dims", [2, 4])
+@pytest.mark.parametrize("n,shapes,q,heads,dh,points", [
+    (2, [(6, 5), (3, 3)], 77, 3, 4, 8),              # tiled kernel
+    (1, [(4, 4)], 9, 1, 256, 32),                     # tiled, 64 lanes per query
+    (2, [(7, 9), (4, 5)], 23, 3, 36, 3),              # vec4 kernel (6 samples)
+    (2, [(9, 7), (5, 4), (3, 2)], 17, 2, 3, 2),       # generic kernel (head_dim 3)
+])
+def test_msda_ref_shapes(sds, ref_dims, n, shapes, q, heads, dh, points):
+    for padded in (True, False):
+        check_msda_ref(sds, "msda-ref", n, shapes, q, heads, dh, points, ref_dims, padded=padded, seed=67)
+
+
+def test_msda_ref_matches_loc_path(sds):
+    """With ratios of 1 and no mask, the in-kernel locations give the same
+    result as msda_forward at the oracle's locations (f32-rounded)."""
+    shapes = [(6, 5), (3, 3)]
+    d = synth.msda_ref_inputs(2, shapes, 40, 2, 8, 4, ref_dims=2, padded=False, seed=71)
+    loc = oracle.msda_locations(d["reference"], d["offsets"], shapes).astype(np.float32)
+    v, ref, off, attn, lc = (to_dev(a, "f32") for a in (d["value"], d["reference"], d["offsets"], d["attn"], loc))
+    say("msda-ref-vs-loc")
+    a = to_host(sds.msda_forward_ref(v, shapes, ref, off, attn))
+    b = to_host(sds.msda_forward(v, shapes, lc, attn))
+    assert rel_err(a, b) <= TOL["f32"]
+
+
 # ---------------------------------------------------------------- MSDA backward
 
 
