@@ -146,6 +146,41 @@ def dcn_backward(x, offset, mask, grad_out, group, kernel=(3, 3), stride=(1, 1),
     return gx, go, gm
 
 
+def depthwise3x3(x, weight, bias, dtype=None):
+    """Depthwise 3x3 convolution, stride 1, zero padding 1, float64: the first
+    half of the DCNv4 offset subnetwork, a separable convolution ("DCNv4:
+    Unbounded Weights", "1. Remove Softmax").  x: [n,h,w,c]; weight:
+    [3][3][c] (row, column, channel); bias: [c].  Written as the direct sum
+    out[y,x,c] = bias[c] + sum_{i,j} weight[i,j,c] * x[y+i-1, x+j-1, c]."""
+    x64, w64, b64 = to_f64(x, dtype), to_f64(weight, dtype), to_f64(bias, dtype)
+    n, h, w, c = x64.shape
+    xp = np.zeros((n, h + 2, w + 2, c))
+    xp[:, 1:-1, 1:-1] = x64
+    out = np.broadcast_to(b64, (n, h, w, c)).copy()
+    for i in range(3):
+        for j in range(3):
+            out += w64[i, j] * xp[:, i:i + h, j:j + w]
+    return out
+
+
+def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, taps=9, dtype=None):
+    """Offsets [n,h,w,group,taps,2] and mask [n,h,w,group,taps] (float64) of
+    the DCNv4 front-end: the depthwise 3x3 convolution, then ONE linear layer
+    that predicts offsets and modulation together ("DCNv4...", "1. Remove
+    Softmax": merged offset and weight linears, no softmax, no LayerNorm or
+    GELU between the two halves).  om_weight: [c][group*taps*3] (input x
+    output), om_bias: [group*taps*3]; output channels 0 .. group*taps*2-1 are
+    the offsets in [group][taps][2] order, the rest the mask in [group][taps]
+    order."""
+    d = depthwise3x3(x, dw_weight, dw_bias, dtype)
+    n, h, w, c = d.shape
+    om = d.reshape(-1, c) @ to_f64(om_weight, dtype) + to_f64(om_bias, dtype)
+    no = group * taps * 2
+    offset = om[:, :no].reshape(n, h, w, group, taps, 2)
+    mask = om[:, no:].reshape(n, h, w, group, taps)
+    return offset, mask
+
+
 def msda_forward(value, shapes, loc, attn, softmax=True, dtype=None, tent=False):
     """out[n,q,heads,head_dim] of multi-scale deformable attention, float64.
     value: [n,S,heads,head_dim]; shapes: [(H_l, W_l)]; loc: [n,q,heads,L,P,2]

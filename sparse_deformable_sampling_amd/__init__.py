@@ -21,8 +21,8 @@ import ctypes
 
 from . import _binding as _b
 
-__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "msda_forward", "msda_forward_ref", "msda_backward",
-           "DcnError"]
+__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "dcnv4_offset_mask", "msda_forward", "msda_forward_ref",
+           "msda_backward", "DcnError"]
 
 DcnError = _b.DcnError
 
@@ -117,6 +117,30 @@ def dcn_backward(x, offset, mask, grad_out, group, kernel=3, stride=1, pad=1, di
                                       _ptr(gx), _ptr(go), _ptr(gm), _ptr(ws), nbytes.value if ws is not None else 0,
                                       _stream(dev)))
     return gx, go, gm
+
+
+def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, kernel=3, pad=None, dil=1):
+    """DCNv4 front-end on the GPU: (offset [n,h,w,group,K,2], mask
+    [n,h,w,group,K]) from x [n,h,w,c] through the depthwise 3x3 convolution
+    (dw_weight [3,3,c], dw_bias [c]) and the merged linear (om_weight
+    [c, group*K*3], om_bias [group*K*3]).  f16 or bf16."""
+    dev = _check_tensors(x, dw_weight, dw_bias, om_weight, om_bias)
+    kh, kw = (kernel, kernel) if isinstance(kernel, int) else kernel
+    dh, dw = (dil, dil) if isinstance(dil, int) else dil
+    if pad is None:
+        pad = ((kh - 1) * dh // 2, (kw - 1) * dw // 2)
+    n, h, w, c = x.shape
+    K = kh * kw
+    if tuple(dw_weight.shape) != (3, 3, c) or tuple(dw_bias.shape) != (c,) or \
+            tuple(om_weight.shape) != (c, group * K * 3) or tuple(om_bias.shape) != (group * K * 3,):
+        raise ValueError("dw_weight [3,3,c], dw_bias [c], om_weight [c, group*K*3], om_bias [group*K*3] expected")
+    torch = _torch()
+    offset = torch.empty((n, h, w, group, K, 2), dtype=x.dtype, device=dev)
+    mask = torch.empty((n, h, w, group, K), dtype=x.dtype, device=dev)
+    desc, _ = _desc_for(x, offset, mask, group, (kh, kw), 1, pad, (dh, dw), 1.0, False)
+    _b.check(_b.lib().dcn_offset_mask(ctypes.byref(desc), _ptr(x), _ptr(dw_weight), _ptr(dw_bias), _ptr(om_weight),
+                                      _ptr(om_bias), _ptr(offset), _ptr(mask), _stream(dev)))
+    return offset, mask
 
 
 def msda_forward(value, spatial_shapes, loc, attn, softmax=True, out=None):

@@ -30,6 +30,7 @@ class MsdaDesc(ctypes.Structure):
 
 
 EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "dcn_backward_workspace_size", "dcn_backward_ws",
+           "dcn_offset_mask",
            "msda_forward", "msda_forward_ref", "msda_backward", "dcn_status_str", "dcn_last_error")
 
 _lib = None
@@ -58,6 +59,8 @@ def lib():
     L.dcn_backward_ws.restype = ctypes.c_int
     L.msda_forward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp]
     L.msda_forward.restype = ctypes.c_int
+    L.dcn_offset_mask.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dcn_offset_mask.restype = ctypes.c_int
     L.msda_forward_ref.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp, vp,
                                    vp, vp, vp, vp, vp]
     L.msda_forward_ref.restype = ctypes.c_int

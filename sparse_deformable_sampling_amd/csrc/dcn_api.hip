@@ -8,6 +8,7 @@
 
 #include "../../include/dcn.h"
 #include "dcn_launch.h"
+#include "dcn_ring.h"
 
 namespace {
 
@@ -183,6 +184,31 @@ dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offs
 {
     return backward_impl(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, workspace,
                          workspace_bytes, stream);
+}
+
+dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_weight, const void* dw_bias,
+                           const void* om_weight, const void* om_bias, void* offset, void* mask, void* stream)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    if (G.ho != G.h || G.wo != G.w)
+        return fail(DCN_ERR_UNSUPPORTED, "dcn_offset_mask needs an output the size of the input (stride 1, "
+                    "(kernel-1)*dil == 2*pad)");
+    if (desc->dtype == DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "dcn_offset_mask supports f16 and bf16");
+    if (G.c % 8) return fail(DCN_ERR_UNSUPPORTED, "dcn_offset_mask needs c %% 8 == 0");
+    if ((st = check_ptr(x, "x", 16)) || (st = check_ptr(dw_weight, "dw_weight", 16)) ||
+        (st = check_ptr(dw_bias, "dw_bias", 16)) || (st = check_ptr(om_weight, "om_weight", 2)) ||
+        (st = check_ptr(om_bias, "om_bias", 2)) || (st = check_ptr(offset, "offset", 2)) ||
+        (st = check_ptr(mask, "mask", 2)))
+        return st;
+    if ((int64_t)G.c * G.g * G.K * 3 >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
+    int lds_limit = 65536, num_cus = 256;
+    dcn::device_limits(&lds_limit, &num_cus);
+    if (!dcn::frontend_supported(G, desc->dtype, lds_limit))
+        return fail(DCN_ERR_UNSUPPORTED, "c and group*K*3 are too large for the LDS tiles");
+    return hip_status(dcn::launch_dcn_offset_mask(G, desc->dtype, x, dw_weight, dw_bias, om_weight, om_bias, offset,
+                                                  mask, (hipStream_t)stream));
 }
 
 // Validation shared by the MSDA entry points; fills G on success.

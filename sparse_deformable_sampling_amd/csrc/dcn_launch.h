@@ -38,6 +38,12 @@ hipError_t launch_dcn_forward(const Geom& g, int dtype, const void* x, const voi
 // only when gx is requested), which is then rounded into gx.
 hipError_t launch_dcn_backward(const Geom& g, int dtype, const void* x, const void* off, const void* mask,
                                const void* gout, void* gx, void* goff, void* gmask, float* ws, hipStream_t s);
+// DCNv4 front-end (dcn_frontend.hip): depthwise 3x3 of x, then the merged
+// offset+mask linear, into the core's offset and mask layouts.  f16/bf16,
+// c % 8 == 0; frontend_supported tells whether the LDS tiles fit.
+bool frontend_supported(const Geom& g, int dtype, int lds_limit);
+hipError_t launch_dcn_offset_mask(const Geom& g, int dtype, const void* x, const void* dww, const void* dwb,
+                                  const void* omw, const void* omb, void* off, void* mask, hipStream_t s);
 hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
                                float* out, hipStream_t s);
 // Locations formed in the kernel from a point (ref_dims 2) or box (4)

@@ -221,3 +221,30 @@ def test_msda_forward_ref_validation():
     assert call(2, good[:2] + (vp(0x2001),) + good[3:]) == B.DCN_ERR_UNSUPPORTED
     desc.dtype = B.DCN_F16
     assert call(2, good) == B.DCN_ERR_UNSUPPORTED
+
+
+def test_offset_mask_validation():
+    """The DCNv4 front-end takes f16/bf16, c % 8 == 0, an output the size of
+    the input and all seven tensors (x and the depthwise ones 16-byte
+    aligned); each violation is refused before any launch."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = [vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), vp(0x7000)]
+
+    def call(desc, args=good):
+        return L.dcn_offset_mask(ctypes.byref(desc), *args, None)
+
+    assert call(B.make_desc(1, 8, 8, 16, 2)) == B.DCN_ERR_UNSUPPORTED           # f32
+    assert call(B.make_desc(1, 8, 8, 12, 2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED   # c % 8
+    assert call(B.make_desc(1, 8, 8, 16, 2, stride=2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
+    assert call(B.make_desc(1, 8, 8, 16, 2, pad=0, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
+    desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_BF16)
+    for i in range(7):
+        args = list(good)
+        args[i] = None
+        assert call(desc, args) == B.DCN_ERR_INVALID, i
+    for i, p in ((0, 0x1008), (1, 0x2008), (2, 0x3004), (3, 0x4001), (5, 0x6001)):
+        args = list(good)
+        args[i] = vp(p)
+        assert call(desc, args) == B.DCN_ERR_UNSUPPORTED, i
+    assert L.dcn_offset_mask(None, *good, None) == B.DCN_ERR_INVALID

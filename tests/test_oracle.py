@@ -568,3 +568,42 @@ def test_msda_forward_ref_valid_frame_and_padding():
     pad[0, [j * W + i for j in range(H) for i in range(W) if i >= Wv or j >= Hv]] = 1   # the padded border
     out = oracle.msda_forward_ref(value, shapes, ref, off, attn, ratios, pad, softmax=False)
     np.testing.assert_allclose(out[0, :, 0], want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- DCNv4 front-end (NEXT-3)
+
+def test_depthwise3x3_against_library_correlation():
+    """The direct-sum depthwise convolution equals scipy's 2-D correlation
+    with zero fill, channel by channel (a library routine)."""
+    from scipy.signal import correlate2d
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 5, 7, 3))
+    w = rng.standard_normal((3, 3, 3))
+    b = rng.standard_normal(3)
+    got = oracle.depthwise3x3(x, w, b)
+    for n in range(2):
+        for c in range(3):
+            want = correlate2d(x[n, :, :, c], w[:, :, c], mode="same", boundary="fill", fillvalue=0) + b[c]
+            np.testing.assert_allclose(got[n, :, :, c], want, rtol=0, atol=1e-12)
+
+
+def test_dcnv4_offset_mask_layout_and_special_cases():
+    """A centre-only depthwise kernel is the identity, so the front-end is
+    then one matmul; a one-hot linear column routes input channel i to a
+    chosen offset or mask slot, which pins the output channel order."""
+    rng = np.random.default_rng(5)
+    n, h, w, c, G, K = 1, 4, 5, 6, 2, 9
+    x = rng.standard_normal((n, h, w, c))
+    dw = np.zeros((3, 3, c))
+    dw[1, 1] = 1.0
+    wom = np.zeros((c, G * K * 3))
+    wom[2, (1 * K + 4) * 2 + 1] = 1.0            # channel 2 -> group 1, tap 4, dy
+    wom[5, G * K * 2 + 0 * K + 7] = 1.0          # channel 5 -> mask of group 0, tap 7
+    bom = np.zeros(G * K * 3)
+    bom[G * K * 2 + 1 * K + 0] = 0.5             # bias of the mask of group 1, tap 0
+    off, msk = oracle.dcnv4_offset_mask(x, dw, np.zeros(c), wom, bom, G)
+    assert off.shape == (n, h, w, G, K, 2) and msk.shape == (n, h, w, G, K)
+    np.testing.assert_array_equal(off[..., 1, 4, 1], x[..., 2])
+    np.testing.assert_array_equal(msk[..., 0, 7], x[..., 5])
+    assert np.all(msk[..., 1, 0] == 0.5)
+    assert np.count_nonzero(off) == np.count_nonzero(x[..., 2])

@@ -599,3 +599,68 @@ def test_msda_backward_far_outside_and_partial_outputs(sds):
                 assert rel_err(to_host(t), ref) <= tol
             else:
                 assert t is None
+
+
+# ---------------------------------------------------------------- DCNv4 front-end
+
+
+FRONT_KEYS = ("x", "dw_weight", "dw_bias", "om_weight", "om_bias")
+
+
+def check_frontend(sds, name, n, h, w, c, g, dtype, kernel=3, dil=1, seed=1):
+    kh, kw = (kernel, kernel) if isinstance(kernel, int) else kernel
+    K = kh * kw
+    d = synth.frontend_inputs(n, h, w, c, g, taps=K, dtype=dtype, seed=seed)
+    say(name, dtype, (n, h, w, c, g), "kernel", kernel, "dil", dil)
+    off, mask = sds.dcnv4_offset_mask(*(to_dev(d[k], dtype) for k in FRONT_KEYS), group=g, kernel=kernel, dil=dil)
+    roff, rmask = oracle.dcnv4_offset_mask(*(d[k] for k in FRONT_KEYS), group=g, taps=K, dtype=dtype)
+    eo, em = rel_err(to_host(off), roff), rel_err(to_host(mask), rmask)
+    say("  err", name, dtype, "offset %.3e mask %.3e" % (eo, em))
+    assert eo <= TOL[dtype] and em <= TOL[dtype], (name, dtype, eo, em)
+    return d, off, mask
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("stage", ["stage1", "stage2", "stage3"])
+def test_frontend_stages_full(sds, dtype, stage):
+    """The DCNv4 front-end at the three stage shapes (C=64/128/320, G=4/8/20),
+    batch 8 of the full 64: the kernel is per-pixel, so this spans every tile
+    kind (full rows of 56, a 28-pixel row tile, 14) and all column chunks."""
+    n, hw, c, g = {"stage1": (8, 56, 64, 4), "stage2": (8, 28, 128, 8), "stage3": (8, 14, 320, 20)}[stage]
+    check_frontend(sds, stage, n, hw, hw, c, g, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 8, 1), (2, 3, 70, 8, 2), (1, 5, 129, 24, 3), (3, 9, 11, 40, 5),
+                                   (1, 2, 64, 136, 1), (1, 4, 65, 16, 16), (1, 7, 3, 512, 8)])
+def test_frontend_ragged_shapes(sds, dtype, shape):
+    """Row tiles cut mid-row (w = 70, 129, 65), one pixel, C not a multiple of
+    16 (8, 24, 40, 136: the zero-padded k tail), output counts not a multiple
+    of 16 (3*9*g), several column chunks (g=16: 432 outputs)."""
+    n, h, w, c, g = shape
+    check_frontend(sds, "ragged", n, h, w, c, g, dtype, seed=31)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_frontend_other_kernels(sds, dtype):
+    """K = kernel_h*kernel_w outputs per group for other same-size kernels
+    (the depthwise stays 3x3)."""
+    check_frontend(sds, "k5", 2, 9, 10, 32, 2, dtype, kernel=5)
+    check_frontend(sds, "k1x3", 2, 9, 10, 32, 4, dtype, kernel=(1, 3))
+    check_frontend(sds, "k3d2", 2, 9, 10, 32, 2, dtype, kernel=3, dil=2)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_frontend_feeds_the_core(sds, dtype):
+    """Front-end then core op, both on the GPU: equal to the core op applied to
+    the front-end's own (rounded) outputs in the oracle, i.e. the layouts the
+    front-end writes are the ones the core reads."""
+    n, h, w, c, g = 2, 12, 13, 64, 4
+    d, off, mask = check_frontend(sds, "chain", n, h, w, c, g, dtype, seed=37)
+    x = to_dev(d["x"], dtype)
+    out = sds.dcn_forward(x, off, mask, group=g, softmax=False)
+    host = {"f16": lambda t: to_host(t).astype(np.float16), "bf16": lambda t: synth.store(to_host(t), "bf16")}[dtype]
+    ref = oracle.dcn_forward(d["x"], host(off), host(mask), group=g, softmax=False, dtype=dtype)
+    err = rel_err(to_host(out), ref)
+    say("  err chain core", dtype, "%.3e" % err)
+    assert err <= TOL[dtype]
