@@ -33,7 +33,9 @@ HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
 ES = {"f32": 4, "f16": 2, "bf16": 2}
 
-STAGES = {"stage1": (64, 56, 56, 64, 4), "stage2": (64, 28, 28, 128, 8), "stage3": (64, 14, 14, 320, 20)}
+STAGES = {"stage1": (64, 56, 56, 64, 4), "stage2": (64, 28, 28, 128, 8), "stage3": (64, 14, 14, 320, 20),
+          # the DCNv4 pages' module measurement: 56x56x128, batch 64, 4 groups of 32 channels
+          "table10": (64, 56, 56, 128, 4)}
 
 
 def parse():
@@ -130,6 +132,82 @@ def dcn_bwd_runner(torch, softmax, seed=1, stage="stage1", dtype="f32"):
     r = Runner("%s_bwd_%s_%s" % ("dcnv3" if softmax else "dcnv4", stage, dtype), args, B.lib().dcn_backward_ws,
                n * h * w * c * 9, min_bytes, stream)
     r.keep = keep
+    return r
+
+
+FRONT_KEYS = ("x", "dw_weight", "dw_bias", "om_weight", "om_bias")
+
+
+def frontend_runner(torch, stage, dtype, seed=1):
+    """DCNv4 front-end (dcn_offset_mask): min_bytes counts x, the weights and
+    the offset and mask outputs once."""
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, h, w, c, g = STAGES[stage]
+    d = synth.frontend_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
+    es = ES[dtype]
+    min_bytes = es * (sum(d[k].size for k in FRONT_KEYS) + n * h * w * g * 27)
+    code = {"f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, False, code)
+    base = [upload(torch, d[k], dtype) for k in FRONT_KEYS]
+    stream = torch.cuda.current_stream()
+    args, keep = [], []
+    for i in range(n_sets(min_bytes)):
+        ins = [base[0].clone()] + base[1:] if i else base
+        off = torch.empty((n, h, w, g, 9, 2), dtype=ins[0].dtype, device="cuda")
+        mask = torch.empty((n, h, w, g, 9), dtype=ins[0].dtype, device="cuda")
+        keep += ins + [off, mask]
+        args.append((ctypes.byref(desc),) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + [off, mask]) +
+                    (ctypes.c_void_p(stream.cuda_stream),))
+    r = Runner("dcnv4_offset_mask_%s_%s" % (stage, dtype), args, B.lib().dcn_offset_mask, n * h * w * c * 9,
+               min_bytes, stream)
+    r.keep = keep
+    return r
+
+
+def module_runner(torch, stage="table10", dtype="f16", seed=1):
+    """The whole DCNv4 module forward, as the pages measure it (Table 10):
+    value = input_proj(x) and out = output_proj(core(...)) as plain library
+    GEMMs (torch.mm on the same stream), the front-end and the core in
+    libdcn.  min_bytes sums each step's own reads and writes once:
+    6*P*C + 2*P*G*K*3 elements for P pixels (weights aside)."""
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, h, w, c, g = STAGES[stage]
+    d = synth.frontend_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
+    es = ES[dtype]
+    P = n * h * w
+    min_bytes = es * (6 * P * c + 2 * P * g * 27)
+    code = {"f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, False, code)
+    fe = [upload(torch, d[k], dtype) for k in FRONT_KEYS]
+    rng = np.random.default_rng(seed + 77)
+    w_in, w_out = (upload(torch, synth.store((rng.standard_normal((c, c)) / math.sqrt(c)).astype(np.float32), dtype), dtype)
+                   for _ in range(2))   # [in][out]: x @ w
+    stream = torch.cuda.current_stream()
+    L = B.lib()
+    sets = []
+    for i in range(n_sets(min_bytes)):
+        x = fe[0].clone() if i else fe[0]
+        t = dict(x=x, value=torch.empty((P, c), dtype=x.dtype, device="cuda"),
+                 off=torch.empty((n, h, w, g, 9, 2), dtype=x.dtype, device="cuda"),
+                 mask=torch.empty((n, h, w, g, 9), dtype=x.dtype, device="cuda"),
+                 y=torch.empty((P, c), dtype=x.dtype, device="cuda"), out=torch.empty((P, c), dtype=x.dtype, device="cuda"))
+        sets.append(t)
+    vp = ctypes.c_void_p
+    sp = vp(stream.cuda_stream)
+
+    def step(t):
+        torch.mm(t["x"].view(P, c), w_in, out=t["value"])
+        st = L.dcn_offset_mask(ctypes.byref(desc), vp(t["x"].data_ptr()), *(vp(a.data_ptr()) for a in fe[1:]),
+                               vp(t["off"].data_ptr()), vp(t["mask"].data_ptr()), sp)
+        if st == 0:
+            st = L.dcn_forward(ctypes.byref(desc), vp(t["value"].data_ptr()), vp(t["off"].data_ptr()),
+                               vp(t["mask"].data_ptr()), vp(t["y"].data_ptr()), sp)
+        torch.mm(t["y"], w_out, out=t["out"])
+        return st
+
+    r = Runner("dcnv4_module_%s_%s" % (stage, dtype), [(t,) for t in sets], step, n * h * w * c * 9, min_bytes,
+               stream)
+    r.keep = (fe, w_in, w_out, sets)
     return r
 
 
@@ -373,7 +451,13 @@ def main():
         name = args.only
         if name == "copy_calib":
             return copy_calib(torch, args.steps, args.warmup)
-        if name.startswith("msda_bwd"):
+        if name.startswith("dcnv4_offset_mask"):
+            parts = name.split("_")   # dcnv4_offset_mask_table10_f16
+            r = frontend_runner(torch, parts[3], parts[4])
+        elif name.startswith("dcnv4_module"):
+            parts = name.split("_")   # dcnv4_module_table10_f16
+            r = module_runner(torch, parts[2], parts[3])
+        elif name.startswith("msda_bwd"):
             r = msda_bwd_runner(torch)
         elif name.startswith("msda_fwd_ref"):
             r = msda_ref_runner(torch)
@@ -400,7 +484,8 @@ def main():
     if not args.no_secondary:
         jobs = [("dcnv4", "stage1", "f32"), ("dcnv4", "stage1", "bf16"), ("dcnv3", "stage1", "f32"),
                 ("dcnv3", "stage1", "f16"), ("dcnv4", "stage2", "f16"), ("dcnv4", "stage2", "bf16"),
-                ("dcnv4", "stage3", "f16"), ("dcnv4", "stage3", "bf16")]
+                ("dcnv4", "stage3", "f16"), ("dcnv4", "stage3", "bf16"), ("dcnv4", "table10", "f16"),
+                ("dcnv4", "table10", "f32")]
         for kind, stage, dt in jobs:
             r = dcn_fwd_runner(torch, stage, dt, kind == "dcnv3")
             secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
@@ -413,6 +498,17 @@ def main():
             secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
+        for stage, dt in (("table10", "f16"), ("table10", "bf16"), ("stage1", "f16"), ("stage2", "f16"),
+                          ("stage3", "f16")):
+            r = frontend_runner(torch, stage, dt)
+            secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
+            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+            del r
+        r = module_runner(torch, "table10", "f16")
+        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        secondary[r.name]["context_pages_a100_fp16_ms"] = 0.873
+        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+        del r
         r = msda_runner(torch)
         secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)

@@ -149,15 +149,16 @@ dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offs
  * GELU between).  For every pixel of x ([n][h][w][c]):
  *   d  = depthwise 3x3 of x, stride 1, zero padding 1:
  *        d[c] = dw_bias[c] + sum_{i,j} dw_weight[i][j][c] * x[y+i-1][x+j-1][c]
- *   om = d . om_weight + om_bias       (om_weight [c][group*K*3], om_bias [group*K*3])
+ *   om = om_weight d + om_bias         (om_weight [group*K*3][c], a linear layer's
+ *                                       [out][in] layout; om_bias [group*K*3])
  *   offset[g][k][a] = om[(g*K + k)*2 + a],  mask[g][k] = om[group*K*2 + g*K + k]
  * with K = kernel_h*kernel_w; offset and mask take the layouts dcn_forward
  * reads.  d is rounded to desc->dtype before the linear layer (on the matrix
  * cores, fp32 sums); each output is rounded once.  desc->dtype must be f16 or
  * bf16, c % 8 == 0, and the core's output must have the input's size
  * (stride 1, (kernel-1)*dil == 2*pad); otherwise DCN_ERR_UNSUPPORTED, as when
- * c and group*K*3 exceed the kernel's LDS tiles.  x, dw_weight and dw_bias
- * must be 16-byte aligned. */
+ * c and group*K*3 exceed the kernel's LDS tiles.  x, dw_weight, dw_bias,
+ * om_weight, offset and mask must be 16-byte aligned. */
 dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_weight, const void* dw_bias,
                            const void* om_weight, const void* om_bias, void* offset, void* mask, void* stream);
 

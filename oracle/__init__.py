@@ -168,13 +168,13 @@ def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, taps=9, 
     the DCNv4 front-end: the depthwise 3x3 convolution, then ONE linear layer
     that predicts offsets and modulation together ("DCNv4...", "1. Remove
     Softmax": merged offset and weight linears, no softmax, no LayerNorm or
-    GELU between the two halves).  om_weight: [c][group*taps*3] (input x
-    output), om_bias: [group*taps*3]; output channels 0 .. group*taps*2-1 are
+    GELU between the two halves).  om_weight: [group*taps*3][c] (output x
+    input, as a linear layer stores it), om_bias: [group*taps*3]; output channels 0 .. group*taps*2-1 are
     the offsets in [group][taps][2] order, the rest the mask in [group][taps]
     order."""
     d = depthwise3x3(x, dw_weight, dw_bias, dtype)
     n, h, w, c = d.shape
-    om = d.reshape(-1, c) @ to_f64(om_weight, dtype) + to_f64(om_bias, dtype)
+    om = d.reshape(-1, c) @ to_f64(om_weight, dtype).T + to_f64(om_bias, dtype)
     no = group * taps * 2
     offset = om[:, :no].reshape(n, h, w, group, taps, 2)
     mask = om[:, no:].reshape(n, h, w, group, taps)

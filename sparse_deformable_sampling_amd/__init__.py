@@ -123,7 +123,7 @@ def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, kernel=3
     """DCNv4 front-end on the GPU: (offset [n,h,w,group,K,2], mask
     [n,h,w,group,K]) from x [n,h,w,c] through the depthwise 3x3 convolution
     (dw_weight [3,3,c], dw_bias [c]) and the merged linear (om_weight
-    [c, group*K*3], om_bias [group*K*3]).  f16 or bf16."""
+    [group*K*3, c], om_bias [group*K*3]).  f16 or bf16."""
     dev = _check_tensors(x, dw_weight, dw_bias, om_weight, om_bias)
     kh, kw = (kernel, kernel) if isinstance(kernel, int) else kernel
     dh, dw = (dil, dil) if isinstance(dil, int) else dil
@@ -132,8 +132,8 @@ def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, kernel=3
     n, h, w, c = x.shape
     K = kh * kw
     if tuple(dw_weight.shape) != (3, 3, c) or tuple(dw_bias.shape) != (c,) or \
-            tuple(om_weight.shape) != (c, group * K * 3) or tuple(om_bias.shape) != (group * K * 3,):
-        raise ValueError("dw_weight [3,3,c], dw_bias [c], om_weight [c, group*K*3], om_bias [group*K*3] expected")
+            tuple(om_weight.shape) != (group * K * 3, c) or tuple(om_bias.shape) != (group * K * 3,):
+        raise ValueError("dw_weight [3,3,c], dw_bias [c], om_weight [group*K*3, c], om_bias [group*K*3] expected")
     torch = _torch()
     offset = torch.empty((n, h, w, group, K, 2), dtype=x.dtype, device=dev)
     mask = torch.empty((n, h, w, group, K), dtype=x.dtype, device=dev)

@@ -198,9 +198,9 @@ dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_w
     if (desc->dtype == DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "dcn_offset_mask supports f16 and bf16");
     if (G.c % 8) return fail(DCN_ERR_UNSUPPORTED, "dcn_offset_mask needs c %% 8 == 0");
     if ((st = check_ptr(x, "x", 16)) || (st = check_ptr(dw_weight, "dw_weight", 16)) ||
-        (st = check_ptr(dw_bias, "dw_bias", 16)) || (st = check_ptr(om_weight, "om_weight", 2)) ||
-        (st = check_ptr(om_bias, "om_bias", 2)) || (st = check_ptr(offset, "offset", 2)) ||
-        (st = check_ptr(mask, "mask", 2)))
+        (st = check_ptr(dw_bias, "dw_bias", 16)) || (st = check_ptr(om_weight, "om_weight", 16)) ||
+        (st = check_ptr(om_bias, "om_bias", 2)) || (st = check_ptr(offset, "offset", 16)) ||
+        (st = check_ptr(mask, "mask", 16)))
         return st;
     if ((int64_t)G.c * G.g * G.K * 3 >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
     int lds_limit = 65536, num_cus = 256;

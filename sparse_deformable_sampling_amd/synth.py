@@ -80,13 +80,13 @@ def dcn_inputs(n, h, w, c, group, out_hw, taps=9, offset=("normal", 1.5), dtype=
 def frontend_inputs(n, h, w, c, group, taps=9, dtype="f16", seed=1):
     """Inputs of the DCNv4 front-end: x ~ N(0,1) [n,h,w,c]; depthwise weights
     [3,3,c] ~ N(0, 1/9) and bias [c] ~ N(0, 0.1^2); merged linear weights
-    [c, group*taps*3] ~ N(0, 1/c) and bias ~ N(0, 0.1^2) (unit-scale outputs,
+    [group*taps*3, c] ~ N(0, 1/c) and bias ~ N(0, 0.1^2) (unit-scale outputs,
     like a layer at initialisation)."""
     no = group * taps * 3
     return {"x": store(normal((n, h, w, c), 1.0, seed, X), dtype),
             "dw_weight": store(normal((3, 3, c), 1.0 / 3.0, seed, DW_WEIGHT), dtype),
             "dw_bias": store(normal((c,), 0.1, seed, DW_BIAS), dtype),
-            "om_weight": store(normal((c, no), float(c) ** -0.5, seed, OM_WEIGHT), dtype),
+            "om_weight": store(normal((no, c), float(c) ** -0.5, seed, OM_WEIGHT), dtype),
             "om_bias": store(normal((no,), 0.1, seed, OM_BIAS), dtype)}
 
 

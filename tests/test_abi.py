@@ -225,8 +225,7 @@ def test_msda_forward_ref_validation():
 
 def test_offset_mask_validation():
     """The DCNv4 front-end takes f16/bf16, c % 8 == 0, an output the size of
-    the input and all seven tensors (x and the depthwise ones 16-byte
-    aligned); each violation is refused before any launch."""
+    the input and all seven tensors (16-byte aligned but for om_bias); each violation is refused before any launch."""
     L = B.lib()
     vp = ctypes.c_void_p
     good = [vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), vp(0x7000)]
@@ -243,7 +242,7 @@ def test_offset_mask_validation():
         args = list(good)
         args[i] = None
         assert call(desc, args) == B.DCN_ERR_INVALID, i
-    for i, p in ((0, 0x1008), (1, 0x2008), (2, 0x3004), (3, 0x4001), (5, 0x6001)):
+    for i, p in ((0, 0x1008), (1, 0x2008), (2, 0x3004), (3, 0x4008), (4, 0x5001), (5, 0x6008), (6, 0x7004)):
         args = list(good)
         args[i] = vp(p)
         assert call(desc, args) == B.DCN_ERR_UNSUPPORTED, i

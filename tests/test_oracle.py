@@ -589,16 +589,16 @@ def test_depthwise3x3_against_library_correlation():
 
 def test_dcnv4_offset_mask_layout_and_special_cases():
     """A centre-only depthwise kernel is the identity, so the front-end is
-    then one matmul; a one-hot linear column routes input channel i to a
+    then one matmul; a one-hot linear row routes input channel i to a
     chosen offset or mask slot, which pins the output channel order."""
     rng = np.random.default_rng(5)
     n, h, w, c, G, K = 1, 4, 5, 6, 2, 9
     x = rng.standard_normal((n, h, w, c))
     dw = np.zeros((3, 3, c))
     dw[1, 1] = 1.0
-    wom = np.zeros((c, G * K * 3))
-    wom[2, (1 * K + 4) * 2 + 1] = 1.0            # channel 2 -> group 1, tap 4, dy
-    wom[5, G * K * 2 + 0 * K + 7] = 1.0          # channel 5 -> mask of group 0, tap 7
+    wom = np.zeros((G * K * 3, c))               # [output][input], as a linear layer stores it
+    wom[(1 * K + 4) * 2 + 1, 2] = 1.0            # channel 2 -> group 1, tap 4, dy
+    wom[G * K * 2 + 0 * K + 7, 5] = 1.0          # channel 5 -> mask of group 0, tap 7
     bom = np.zeros(G * K * 3)
     bom[G * K * 2 + 1 * K + 0] = 0.5             # bias of the mask of group 1, tap 0
     off, msk = oracle.dcnv4_offset_mask(x, dw, np.zeros(c), wom, bom, G)
