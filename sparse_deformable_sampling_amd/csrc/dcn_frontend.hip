@@ -258,6 +258,302 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     copy_out(lds + F.o_mask, reinterpret_cast<unsigned char*>(mask + (long)px0 * NMASK), npx * NMASK * 2, tid);
 }
 
+// ---------------------------------------------------------------------------
+// Wave-independent kernel for C8 = KP/8 in {4, 8, 16, 32} (C up to 256): the
+// weights W_om (zero-padded to 16-row blocks) and the bias are loaded into
+// LDS once per workgroup; after that every wave works on its own 16-pixel
+// blocks with no workgroup barrier, so that waves in different phases
+// (loads, products, stores) overlap on a CU.  A lane keeps one 8-channel
+// group (lane % C8) for good, with its nine depthwise weight vectors and
+// bias in registers, and slides a 3 x (R+2) window of x along a run of R
+// pixels of one image row (R = 2 for even widths: six 16-byte loads per
+// pixel instead of nine).  The wave's A tile [16][KP] and output image sit in its own LDS
+// slice.
+
+struct WaveCfg {
+    int AST;         // A / Bt row stride in elements (KP + 8)
+    int NO, NOFF;    // G*K*3 outputs, G*K*2 of them offsets
+    int ncb;         // 16-output blocks
+    int npix, nblk;  // pixels, 16-pixel blocks
+    int nw;          // waves per workgroup
+    int nwg;         // workgroups (a multiple of 8)
+    int bias_off;    // LDS byte offsets: Bt at 0, bias (fp32), wave slices
+    int w_off, w_bytes;  // wave slices: A [16][AST], then the output image in the same bytes
+    int lds_bytes;
+    uint32_t x_bytes;
+    FastDiv div_w, div_h;
+};
+
+// Make this wave's LDS writes visible to its own later LDS reads.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+// acc[u] += w[u] * x[u] for 8 storage-type values in each of w and x.
+template <int DT>
+__device__ __forceinline__ void fma8(u32x4 w, u32x4 x, float* acc)
+{
+    float wv[8], xv[8];
+    widen8<DT>(w, wv);
+    widen8<DT>(x, xv);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(wv[u], xv[u], acc[u]);
+}
+
+__device__ __forceinline__ void wave_copy_out(const unsigned char* src, unsigned char* dst, int bytes, int lane)
+{
+    const int nv = bytes >> 4;
+    for (int u = lane; u < nv; u += 64)
+        *reinterpret_cast<uint4*>(dst + (size_t)u * 16) = *reinterpret_cast<const uint4*>(src + u * 16);
+    const int tail = (bytes - nv * 16) >> 1;
+    if (lane < tail)
+        *reinterpret_cast<uint16_t*>(dst + (size_t)nv * 16 + lane * 2) =
+            *reinterpret_cast<const uint16_t*>(src + nv * 16 + lane * 2);
+}
+
+template <int DT, int C8, int R>
+__global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, const typename Elem<DT>::T* __restrict__ x,
+                                                             const typename Elem<DT>::T* __restrict__ dww,
+                                                             const typename Elem<DT>::T* __restrict__ dwb,
+                                                             const typename Elem<DT>::T* __restrict__ omw,
+                                                             const typename Elem<DT>::T* __restrict__ omb,
+                                                             typename Elem<DT>::T* __restrict__ off,
+                                                             typename Elem<DT>::T* __restrict__ mask)
+{
+    using T = typename Elem<DT>::T;
+    constexpr int KP = C8 * 8, KS = KP / 32;       // MFMA k steps
+    constexpr int RUNS = 16 / R;                  // runs per block
+    constexpr int LPR = 64 / C8;                  // runs one pass of the wave covers
+    extern __shared__ __align__(16) unsigned char lds[];
+    T* Bt = reinterpret_cast<T*>(lds);                           // [ncb*16][AST]
+    const float* bs = reinterpret_cast<const float*>(lds + F.bias_off);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int C = G.c, H = G.h, W = G.w;
+    const int AST = F.AST, NOFF = F.NOFF, NMASK = F.NOFF / 2, NO = F.NO;
+
+    // ---- once per workgroup: W_om rows (zero past NO and C) and the bias
+    {
+        float* bsw = reinterpret_cast<float*>(lds + F.bias_off);
+        const int nthr = F.nw * 64;
+        for (int e = tid; e < F.ncb * 16 * C8; e += nthr) {
+            const int j = e / C8, k8 = (e - j * C8) * 8;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (j < NO && k8 < C) v = *reinterpret_cast<const uint4*>(omw + (long)j * C + k8);
+            *reinterpret_cast<uint4*>(Bt + j * AST + k8) = v;
+        }
+        for (int j = tid; j < NO; j += nthr) bsw[j] = to_f32(omb[j]);
+    }
+    __syncthreads();
+
+    unsigned char* slice = lds + F.w_off + wid * F.w_bytes;
+    T* A = reinterpret_cast<T*>(slice);                           // [16][AST]
+    T* Ooff = reinterpret_cast<T*>(slice);                        // [16][NOFF], over A once it is read
+    T* Omask = Ooff + 16 * NOFF;                                  // [16][NMASK]
+
+    // this lane's channel group, its depthwise weights and bias
+    const int cc = (lane % C8) * 8;
+    const bool live = cc < C;
+    u32x4 wr[9], br = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wr[t] = live ? *reinterpret_cast<const u32x4*>(dww + t * C + cc) : u32x4{0u, 0u, 0u, 0u};
+    if (live) br = *reinterpret_cast<const u32x4*>(dwb + cc);
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)F.x_bytes, 0x00020000);
+    const uint32_t colB = (uint32_t)C * 2u, rowB = (uint32_t)W * colB;
+    const int kg = 8 * (lane >> 4);
+    const bool quad = (NMASK & 3) == 0;
+
+    // blocks: each XCD sweeps a contiguous range, its waves interleaved
+    const int xcd = blockIdx.x % 8, nwx = (gridDim.x / 8) * F.nw;
+    const int q8 = F.nblk / 8, r8 = F.nblk % 8;
+    const int lo = xcd * q8 + min(xcd, r8), cnt = q8 + (xcd < r8 ? 1 : 0);
+    for (int bi = (blockIdx.x / 8) * F.nw + wid; bi < cnt; bi += nwx) {
+        const int px0 = (lo + bi) * 16;
+        const int npx = min(16, F.npix - px0);
+
+        // ---- depthwise into A: runs lane/C8, lane/C8 + LPR, ...  With R = 2
+        // the width is even, so a run never leaves its image row and a run
+        // that starts on a pixel ends on one.  Rows past the block's pixels
+        // are left as they are: they only feed output columns that are not
+        // stored.  Channel groups past C are written as zeros.
+#pragma unroll 1
+        for (int ru = lane / C8; ru < RUNS; ru += LPR) {
+            const int p0 = ru * R;
+            if (p0 >= npx) continue;
+            // keep the weights packed from run to run: their widening stays at
+            // the point of use instead of being hoisted into 72 live registers
+#pragma unroll
+            for (int t = 0; t < 9; ++t) asm volatile("" : "+v"(wr[t].x), "+v"(wr[t].y), "+v"(wr[t].z), "+v"(wr[t].w));
+            asm volatile("" : "+v"(br.x), "+v"(br.y), "+v"(br.z), "+v"(br.w));
+            float acc[R][8];
+            if (live) {
+                const uint32_t pix0 = (uint32_t)(px0 + p0);
+                const uint32_t ny = fdiv(pix0, F.div_w), xc = pix0 - ny * (uint32_t)W;
+                const uint32_t y = ny - fdiv(ny, F.div_h) * (uint32_t)H;
+                const uint32_t base = pix0 * colB + (uint32_t)cc * 2u;
+                const bool up = y > 0, down = y + 1 < (uint32_t)H, left = xc > 0, right = xc + R < (uint32_t)W;
+                u32x4 X[3][R + 2];
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < R + 2; ++j) {
+                        const bool ok = (i != 0 || up) && (i != 2 || down) && (j != 0 || left) && (j != R + 1 || right);
+                        const uint32_t o =
+                            ok ? base + (uint32_t)(i - 1) * rowB + (uint32_t)(j - 1) * colB : 0x80000000u;
+                        X[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
+                    }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    widen8<DT>(br, acc[r]);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) fma8<DT>(wr[i * 3 + j], X[i][r + j], acc[r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) acc[r][u] = 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) store_vec<DT>(A + (p0 + r) * AST + cc, acc[r]);
+        }
+        wave_lds_sync();
+
+        // ---- om^T = W_om d^T for the block's 16 pixels: d fragments held in
+        // registers, weight fragments read from LDS; lane l ends with outputs
+        // j0..j0+3 (j0 = 16*cb + 4*(l/16)) of pixel l%16.
+        uint4 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const uint4*>(A + (lane & 15) * AST + ks * 32 + kg);
+        wave_lds_sync();   // A is in registers now; the output image overwrites it
+        const int row = lane & 15;
+#pragma unroll 2
+        for (int cb = 0; cb < F.ncb; ++cb) {
+            const T* bp = Bt + (cb * 16 + (lane & 15)) * AST + kg;
+            f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mfma32<DT>(*reinterpret_cast<const uint4*>(bp + ks * 32), af[ks], acc);
+            const int j0 = cb * 16 + 4 * (lane >> 4);
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[i] + bs[min(j0 + i, NO - 1)];
+            if (quad && j0 + 3 < NOFF) {
+                *reinterpret_cast<uint2*>(Ooff + row * NOFF + j0) = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+            } else if (quad && j0 >= NOFF && j0 + 3 < NO) {
+                *reinterpret_cast<uint2*>(Omask + row * NMASK + (j0 - NOFF)) =
+                    make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = j0 + i;
+                    if (j < NOFF) Ooff[row * NOFF + j] = from_f32<DT>(v[i]);
+                    else if (j < NO) Omask[row * NMASK + (j - NOFF)] = from_f32<DT>(v[i]);
+                }
+            }
+        }
+        wave_lds_sync();
+
+        // ---- the block's outputs are contiguous in both tensors
+        wave_copy_out(reinterpret_cast<const unsigned char*>(Ooff), reinterpret_cast<unsigned char*>(off + (long)px0 * NOFF),
+                      npx * NOFF * 2, lane);
+        wave_copy_out(reinterpret_cast<const unsigned char*>(Omask),
+                      reinterpret_cast<unsigned char*>(mask + (long)px0 * NMASK), npx * NMASK * 2, lane);
+        wave_lds_sync();   // the image is read out before the next block rewrites it
+    }
+}
+
+template <int DT, int C8, int R>
+hipError_t launch_wave_c8(const Geom& G, const WaveCfg& F, const void* x, const void* dww, const void* dwb,
+                          const void* omw, const void* omb, void* off, void* mask, hipStream_t s)
+{
+    using T = typename Elem<DT>::T;
+    auto* fn = dcn_offset_mask_wave<DT, C8, R>;
+    // Workgroups of 4 or 8 waves, whichever keeps more waves resident on a
+    // CU (the weights are loaded once per workgroup: ties go to 8); as many
+    // workgroups as stay resident together, a multiple of 8 (one range of
+    // blocks per XCD).
+    int lds_limit, num_cus;
+    device_limits(&lds_limit, &num_cus);
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       std::min(F.w_off + 8 * F.w_bytes, lds_limit));
+    if (e != hipSuccess) return e;
+    WaveCfg L = F;
+    int best = -1;
+    for (int nw = 8; nw >= 4; nw /= 2) {
+        const int bytes = F.w_off + nw * F.w_bytes;
+        if (bytes > lds_limit) continue;
+        int per_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, nw * 64, bytes);
+        if (e != hipSuccess) return e;
+        if (per_cu * nw > best) {
+            best = per_cu * nw;
+            L.nw = nw;
+            L.lds_bytes = bytes;
+        }
+    }
+    if (best < 0) return hipErrorInvalidValue;
+    const int need = (F.nblk + L.nw - 1) / L.nw;
+    L.nwg = (std::min(need, std::max(1, best / L.nw) * num_cus) + 7) / 8 * 8;
+    fn<<<dim3(L.nwg), dim3(L.nw * 64), L.lds_bytes, s>>>(G, L, (const T*)x, (const T*)dww, (const T*)dwb,
+                                                         (const T*)omw, (const T*)omb, (T*)off, (T*)mask);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_wave(const Geom& G, const WaveCfg& F, int c8, const void* x, const void* dww, const void* dwb,
+                       const void* omw, const void* omb, void* off, void* mask, hipStream_t s)
+{
+    // runs of two pixels need an even width
+    const bool r2 = G.w % 2 == 0;
+#define DCN_FE_CASE(N)                                                                          \
+    case N:                                                                                     \
+        return r2 ? launch_wave_c8<DT, N, 2>(G, F, x, dww, dwb, omw, omb, off, mask, s)        \
+                  : launch_wave_c8<DT, N, 1>(G, F, x, dww, dwb, omw, omb, off, mask, s);
+    switch (c8) {
+        DCN_FE_CASE(4)
+        DCN_FE_CASE(8)
+        DCN_FE_CASE(16)
+        DCN_FE_CASE(32)
+    }
+#undef DCN_FE_CASE
+    return hipErrorInvalidValue;
+}
+
+// Plan of the wave kernel; false (use the tile kernel) when C rounded up to
+// 32 is not 32, 64, 128 or 256 or the weights and 4 wave slices exceed LDS.
+bool plan_wave(const Geom& G, int dtype, int lds_limit, int num_cus, WaveCfg* F, int* c8)
+{
+    if (dtype != DT_F16 && dtype != DT_BF16) return false;
+    if (G.c % 8 != 0) return false;
+    if ((long)G.n * G.h * G.w * G.c * 2 >= (1l << 31)) return false;
+    const int KP = (G.c + 31) / 32 * 32;
+    if (KP != 32 && KP != 64 && KP != 128 && KP != 256) return false;
+    *c8 = KP / 8;
+    F->AST = KP + 8;
+    F->NO = G.g * G.K * 3;
+    F->NOFF = G.g * G.K * 2;
+    F->ncb = (F->NO + 15) / 16;
+    F->npix = G.n * G.h * G.w;
+    F->nblk = (F->npix + 15) / 16;
+    const int b_bytes = F->ncb * 16 * F->AST * 2;
+    F->bias_off = b_bytes;
+    F->w_off = (b_bytes + F->NO * 4 + 15) / 16 * 16;
+    F->w_bytes = std::max(16 * F->AST * 2, 48 * F->NOFF);
+    // workgroup size and count are set at launch from the kernel's occupancy
+    F->nw = 4;
+    F->lds_bytes = F->w_off + F->nw * F->w_bytes;
+    if (F->lds_bytes > lds_limit) return false;
+    F->nwg = 0;
+    F->x_bytes = (uint32_t)((long)G.n * G.h * G.w * G.c * 2);
+    F->div_w = make_fastdiv((uint32_t)G.w);
+    F->div_h = make_fastdiv((uint32_t)G.h);
+    return true;
+}
+
 template <int DT, int MB>
 hipError_t launch_mb(const Geom& G, const FrontCfg& F, const void* x, const void* dww, const void* dwb,
                      const void* omw, const void* omb, void* off, void* mask, hipStream_t s)
@@ -336,6 +632,11 @@ hipError_t launch_dcn_offset_mask(const Geom& G, int dtype, const void* x, const
 {
     int lds_limit, num_cus;
     device_limits(&lds_limit, &num_cus);
+    WaveCfg WF;
+    int c8;
+    if (plan_wave(G, dtype, lds_limit, num_cus, &WF, &c8))
+        return dtype == DT_F16 ? launch_wave<DT_F16>(G, WF, c8, x, dww, dwb, omw, omb, off, mask, s)
+                               : launch_wave<DT_BF16>(G, WF, c8, x, dww, dwb, omw, omb, off, mask, s);
     FrontCfg F;
     if (!plan_frontend(G, dtype, lds_limit, num_cus, &F)) return hipErrorInvalidValue;
     return dtype == DT_F16 ? launch_typed<DT_F16>(G, F, x, dww, dwb, omw, omb, off, mask, s)
