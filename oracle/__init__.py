@@ -5,18 +5,27 @@ smoke check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py``
 may import this package.  The product library (``sparse_deformable_sampling_amd``)
 never imports it, and the two share no code.
 
-The arithmetic lives in ``dcn_oracle.c`` (compiled with gcc into
-``oracle/_build/liboracle.so``); this module only converts the stored input
-values to float64 exactly and marshals the arrays.  Every function states the
-passage of the pages it follows in the C source:
+The sampling arithmetic lives in ``dcn_oracle.c`` (compiled with gcc into
+``oracle/_build/liboracle.so``); this module converts the stored input values
+to float64 exactly and marshals the arrays.  Two groups of functions here are
+numpy float64 written out from their definitions: the MSDA reference-to-
+location formula (``msda_locations``) and the DCNv4 front-end (the depthwise
+3x3 sum and the merged linear, ``depthwise3x3``, ``dcnv4_offset_mask``).
+Every function states the passage of the pages it follows:
 
 * "InternImage: Deformable Convolutions at Scale", Ch.2-4 (bilinear read,
   DCNv3 operator and softmax, groups);
 * "DCNv4: Unbounded Weights", "Why Is Sampling Just 9 Points Still Slow?" and
-  "1. Remove Softmax" (the per-group sum, unnormalised modulation);
+  "1. Remove Softmax" (the per-group sum, unnormalised modulation, the merged
+  offset/modulation linear after a depthwise 3x3);
 * "Deformable DETR: Learn Where to Read", "A learned location can fall between
   cells" and "Mix samples with a per-head budget" (MSDA sampling and joint
-  softmax).
+  softmax); "A reference links resolutions without equating their pixels"
+  (locations from references and valid ratios).
+
+Conventions no number in the pages fixes (tap order, offset pair order,
+offset_scale, the front-end's output order) are parity unpinned; every other
+function is pinned in ``tests/test_oracle.py``.
 """
 from __future__ import annotations
 

@@ -621,22 +621,27 @@ def check_frontend(sds, name, n, h, w, c, g, dtype, kernel=3, dil=1, seed=1):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("stage", ["stage1", "stage2", "stage3"])
+@pytest.mark.parametrize("stage", ["stage1", "stage2", "stage3", "table10"])
 def test_frontend_stages_full(sds, dtype, stage):
-    """The DCNv4 front-end at the three stage shapes (C=64/128/320, G=4/8/20),
-    batch 8 of the full 64: the kernel is per-pixel, so this spans every tile
-    kind (full rows of 56, a 28-pixel row tile, 14) and all column chunks."""
-    n, hw, c, g = {"stage1": (8, 56, 64, 4), "stage2": (8, 28, 128, 8), "stage3": (8, 14, 320, 20)}[stage]
+    """The DCNv4 front-end at the three stage shapes (C=64/128/320, G=4/8/20)
+    and the pages' module shape (56x56x128, G=4), batch 8 of the full 64: the
+    kernels are per-pixel, so the smaller batch runs the same code paths
+    (the wave kernel for C=64/128, the tile kernel for C=320)."""
+    n, hw, c, g = {"stage1": (8, 56, 64, 4), "stage2": (8, 28, 128, 8), "stage3": (8, 14, 320, 20),
+                   "table10": (8, 56, 128, 4)}[stage]
     check_frontend(sds, stage, n, hw, hw, c, g, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 1, 1, 8, 1), (2, 3, 70, 8, 2), (1, 5, 129, 24, 3), (3, 9, 11, 40, 5),
-                                   (1, 2, 64, 136, 1), (1, 4, 65, 16, 16), (1, 7, 3, 512, 8)])
+                                   (1, 2, 64, 136, 1), (1, 4, 65, 16, 16), (1, 7, 3, 512, 8), (1, 3, 10, 64, 2),
+                                   (2, 6, 20, 256, 4), (1, 5, 7, 192, 2), (2, 4, 9, 256, 8)])
 def test_frontend_ragged_shapes(sds, dtype, shape):
-    """Row tiles cut mid-row (w = 70, 129, 65), one pixel, C not a multiple of
-    16 (8, 24, 40, 136: the zero-padded k tail), output counts not a multiple
-    of 16 (3*9*g), several column chunks (g=16: 432 outputs)."""
+    """Blocks cut mid-row and at the end of the data (870, 645, 30 pixels),
+    odd widths (one-pixel runs), one pixel, C not a multiple of 32 (8, 24, 40,
+    136: the zero-padded k tail), C = 256 (the widest wave-kernel case), C =
+    136, 192 and 512 (the tile kernel), output counts not a multiple of 16
+    or of 4 per pixel (3*9*g), 432 outputs."""
     n, h, w, c, g = shape
     check_frontend(sds, "ragged", n, h, w, c, g, dtype, seed=31)
 
