@@ -169,6 +169,7 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)F.x_bytes, 0x00020000);
     const uint32_t colB = (uint32_t)C * 2u, rowB = (uint32_t)W * colB;
     int p = tid / F.c8, cg = tid - p * F.c8;
+#pragma unroll 2
     for (; p < TM; p += F.dp) {
         const int cc = cg * 8;
         float acc[8];
@@ -216,14 +217,24 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
         f4_t acc[MB];
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb) acc[rb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int kk = 0; kk < F.KP; kk += 32) {
-            const int k0 = kk + kg;
-            const uint4 a = k0 < C ? *reinterpret_cast<const uint4*>(wrow + k0) : make_uint4(0u, 0u, 0u, 0u);
+        // weight fragments eight k steps at a time: the eight loads are in
+        // flight together instead of one L2 round trip per step
+        for (int kc = 0; kc < F.KP; kc += 256) {
+            uint4 wf[8];
 #pragma unroll
-            for (int rb = 0; rb < MB; ++rb) {
-                const uint4 b = *reinterpret_cast<const uint4*>(A + (rb * 16 + (lane & 15)) * F.AST + k0);
-                acc[rb] = mfma32<DT>(a, b, acc[rb]);
+            for (int s = 0; s < 8; ++s) {
+                const int k0 = kc + 32 * s + kg;
+                wf[s] = k0 < C ? *reinterpret_cast<const uint4*>(wrow + k0) : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                if (kc + 32 * s >= F.KP) break;
+                const int k0 = kc + 32 * s + kg;
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb) {
+                    const uint4 b = *reinterpret_cast<const uint4*>(A + (rb * 16 + (lane & 15)) * F.AST + k0);
+                    acc[rb] = mfma32<DT>(wf[s], b, acc[rb]);
+                }
             }
         }
         const int j0 = cb * 16 + 4 * (lane >> 4);
@@ -601,7 +612,8 @@ void layout(const Geom& G, int mb, FrontCfg* F)
 }
 
 // Tile plan: the largest tile whose LDS keeps two workgroups per CU and that
-// still gives two tiles per CU; else the largest that fits at all.  False if
+// still gives a tile per CU (larger tiles reuse each weight fragment read
+// from L2 for more pixels); else the largest that fits at all.  False if
 // not even a 16-pixel tile fits.
 bool plan_frontend(const Geom& G, int dtype, int lds_limit, int num_cus, FrontCfg* F)
 {
@@ -610,7 +622,7 @@ bool plan_frontend(const Geom& G, int dtype, int lds_limit, int num_cus, FrontCf
     if ((long)G.n * G.h * G.w * G.c * 2 >= (1l << 31)) return false;   // buffer offsets, out-of-range marker 2^31
     for (int mb = 4; mb >= 1; mb /= 2) {
         layout(G, mb, F);
-        if (F->lds_bytes <= std::min(FT_LDS_TARGET, lds_limit) && F->ntiles >= 2 * num_cus) return true;
+        if (F->lds_bytes <= std::min(FT_LDS_TARGET, lds_limit) && F->ntiles >= num_cus) return true;
     }
     for (int mb = 4; mb >= 1; mb /= 2) {
         layout(G, mb, F);

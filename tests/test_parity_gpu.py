@@ -635,13 +635,15 @@ def test_frontend_stages_full(sds, dtype, stage):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 1, 1, 8, 1), (2, 3, 70, 8, 2), (1, 5, 129, 24, 3), (3, 9, 11, 40, 5),
                                    (1, 2, 64, 136, 1), (1, 4, 65, 16, 16), (1, 7, 3, 512, 8), (1, 3, 10, 64, 2),
-                                   (2, 6, 20, 256, 4), (1, 5, 7, 192, 2), (2, 4, 9, 256, 8)])
+                                   (2, 6, 20, 256, 4), (1, 5, 7, 192, 2), (2, 4, 9, 256, 8),
+                                   (1, 5, 7, 160, 10)])
 def test_frontend_ragged_shapes(sds, dtype, shape):
     """Blocks cut mid-row and at the end of the data (870, 645, 30 pixels),
     odd widths (one-pixel runs), one pixel, C not a multiple of 32 (8, 24, 40,
     136: the zero-padded k tail), C = 256 (the widest wave-kernel case), C =
-    136, 192 and 512 (the tile kernel), output counts not a multiple of 16
-    or of 4 per pixel (3*9*g), 432 outputs."""
+    136, 160, 192 and 512 (the tile kernel; 160 with 270 outputs on one
+    ragged tile), output counts not a multiple of 16 or of 4 per pixel
+    (3*9*g), 432 outputs."""
     n, h, w, c, g = shape
     check_frontend(sds, "ragged", n, h, w, c, g, dtype, seed=31)
 
