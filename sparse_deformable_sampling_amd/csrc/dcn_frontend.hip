@@ -10,23 +10,26 @@
 //   offset[g][k][0..1] = om[(g*K + k)*2 + 0..1],  mask[g][k] = om[G*K*2 + g*K + k].
 //
 // The op reads x once and writes G*K*3 values per pixel (more bytes out than
-// in for the usual G*K*3 > C): it is HBM-bound, the product is small.  One
-// workgroup of four waves takes a tile of TM consecutive pixels in the
-// flattened [n][h][w] order (no idle rows at narrow maps):
-//  - depthwise: a thread takes (pixel, 8 channels), reads the 3x3
-//    neighbourhood with 16-byte loads (the overlapping rows hit in cache),
-//    sums in fp32 and writes d, rounded once to the storage type, into an LDS
-//    tile A[TM][C] (row stride C+8 elements, so that the 16 rows one MFMA
-//    operand read touches fall on distinct banks);
-//  - the linear layer on the matrix cores, v_mfma_f32_16x16x32 (f16 or bf16
-//    operands, fp32 sums): wave w takes 16-column blocks w, w+4, ...; the A
-//    operand comes from LDS, the B operand straight from W_om in global memory
-//    (16 contiguous bytes of one weight row per lane; the weights, a few KB to
-//    a few hundred KB, stay in L2 across workgroups);
-//  - epilogue: bias added in fp32, each value rounded once into an LDS image
-//    of the tile's outputs.  For consecutive pixels these are one contiguous
-//    block of the offset tensor and one of the mask tensor, which the
-//    workgroup then writes with 16-byte stores.
+// in for the usual G*K*3 > C): it is HBM-bound; the product is small but
+// dense, so it goes on the matrix cores: om^T = W_om d^T with
+// v_mfma_f32_16x16x32 (f16 or bf16 operands, fp32 sums), 16 weight rows as
+// the A operand and 16 pixels of d as the B operand.  Lane l then holds four
+// consecutive outputs of one pixel, which go out as one 8-byte write.  Both
+// kernels work on consecutive pixels of the flattened [n][h][w] order, whose
+// outputs are one contiguous block of the offset tensor and one of the mask
+// tensor: they assemble that block in LDS and write it with 16-byte stores.
+//
+// Two kernels:
+//  - dcn_offset_mask_wave (C up to 256, C/8 dividing 64): W_om in LDS once
+//    per workgroup, then each wave alone on its own 16-pixel blocks (see the
+//    comment above it);
+//  - dcn_offset_mask_k, the tile kernel for the other C: a workgroup of four
+//    waves takes TM = 16, 32 or 64 pixels, computes their depthwise 3x3 (a
+//    thread per (pixel, 8 channels), 16-byte loads, fp32 sums, d rounded
+//    once to the storage type) into an LDS tile A[TM][C] (rows C+8 elements
+//    apart, so that the 16 rows one operand read touches fall on distinct
+//    banks), and wave w takes the 16-output blocks w, w+4, ..., reading
+//    the weight rows straight from L2.
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -278,19 +281,20 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
 // group (lane % C8) for good, with its nine depthwise weight vectors and
 // bias in registers, and slides a 3 x (R+2) window of x along a run of R
 // pixels of one image row (R = 2 for even widths: six 16-byte loads per
-// pixel instead of nine).  The wave's A tile [16][KP] and output image sit in its own LDS
-// slice.
+// pixel instead of nine).  The wave's d tile [16][KP] sits in its own LDS
+// slice; once its MFMA operands are in registers, the block's output image
+// takes the same bytes.
 
 struct WaveCfg {
     int AST;         // A / Bt row stride in elements (KP + 8)
     int NO, NOFF;    // G*K*3 outputs, G*K*2 of them offsets
     int ncb;         // 16-output blocks
     int npix, nblk;  // pixels, 16-pixel blocks
-    int nw;          // waves per workgroup
-    int nwg;         // workgroups (a multiple of 8)
+    int nw;          // waves per workgroup (4 or 8, chosen at launch)
+    int nwg;         // workgroups, a multiple of 8 (chosen at launch)
     int bias_off;    // LDS byte offsets: Bt at 0, bias (fp32), wave slices
     int w_off, w_bytes;  // wave slices: A [16][AST], then the output image in the same bytes
-    int lds_bytes;
+    int lds_bytes;   // w_off + nw * w_bytes
     uint32_t x_bytes;
     FastDiv div_w, div_h;
 };
