@@ -461,6 +461,21 @@ def test_msda_tiled_shapes(sds, n, shapes, q, heads, dh, points):
         check_msda(sds, "msda-tiled", n, shapes, q, heads, dh, points, softmax=softmax, seed=47, offset_std=3.0)
 
 
+MID_SHAPES = [(64, 80), (32, 40), (16, 20), (8, 10)]   # S = 6800
+
+
+@pytest.mark.parametrize("q,dh,points,softmax,ref", [
+    (6800, 32, 4, True, "cells"),      # the encoder recipe at a third of its cells
+    (6000, 32, 4, False, "uniform"),   # a ragged last tile, raw weights, random locations
+    (3400, 64, 2, True, "uniform"),    # 16 lanes per query
+    (6800, 16, 4, True, "cells"),      # 4 lanes per query
+])
+def test_msda_mid_size(sds, q, dh, points, softmax, ref):
+    """Mid-size MSDA (2 images, 8 heads, thousands of queries over 4 levels):
+    many tiles per (image, head) pair, every tile kind of the tiled kernel."""
+    check_msda(sds, "msda-mid", 2, MID_SHAPES, q, 8, dh, points, softmax=softmax, seed=43, ref=ref)
+
+
 @pytest.mark.parametrize("shapes,points", [([(1, 1)], 1), ([(5, 3)], 8), ([(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 2)])
 def test_msda_levels_points(sds, shapes, points):
     for softmax in (True, False):
