@@ -298,8 +298,9 @@ hipError_t launch_dcn_forward(const Geom& G, int dtype, const void* x, const voi
     device_limits(&lds_limit, &num_cus);
     // The LDS sliding-window kernel where it applies, else the direct gathers.
     RingCfg rr;
-    if (plan_ring(G, dtype, x, off, mask, out, lds_limit, num_cus, &rr))
-        return launch_dcn_forward_ring(G, rr, dtype, x, off, mask, out, s);
+    Geom gk;
+    if (plan_ring(G, dtype, x, off, mask, out, lds_limit, num_cus, &rr, &gk))
+        return launch_dcn_forward_ring(gk, rr, dtype, x, off, mask, out, s);
     switch (dtype * 2 + (G.softmax ? 1 : 0)) {
         case DT_F32 * 2 + 0: return launch_typed<DT_F32, false>(G, x, off, mask, out, s);
         case DT_F32 * 2 + 1: return launch_typed<DT_F32, true>(G, x, off, mask, out, s);

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     auto load_offsets = [&](int s) {
         const int rr = r_begin + s * rc.tr + rl;
         const bool v = rl < rc.tr && rr < r_end;
-        const uint32_t item = ((uint32_t)(n * G.ho + rr) * G.wo + c) * G.g + g;
+        const uint32_t item = ((uint32_t)(n * G.ho + rr) * G.wo + c) * (G.g >> rc.split_log) + (g >> rc.split_log);
         const uint32_t ob = v ? item * K2B : OOB;
         const uint32_t mb = v ? (item * KMB) & ~3u : OOB;
         psh = ((item * KMB) & 3u) * 8u;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             // staging area has been released) rather than indexed in registers.
             if (fb) {
                 const uint32_t base_img = n * img_bytes + (uint32_t)g * gsize;
-                const uint32_t item = ((uint32_t)(n * G.ho + r) * G.wo + c) * G.g + g;
+                const uint32_t item = ((uint32_t)(n * G.ho + r) * G.wo + c) * (G.g >> rc.split_log) + (g >> rc.split_log);
                 while (fb) {
                     const int k = __builtin_ctz(fb);
                     fb &= fb - 1u;
@@ -493,17 +493,34 @@ hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, 
 
 // Choose the group set, rows per step, halo and chunking for geometry G, or
 // return false when the sliding-window kernel does not apply.
-bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
-               int lds_limit, int num_cus, RingCfg* rc)
+bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const void* mask, const void* out,
+               int lds_limit, int num_cus, RingCfg* rc, Geom* gk)
 {
-    if (G.kh != 3 || G.kw != 3) return false;
+    if (G0.kh != 3 || G0.kw != 3) return false;
     const int es = dtype == DT_F32 ? 4 : 2;
-    const int nch = G.d * es / 16;
-    if (G.d * es % 16 != 0 || (nch != 1 && nch != 2 && nch != 4)) return false;
+    if (G0.d * es % 16 != 0) return false;
     if ((uintptr_t)x % 16 || (uintptr_t)off % 16 || (uintptr_t)mask % 16 || (uintptr_t)out % 16) return false;
-    const long x_bytes = (long)G.n * G.h * G.w * G.c * es;
-    const long off_bytes = (long)G.items * G.K * 2 * es, mask_bytes = (long)G.items * G.K * es;
+    const long x_bytes = (long)G0.n * G0.h * G0.w * G0.c * es;
+    const long off_bytes = (long)G0.items * G0.K * 2 * es, mask_bytes = (long)G0.items * G0.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
+    // A group wider than 64 bytes per pixel (f32 with D > 16, f16/bf16 with
+    // D > 32) runs as 2^split_log groups of 64 bytes, each lane item with its
+    // own share of the channels and the group's offsets and mask: the tap
+    // geometry is then computed once per 64 bytes, but a lane's sums and
+    // corner data stay within the registers of the 4-chunk kernel.
+    const int lane_bytes = 64;
+    int split_log = 0;
+    while ((G0.d * es >> split_log) > lane_bytes) ++split_log;
+    if (split_log > 0 && (G0.d % (1 << split_log) != 0 || (G0.d >> split_log) * es != lane_bytes)) return false;
+    Geom G = G0;
+    G.g = G0.g << split_log;
+    G.d = G0.d >> split_log;
+    G.items = G0.items << split_log;
+    if ((long)G0.items << split_log >= (1L << 31)) return false;
+    const int nch = G.d * es / 16;
+    if (nch != 1 && nch != 2 && nch != 4) return false;
+    *gk = G;
+    rc->split_log = split_log;
 
     // For a target number of items per step, try group sets from all groups
     // down; take the first that keeps a halo of at least HY_MIN rows in LDS

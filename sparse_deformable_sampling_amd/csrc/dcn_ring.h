@@ -26,11 +26,15 @@ struct RingCfg {
     int ring_bytes;   // (R + 1) * pitch
     int lds_bytes;    // the ring (each lane loads its offsets and mask into registers)
     uint32_t x_bytes, off_bytes, mask_bytes;   // buffer extents, rounded up to whole dwords
+    int split_log;    // log2 of the lane items per channel group: a wide group (more than 64 bytes
+                      // per pixel) runs as 2^split_log groups of its channels sharing its offsets and mask
 };
 
-// Fill `rc` for geometry G; false if the sliding-window kernel does not apply.
+// Fill `rc` for geometry G, and `gk` with the geometry the kernel runs on (G,
+// or G with each wide group split into narrower ones); false if the
+// sliding-window kernel does not apply.
 bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const void* mask, const void* out,
-               int lds_limit, int num_cus, RingCfg* rc);
+               int lds_limit, int num_cus, RingCfg* rc, Geom* gk);
 
 hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
                                    const void* mask, void* out, hipStream_t s);

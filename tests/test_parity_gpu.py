@@ -58,6 +58,15 @@ def test_stage1_forward_full(sds, dtype, softmax):
     check_fwd(sds, "stage1", 64, 56, 56, 64, 4, dtype, softmax)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_table10_shape(sds, dtype, softmax):
+    """The pages' module shape 56x56x128, 4 groups of 32 channels (batch 16
+    of 64): f32 groups are 128 bytes per pixel and run as two 64-byte lane
+    items sharing the group's offsets and mask."""
+    check_fwd(sds, "table10", 16, 56, 56, 128, 4, dtype, softmax)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("stage", ["stage2", "stage3"])
 def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
