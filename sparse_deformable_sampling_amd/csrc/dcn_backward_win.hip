@@ -16,18 +16,20 @@
 // the chunk a few rows per step, and keeps a window of grad_x rows of its
 // group in LDS as 64-bit fixed-point sums:
 //  - a contribution v to a cell whose row is in the window is added as
-//    round-down(v * 2^e) with ds_add_u64; its row leaves the window once no
+//    trunc(v * 2^e), sign-extended to 64 bits, with ds_add_u64; its row leaves the window once no
 //    later output row of the chunk can reach it through LDS, and is then
 //    converted back to fp32 and added to grad_x with one fp32 atomic per
 //    element (neighbouring chunks share halo rows);
 //  - a contribution to a row outside the window (an offset beyond the halo)
 //    goes to grad_x with an fp32 atomic directly.
-// The scale 2^e is chosen per workgroup from the bound S = sum over its items
-// of (sum_k |m_k|) * max_c |g_c|, which no cell's sum can exceed: e makes
-// S * 2^e < 2^61, so the 64-bit sums cannot overflow and resolve 2^-61 of S.
-// Non-finite inputs, or an S outside [2^-60, 2^60), turn the fixed-point path
-// off for that workgroup (every contribution then takes the fp32 atomic).
-// Integer sums do not depend on the order of the additions.
+// The scale 2^e is chosen per workgroup from the bound B = max over its items
+// of max_k |m_k| * max_c |g_c|, which no single contribution m_k w g_c (w <= 1)
+// can exceed: e makes B * 2^e < 2^30, so one contribution is one 32-bit
+// integer (a single conversion), resolving 2^-30 of B, and a cell's 64-bit
+// sum of fewer than 2^32 of them cannot overflow.  Non-finite inputs, or a B
+// outside [2^-60, 2^60), turn the fixed-point path off for that workgroup
+// (every contribution then takes the fp32 atomic).  Integer sums do not
+// depend on the order of the additions.
 // With f16/bf16 storage the inputs are widened to fp32 as they are read,
 // grad_offset and grad_mask are rounded once (to nearest even) as they are
 // stored, and grad_x is summed into an fp32 buffer that the caller converts.
@@ -49,13 +51,11 @@ __device__ __forceinline__ float lane_sum(float v, int width)
     return v;
 }
 
-// Fixed-point image of t (|t| < 2^31): floor(t * 2^32) as a two's-complement
-// 64-bit integer.
+// Fixed-point image of t (|t| < 2^31): t truncated to an integer, as a
+// two's-complement 64-bit integer.
 __device__ __forceinline__ unsigned long long to_fixed(float t)
 {
-    const uint32_t hi = (uint32_t)(int)floorf(t);
-    const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(t) * 4294967296.0f);   // fract < 1 - 2^-24
-    return ((unsigned long long)hi << 32) | lo;
+    return (unsigned long long)(long long)(int)t;
 }
 
 // Widen N consecutive storage-type values (N * sizeof(T) a multiple of 8
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
     const int lq = 1 << bc.lq_log;
     const int li = tid >> bc.lq_log, c4 = tid & (lq - 1);
 
-    // ---- the bound S of this workgroup, and whether every input is finite
+    // ---- the bound B of this workgroup, and whether every input is finite
     float part = 0.f;
     int bad = 0;
     // Same lane layout as the main pass: lane (item, chunk) reads its CPL
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
         float ms = 0.f;
         for (int k = c4; k < K; k += lq) {
             const float v = to_f32(mask[item * K + k]);
-            ms += fabsf(v);
+            ms = fmaxf(ms, fabsf(v));
             bad |= !(fabsf(v) <= 3.0e38f);
         }
         float gm = 0.f;
@@ -184,29 +184,31 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                 bad |= !(fabsf(a[j]) <= 3.0e38f);
             }
         }
-        ms = lane_sum(ms, lq);
-        for (int o = 1; o < lq; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+        for (int o = 1; o < lq; o <<= 1) {
+            ms = fmaxf(ms, __shfl_xor(ms, o, 64));
+            gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+        }
         if (SOFTMAX) ms = 1.f;
-        if (c4 == 0) part += ms * gm;
+        part = fmaxf(part, ms * gm);
     }
-    part = lane_sum(part, 64);
+    for (int o = 1; o < 64; o <<= 1) part = fmaxf(part, __shfl_xor(part, o, 64));
     for (int o = 1; o < 64; o <<= 1) bad |= __shfl_xor(bad, o, 64);
     if ((tid & 63) == 0) {
         red_s[tid >> 6] = part;
         red_bad[tid >> 6] = bad;
     }
     __syncthreads();
-    float S = 0.f;
+    float B = 0.f;
     bad = 0;
     for (int w = 0; w < (nthr + 63) / 64; ++w) {
-        S += red_s[w];
+        B = fmaxf(B, red_s[w]);
         bad |= red_bad[w];
     }
-    const bool fixed = !bad && S >= 0x1p-60f && S < 0x1p60f;
+    const bool fixed = !bad && B >= 0x1p-60f && B < 0x1p60f;
     int ex = 0;
-    if (fixed) (void)frexpf(S, &ex);        // S < 2^ex
-    const int e = 61 - ex;                   // S * 2^e < 2^61
-    const float tscale = ldexpf(1.f, e - 32);
+    if (fixed) (void)frexpf(B, &ex);        // B < 2^ex
+    const int e = 30 - ex;                   // B * 2^e < 2^30: rounding of the products cannot reach 2^31
+    const float tscale = ldexpf(1.f, e);
     const float s_hi = ldexpf(1.f, 32 - e), s_lo = ldexpf(1.f, -e);
 
     for (int i = tid; i < bc.aw * rowe; i += nthr) acc[i] = 0ull;

@@ -26,7 +26,9 @@
 //     the lanes that need it.
 // Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
-// accumulation; 16-byte vector stores, one writer per output element.
+// accumulation; 16-byte vector stores, one writer per output element.  A
+// group wider than 64 bytes per pixel runs as several 64-byte items that
+// share the group's offsets and mask (the plan's split_log).
 // WMAX is the workgroup's wave count bound: 16 (four waves per SIMD, <=128
 // VGPRs) where a corner is at most 32 bytes, the next tap's geometry then
 // being computed while its reads land; 8 otherwise, with the geometry of all
@@ -385,8 +387,9 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             // Tail: samples outside the window that may touch the image, read
             // from global memory.  Each lane walks only its own such taps, so a
             // wave runs as many iterations as its busiest lane; the tap's
-            // offsets and modulation are read again from global memory (the
-            // staging area has been released) rather than indexed in registers.
+            // offsets and modulation are read again from global memory rather
+            // than indexed in registers (a dynamic index into the prefetched
+            // registers would move them to scratch).
             if (fb) {
                 const uint32_t base_img = n * img_bytes + (uint32_t)g * gsize;
                 const uint32_t item = ((uint32_t)(n * G.ho + r) * G.wo + c) * (G.g >> rc.split_log) + (g >> rc.split_log);
