@@ -16,7 +16,7 @@
 // the chunk a few rows per step, and keeps a window of grad_x rows of its
 // group in LDS as 64-bit fixed-point sums:
 //  - a contribution v to a cell whose row is in the window is added as
-//    trunc(v * 2^e), sign-extended to 64 bits, with ds_add_u64; its row leaves the window once no
+//    round(v * 2^e), sign-extended to 64 bits, with ds_add_u64; its row leaves the window once no
 //    later output row of the chunk can reach it through LDS, and is then
 //    converted back to fp32 and added to grad_x with one fp32 atomic per
 //    element (neighbouring chunks share halo rows);
@@ -51,11 +51,11 @@ __device__ __forceinline__ float lane_sum(float v, int width)
     return v;
 }
 
-// Fixed-point image of t (|t| < 2^31): t truncated to an integer, as a
-// two's-complement 64-bit integer.
+// Fixed-point image of t (|t| < 2^31): t rounded to the nearest integer, as
+// a two's-complement 64-bit integer.
 __device__ __forceinline__ unsigned long long to_fixed(float t)
 {
-    return (unsigned long long)(long long)(int)t;
+    return (unsigned long long)(long long)(int)__builtin_rintf(t);
 }
 
 // Widen N consecutive storage-type values (N * sizeof(T) a multiple of 8
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
     if (fixed) (void)frexpf(B, &ex);        // B < 2^ex
     const int e = 30 - ex;                   // B * 2^e < 2^30: rounding of the products cannot reach 2^31
     const float tscale = ldexpf(1.f, e);
-    const float s_hi = ldexpf(1.f, 32 - e), s_lo = ldexpf(1.f, -e);
+    const double s_fix = ldexp(1.0, -e);    // value of one fixed-point unit
 
     for (int i = tid; i < bc.aw * rowe; i += nthr) acc[i] = 0ull;
     __syncthreads();
@@ -268,12 +268,16 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                 float sm = 0.f, sdx = 0.f, sdy = 0.f;
                 const float wa = 1.f - a, wb = 1.f - b;
                 const float w4[4] = {wa * wb, a * wb, wa * b, a * b};
+                // Per channel, as interpolations: top/bottom rows at a, then b;
+                // dv/da = t0 + b (t1 - t0) and dv/db = bottom - top.
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
-                    const float v = w4[0] * X00[j] + w4[1] * X01[j] + w4[2] * X10[j] + w4[3] * X11[j];
-                    sm = fmaf(gc[j], v, sm);
-                    sdx = fmaf(gc[j], wb * (X01[j] - X00[j]) + b * (X11[j] - X10[j]), sdx);
-                    sdy = fmaf(gc[j], wa * (X10[j] - X00[j]) + a * (X11[j] - X01[j]), sdy);
+                    const float t0 = X01[j] - X00[j], t1 = X11[j] - X10[j];
+                    const float top = fmaf(a, t0, X00[j]), bot = fmaf(a, t1, X10[j]);
+                    const float dvdb = bot - top;
+                    sm = fmaf(gc[j], fmaf(b, dvdb, top), sm);
+                    sdx = fmaf(gc[j], fmaf(b, t1 - t0, t0), sdx);
+                    sdy = fmaf(gc[j], dvdb, sdy);
                 }
                 if (gx) {
 #pragma unroll
@@ -416,7 +420,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                     const unsigned long long q = arow[xc * pstr + c];
                     if (q != 0ull) {
                         arow[xc * pstr + c] = 0ull;
-                        const float v = (float)(int)(uint32_t)(q >> 32) * s_hi + (float)(uint32_t)q * s_lo;
+                        // the 64-bit sum to fp64 (exact below 2^53 units, one rounding
+                        // above), scaled exactly, rounded once to fp32
+                        const float v = (float)((double)(long long)q * s_fix);
                         atomicAdd(grow + (long)xc * C + c, v);
                     }
                 }
