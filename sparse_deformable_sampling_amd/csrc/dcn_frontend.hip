@@ -293,6 +293,7 @@ struct WaveCfg {
     int nw;          // waves per workgroup (4 or 8, chosen at launch)
     int nwg;         // workgroups, a multiple of 8 (chosen at launch)
     int bias_off;    // LDS byte offsets: Bt at 0, bias (fp32), wave slices
+    int dw_off;      // bf16 only: depthwise weights [9][KP] and bias [KP] as fp32
     int w_off, w_bytes;  // wave slices: A [16][AST], then the output image in the same bytes
     int lds_bytes;   // w_off + nw * w_bytes
     uint32_t x_bytes;
@@ -359,6 +360,15 @@ __global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, c
             *reinterpret_cast<uint4*>(Bt + j * AST + k8) = v;
         }
         for (int j = tid; j < NO; j += nthr) bsw[j] = to_f32(omb[j]);
+        if constexpr (DT == DT_BF16) {
+            // bf16 has no mixed-precision multiply-add: the depthwise weights and
+            // bias are widened once here instead of at every use
+            float* dwf = reinterpret_cast<float*>(lds + F.dw_off);
+            for (int e = tid; e < 10 * KP; e += nthr) {
+                const int t = e / KP, c = e - t * KP;
+                dwf[e] = c >= C ? 0.f : to_f32(t < 9 ? dww[t * C + c] : dwb[c]);
+            }
+        }
     }
     __syncthreads();
 
@@ -371,9 +381,13 @@ __global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, c
     const int cc = (lane % C8) * 8;
     const bool live = cc < C;
     u32x4 wr[9], br = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (DT != DT_BF16) {
 #pragma unroll
-    for (int t = 0; t < 9; ++t) wr[t] = live ? *reinterpret_cast<const u32x4*>(dww + t * C + cc) : u32x4{0u, 0u, 0u, 0u};
-    if (live) br = *reinterpret_cast<const u32x4*>(dwb + cc);
+        for (int t = 0; t < 9; ++t)
+            wr[t] = live ? *reinterpret_cast<const u32x4*>(dww + t * C + cc) : u32x4{0u, 0u, 0u, 0u};
+        if (live) br = *reinterpret_cast<const u32x4*>(dwb + cc);
+    }
+    const float* dwf = reinterpret_cast<const float*>(lds + F.dw_off) + cc;   // bf16: [t][KP], bias at t = 9
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)F.x_bytes, 0x00020000);
     const uint32_t colB = (uint32_t)C * 2u, rowB = (uint32_t)W * colB;
@@ -399,9 +413,11 @@ __global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, c
             if (p0 >= npx) continue;
             // keep the weights packed from run to run: their widening stays at
             // the point of use instead of being hoisted into 72 live registers
+            if constexpr (DT != DT_BF16) {
 #pragma unroll
-            for (int t = 0; t < 9; ++t) asm volatile("" : "+v"(wr[t].x), "+v"(wr[t].y), "+v"(wr[t].z), "+v"(wr[t].w));
-            asm volatile("" : "+v"(br.x), "+v"(br.y), "+v"(br.z), "+v"(br.w));
+                for (int t = 0; t < 9; ++t) asm volatile("" : "+v"(wr[t].x), "+v"(wr[t].y), "+v"(wr[t].z), "+v"(wr[t].w));
+                asm volatile("" : "+v"(br.x), "+v"(br.y), "+v"(br.z), "+v"(br.w));
+            }
             float acc[R][8];
             if (live) {
                 const uint32_t pix0 = (uint32_t)(px0 + p0);
@@ -419,13 +435,39 @@ __global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, c
                             ok ? base + (uint32_t)(i - 1) * rowB + (uint32_t)(j - 1) * colB : 0x80000000u;
                         X[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
                     }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    widen8<DT>(br, acc[r]);
+                if constexpr (DT == DT_BF16) {
+                    float xv[3][R + 2][8];
 #pragma unroll
                     for (int i = 0; i < 3; ++i)
 #pragma unroll
-                        for (int j = 0; j < 3; ++j) fma8<DT>(wr[i * 3 + j], X[i][r + j], acc[r]);
+                        for (int j = 0; j < R + 2; ++j) widen8<DT>(X[i][j], xv[i][j]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float4 b0 = *reinterpret_cast<const float4*>(dwf + 9 * KP);
+                        const float4 b1 = *reinterpret_cast<const float4*>(dwf + 9 * KP + 4);
+                        acc[r][0] = b0.x; acc[r][1] = b0.y; acc[r][2] = b0.z; acc[r][3] = b0.w;
+                        acc[r][4] = b1.x; acc[r][5] = b1.y; acc[r][6] = b1.z; acc[r][7] = b1.w;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 9; ++t) {
+                        const int i = t / 3, j = t % 3;
+                        const float4 w0 = *reinterpret_cast<const float4*>(dwf + t * KP);
+                        const float4 w1 = *reinterpret_cast<const float4*>(dwf + t * KP + 4);
+                        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) acc[r][u] = fmaf(wv[u], xv[i][r + j][u], acc[r][u]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        widen8<DT>(br, acc[r]);
+#pragma unroll
+                        for (int i = 0; i < 3; ++i)
+#pragma unroll
+                            for (int j = 0; j < 3; ++j) fma8<DT>(wr[i * 3 + j], X[i][r + j], acc[r]);
+                    }
                 }
             } else {
 #pragma unroll
@@ -522,8 +564,10 @@ template <int DT>
 hipError_t launch_wave(const Geom& G, const WaveCfg& F, int c8, const void* x, const void* dww, const void* dwb,
                        const void* omw, const void* omb, void* off, void* mask, hipStream_t s)
 {
-    // runs of two pixels need an even width
-    const bool r2 = G.w % 2 == 0;
+    // Runs of two pixels need an even width.  bf16 keeps its whole widened
+    // 3x4 window live (96 registers); from 128 channels on one-pixel runs
+    // leave room for more waves (Table 10 shape: 55 -> 46 us).
+    const bool r2 = G.w % 2 == 0 && !(DT == DT_BF16 && c8 >= 16);
 #define DCN_FE_CASE(N)                                                                          \
     case N:                                                                                     \
         return r2 ? launch_wave_c8<DT, N, 2>(G, F, x, dww, dwb, omw, omb, off, mask, s)        \
@@ -556,7 +600,8 @@ bool plan_wave(const Geom& G, int dtype, int lds_limit, int num_cus, WaveCfg* F,
     F->nblk = (F->npix + 15) / 16;
     const int b_bytes = F->ncb * 16 * F->AST * 2;
     F->bias_off = b_bytes;
-    F->w_off = (b_bytes + F->NO * 4 + 15) / 16 * 16;
+    F->dw_off = (b_bytes + F->NO * 4 + 15) / 16 * 16;
+    F->w_off = F->dw_off + (dtype == DT_BF16 ? 10 * KP * 4 : 0);
     F->w_bytes = std::max(16 * F->AST * 2, 48 * F->NOFF);
     // workgroup size and count are set at launch from the kernel's occupancy
     F->nw = 4;
