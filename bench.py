@@ -265,7 +265,9 @@ def msda_ref_runner(torch, seed=1):
     return r
 
 
-def msda_bwd_runner(torch, seed=1):
+def msda_bwd_runner(torch, gather=True, seed=1):
+    """gather=True: grad_value gathered per cell through one workspace shared by
+    all launches (they run in order on one stream); False: atomic scatter."""
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, q, heads, dh, pts = 8, 17821, 8, 32, 4
     d = synth.msda_inputs(n, MSDA_SHAPES, q, heads, dh, pts, seed=seed, ref="cells")
@@ -277,14 +279,22 @@ def msda_bwd_runner(torch, seed=1):
     base = [upload(torch, a, "f32") for a in (d["value"], d["loc"], d["attn"], g)]
     stream = torch.cuda.current_stream()
     args, keep = [], []
+    ws_args = ()
+    if gather:
+        nb = ctypes.c_size_t(0)
+        B.check(B.lib().msda_backward_workspace_size(ctypes.byref(desc), shapes, ctypes.byref(nb)))
+        ws = torch.empty((nb.value,), dtype=torch.uint8, device="cuda")
+        keep.append(ws)
+        ws_args = (ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nb.value))
     for i in range(n_sets(min_bytes)):
         ins = [t.clone() for t in base] if i else base
         outs = [torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])]
         keep += ins + outs
         args.append((ctypes.byref(desc), shapes) + tuple(ctypes.c_void_p(t.data_ptr()) for t in ins + outs) +
-                    (ctypes.c_void_p(stream.cuda_stream),))
-    r = Runner("msda_bwd_encoder_f32", args, B.lib().msda_backward, n * q * heads * dh * len(MSDA_SHAPES) * pts,
-               min_bytes, stream)
+                    ws_args + (ctypes.c_void_p(stream.cuda_stream),))
+    r = Runner("msda_bwd_encoder_f32" if gather else "msda_bwd_atomic_encoder_f32", args,
+               B.lib().msda_backward_ws if gather else B.lib().msda_backward,
+               n * q * heads * dh * len(MSDA_SHAPES) * pts, min_bytes, stream)
     r.keep = keep
     return r
 
@@ -458,7 +468,7 @@ def main():
             parts = name.split("_")   # dcnv4_module_table10_f16
             r = module_runner(torch, parts[2], parts[3])
         elif name.startswith("msda_bwd"):
-            r = msda_bwd_runner(torch)
+            r = msda_bwd_runner(torch, gather="atomic" not in name)
         elif name.startswith("msda_fwd_ref"):
             r = msda_ref_runner(torch)
         elif name.startswith("msda"):
@@ -517,7 +527,7 @@ def main():
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
         r = msda_bwd_runner(torch)
-        secondary[r.name] = summarize(r, time_steps(torch, r, 10, 2), kernel_ms(torch, r, 10))
+        secondary[r.name] = summarize(r, time_steps(torch, r, 20, 3), kernel_ms(torch, r, 20))
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
         torch.cuda.empty_cache()

@@ -206,6 +206,35 @@ dcn_status msda_backward(const msda_desc* desc, const int32_t* spatial_shapes, c
                          const void* loc, const void* attn, const void* grad_out, void* grad_value,
                          void* grad_loc, void* grad_attn, void* stream);
 
+/* Bytes of device workspace msda_backward_ws needs for grad_value to be
+ * gathered per value cell rather than scattered with atomics (same gradients;
+ * "Deformable DETR: Learn Where to Read", "A learned location can fall between
+ * cells": a cell's value gradient is the sum, over the samples it is a corner
+ * of, of the corner weight times the attention weight times grad_out).  0
+ * when the shape has no gather path (head_dim not a power of two in 4..64,
+ * levels*points not a power of two up to 32, grad_out of 2 GiB or more) or
+ * desc->dtype is not f32.  At the Deformable DETR encoder shape (n=8,
+ * S=len_q=17821, 8 heads, 4 levels x 4 points) it is about 370 MB: 20 bytes
+ * per sample plus 4 bytes per cell of a (H_l+1) x (W_l+1) grid per level,
+ * image and head. */
+dcn_status msda_backward_workspace_size(const msda_desc* desc, const int32_t* spatial_shapes, size_t* bytes);
+
+/* msda_backward with a caller-owned device workspace (256-byte aligned, at
+ * least msda_backward_workspace_size bytes when grad_value is requested and
+ * that size is nonzero; otherwise it may be NULL and is not used).  With a
+ * workspace, grad_value is written once per cell, without atomics and without
+ * a zero-fill; the order in which a cell's contributions are summed still
+ * depends on the order of the counting atomics, so its low bits may differ
+ * from run to run.  A missing or short workspace is DCN_ERR_INVALID, a
+ * misaligned one DCN_ERR_UNSUPPORTED.  grad_value or grad_out that is not
+ * 16-byte aligned (or a loc / grad_loc that is not 8-byte aligned) takes the
+ * atomic scatter instead.  Calls that share a workspace must not overlap in
+ * time.  Everything else is as msda_backward. */
+dcn_status msda_backward_ws(const msda_desc* desc, const int32_t* spatial_shapes, const void* value,
+                            const void* loc, const void* attn, const void* grad_out, void* grad_value,
+                            void* grad_loc, void* grad_attn, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static name of a status code. */
 const char* dcn_status_str(dcn_status status);
 

@@ -199,9 +199,12 @@ def msda_forward_ref(value, spatial_shapes, reference, offsets, attn, valid_rati
 
 
 def msda_backward(value, spatial_shapes, loc, attn, grad_out, softmax=True, need_value=True, need_loc=True,
-                  need_attn=True):
+                  need_attn=True, gather=True):
     """Gradients (grad_value, grad_loc, grad_attn) of msda_forward; a
-    gradient that is not needed comes back as None and is not computed."""
+    gradient that is not needed comes back as None and is not computed.
+    gather=True: grad_value is gathered per value cell through a device
+    workspace allocated here (no atomics into grad_value); gather=False: it is
+    scattered with fp32 atomics."""
     dev = _check_tensors(value, loc, attn, grad_out)
     n, S, M, Dh = value.shape
     if loc.dim() != 6 or loc.shape[-1] != 2:
@@ -218,6 +221,14 @@ def msda_backward(value, spatial_shapes, loc, attn, grad_out, softmax=True, need
     gv = torch.empty_like(value) if need_value else None
     gl = torch.empty_like(loc) if need_loc else None
     ga = torch.empty_like(attn) if need_attn else None
-    _b.check(_b.lib().msda_backward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn), _ptr(grad_out),
-                                    _ptr(gv), _ptr(gl), _ptr(ga), _stream(dev)))
+    if not gather:
+        _b.check(_b.lib().msda_backward(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn),
+                                        _ptr(grad_out), _ptr(gv), _ptr(gl), _ptr(ga), _stream(dev)))
+        return gv, gl, ga
+    nbytes = ctypes.c_size_t(0)
+    _b.check(_b.lib().msda_backward_workspace_size(ctypes.byref(desc), shapes, ctypes.byref(nbytes)))
+    ws = torch.empty((nbytes.value,), dtype=torch.uint8, device=dev) if (need_value and nbytes.value) else None
+    _b.check(_b.lib().msda_backward_ws(ctypes.byref(desc), shapes, _ptr(value), _ptr(loc), _ptr(attn),
+                                       _ptr(grad_out), _ptr(gv), _ptr(gl), _ptr(ga), _ptr(ws),
+                                       nbytes.value if ws is not None else 0, _stream(dev)))
     return gv, gl, ga

@@ -31,7 +31,8 @@ class MsdaDesc(ctypes.Structure):
 
 EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "dcn_backward_workspace_size", "dcn_backward_ws",
            "dcn_offset_mask",
-           "msda_forward", "msda_forward_ref", "msda_backward", "dcn_status_str", "dcn_last_error")
+           "msda_forward", "msda_forward_ref", "msda_backward", "msda_backward_workspace_size", "msda_backward_ws",
+           "dcn_status_str", "dcn_last_error")
 
 _lib = None
 
@@ -67,6 +68,12 @@ def lib():
     L.msda_backward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
                                 vp]
     L.msda_backward.restype = ctypes.c_int
+    L.msda_backward_workspace_size.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    L.msda_backward_workspace_size.restype = ctypes.c_int
+    L.msda_backward_ws.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp, vp,
+                                   vp, vp, ctypes.c_size_t, vp]
+    L.msda_backward_ws.restype = ctypes.c_int
     L.dcn_status_str.argtypes = [ctypes.c_int]
     L.dcn_status_str.restype = ctypes.c_char_p
     L.dcn_last_error.argtypes = []

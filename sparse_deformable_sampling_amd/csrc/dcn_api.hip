@@ -285,9 +285,10 @@ dcn_status msda_forward_ref(const msda_desc* d, const int32_t* shapes, int32_t r
                                                    (hipStream_t)stream));
 }
 
-dcn_status msda_backward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
-                         const void* attn, const void* grad_out, void* grad_value, void* grad_loc, void* grad_attn,
-                         void* stream)
+static dcn_status msda_backward_impl(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                                     const void* attn, const void* grad_out, void* grad_value, void* grad_loc,
+                                     void* grad_attn, void* workspace, size_t workspace_bytes, bool with_ws,
+                                     void* stream)
 {
     dcn::MsdaGeom G;
     dcn_status st = msda_geom(d, shapes, G);
@@ -301,10 +302,48 @@ dcn_status msda_backward(const msda_desc* d, const int32_t* shapes, const void* 
     if (grad_value && (st = check_ptr(grad_value, "grad_value", 4))) return st;
     if (grad_loc && (st = check_ptr(grad_loc, "grad_loc", 4))) return st;
     if (grad_attn && (st = check_ptr(grad_attn, "grad_attn", 4))) return st;
+    size_t need = 0;
+    if (with_ws && grad_value) {
+        need = dcn::msda_backward_workspace(G);
+        if (need) {
+            if (!workspace)
+                return fail(DCN_ERR_INVALID, "msda_backward_ws with grad_value needs a workspace of %zu bytes", need);
+            if (workspace_bytes < need)
+                return fail(DCN_ERR_INVALID, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+            if ((uintptr_t)workspace % 256) return fail(DCN_ERR_UNSUPPORTED, "workspace is not aligned to 256 bytes");
+        }
+    }
     if (!grad_value && !grad_loc && !grad_attn) return ok();
     return hip_status(dcn::launch_msda_backward(G, (const float*)value, (const float*)loc, (const float*)attn,
                                                 (const float*)grad_out, (float*)grad_value, (float*)grad_loc,
-                                                (float*)grad_attn, (hipStream_t)stream));
+                                                (float*)grad_attn, need ? workspace : nullptr, need,
+                                                (hipStream_t)stream));
+}
+
+dcn_status msda_backward(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                         const void* attn, const void* grad_out, void* grad_value, void* grad_loc, void* grad_attn,
+                         void* stream)
+{
+    return msda_backward_impl(d, shapes, value, loc, attn, grad_out, grad_value, grad_loc, grad_attn, nullptr, 0,
+                              false, stream);
+}
+
+dcn_status msda_backward_workspace_size(const msda_desc* d, const int32_t* shapes, size_t* bytes)
+{
+    if (!bytes) return fail(DCN_ERR_INVALID, "bytes is NULL");
+    dcn::MsdaGeom G;
+    dcn_status st = msda_geom(d, shapes, G);
+    if (st) return st;
+    *bytes = d->dtype == DCN_F32 ? dcn::msda_backward_workspace(G) : 0;
+    return ok();
+}
+
+dcn_status msda_backward_ws(const msda_desc* d, const int32_t* shapes, const void* value, const void* loc,
+                            const void* attn, const void* grad_out, void* grad_value, void* grad_loc, void* grad_attn,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    return msda_backward_impl(d, shapes, value, loc, attn, grad_out, grad_value, grad_loc, grad_attn, workspace,
+                              workspace_bytes, true, stream);
 }
 
 }  // extern "C"

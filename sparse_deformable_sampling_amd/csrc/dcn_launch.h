@@ -52,7 +52,12 @@ hipError_t launch_msda_forward(const MsdaGeom& g, const float* value, const floa
 hipError_t launch_msda_forward_ref(const MsdaGeom& g, int ref_dims, const float* value, const float* ref,
                                    const float* ratios, const float* offsets, const float* attn,
                                    const uint8_t* pad, float* out, hipStream_t s);
+// With a workspace of at least msda_backward_workspace(g) bytes (0: the shape
+// has no gather path), grad_value is gathered per cell; otherwise it is
+// zero-filled and scattered with atomics.
+size_t msda_backward_workspace(const MsdaGeom& g);
 hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const float* loc, const float* attn,
-                                const float* gout, float* gvalue, float* gloc, float* gattn, hipStream_t s);
+                                const float* gout, float* gvalue, float* gloc, float* gattn, void* ws,
+                                size_t ws_bytes, hipStream_t s);
 
 }  // namespace dcn

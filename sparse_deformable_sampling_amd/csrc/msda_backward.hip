@@ -17,18 +17,40 @@
 //  - Phase 1, one thread per sample: joint softmax, fp64 pixel coordinate,
 //    the four corners' byte offsets (past the end of the buffer for a corner
 //    outside the level) and (a, b, A) into LDS.
-//  - Phase 2, lane = (query, channel): for every sample, read the four corner
-//    values of this channel, scatter A*w*g into grad_value with buffer
-//    atomics (the head_dim lanes of a query add to one contiguous run, the
-//    access pattern fp32 atomics serve fastest; out-of-range corners are
-//    dropped by the buffer range check), and reduce the three channel sums
-//    across the query's lanes; the query's first lane writes (dL/du, dL/dv,
-//    A, dL/dA) back into the sample's LDS record.
+//  - Phase 2, lane = (query, 4 channels) (1 channel below head_dim 4): for
+//    every sample, read the four corners' 16-byte slices, scatter A*w*g into
+//    grad_value with buffer atomics (a query's lanes add to one contiguous
+//    run, the access pattern fp32 atomics serve fastest; out-of-range corners
+//    are dropped by the buffer range check), and reduce the three channel
+//    sums across the query's lanes with DPP moves; the query's first lane
+//    writes (dL/du, dL/dv, A, dL/dA) back into the sample's LDS record.
 //  - Phase 3, one thread per sample: softmax backward over the query's
 //    samples, coalesced stores of grad_loc and grad_attn.
+//
+// With a workspace, grad_value is a gather instead of a scatter.  The value
+// gradient of a cell is a sum over the samples whose four corners include it,
+// so the samples are first grouped by cell (a counting sort per (image, head)
+// pair) and each cell then reads its own samples and writes its gradient
+// once: no atomics and no zero-fill.
+//  - Bucket of a sample: the cell (x0, y0) = (floor x, floor y) of its corner
+//    with the smallest coordinates, on a grid of (H_l+1) x (W_l+1) per level
+//    (x0, y0 >= -1 for a sample inside the level's extended range).  Cell
+//    (x, y) is a corner of the samples of buckets x0 in {x-1, x}, y0 in
+//    {y-1, y}: two runs of two adjacent buckets, contiguous in bucket order.
+//  - msda_bwd_count: one thread per sample, atomic count per bucket; the
+//    returned count is the sample's rank within its bucket.
+//  - msda_bwd_scan: exclusive prefix sum of the counts, one workgroup per pair.
+//  - the tiled kernel writes each sample's record (query, A, a, b) at
+//    offset + rank, alongside grad_loc and grad_attn.
+//  - msda_bwd_cells: a group of head_dim/4 lanes per cell, 4 channels a lane;
+//    the group reads its two runs of records in batches (one record per lane,
+//    the corner weight formed by the lane that read it, broadcast through
+//    LDS) and the matching 16-byte slices of grad_out, and stores the sum.
+//    Coarse levels, whose cells have the longest runs, are dispatched first.
 #include <algorithm>
 
 #include "dcn_device.h"
+#include "dcn_ring.h"
 
 namespace dcn {
 
@@ -37,18 +59,84 @@ namespace {
 constexpr uint32_t MS_OOB = 0x80000000u;
 constexpr int MS_REC_MAX = 1024;
 
+// Buckets of the value-gradient gather (see above).
+struct MsdaSortCfg {
+    int Sp;                                // buckets per pair: sum of (H_l+1)(W_l+1); offsets hold Sp+1
+    int pstart[MSDA_MAX_LEVELS];           // first bucket of level l within a pair
+    int wg_per_pair[MSDA_MAX_LEVELS];      // cell-kernel workgroups per pair at level l
+    int gpc[MSDA_MAX_LEVELS];              // lane groups per cell at level l (a power of two)
+    int blk_start[MSDA_MAX_LEVELS + 1];    // first cell-kernel workgroup of the k-th level taken (coarsest
+                                           // first), each a multiple of 8; the last is the grid size
+};
+
+// Pixel coordinate of a sample on a level of W x H cells (cell centres at
+// integers, formed in fp64), its top-left corner (x0, y0) and fractions.
+// False when no corner lies inside the level.
+__device__ __forceinline__ bool msda_corner(float2 uv, int Wl, int Hl, int& x0, int& y0, float& fa, float& fb)
+{
+    const double x = (double)uv.x * Wl - 0.5, y = (double)uv.y * Hl - 0.5;
+    if (!(x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl)) return false;
+    const double fx = floor(x), fy = floor(y);
+    fa = (float)(x - fx);
+    fb = (float)(y - fy);
+    x0 = (int)fx;
+    y0 = (int)fy;
+    return true;
+}
+
+// Make this wave's LDS writes visible to its own later LDS reads.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ float lane_sum(float v, int width)
 {
     for (int o = 1; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
-template <bool SOFTMAX>
+// Sum over aligned groups of `w` lanes (a power of two up to 64): DPP moves
+// within a row of 16 (swap neighbours, then pairs, then mirror within 8 and
+// within 16 lanes), cross-lane shuffles beyond; every lane of a group ends
+// with the group's sum.
+__device__ __forceinline__ float row_sum(float v, int w)
+{
+    if (w >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+    if (w >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+    if (w >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+    if (w >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)); // row mirror
+    if (w >= 32) v += __shfl_xor(v, 16, 64);
+    if (w >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// V consecutive fp32 values at byte offset o (zeros past the buffer's end).
+template <int V>
+__device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, uint32_t o, float* v)
+{
+    if constexpr (V == 4) {
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    } else {
+        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+    }
+}
+
+// SORTED: write each sample's record for the gather (records, offsets and
+// ranks as described above) instead of adding into grad_value.
+// V channels per lane in phase 2: 4 for the gather (head_dim >= 4), else 1,
+// so that each atomic instruction covers a query's whole run of channels.
+template <bool SOFTMAX, bool SORTED, int V>
 __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int Dlog, int QT, int tiles, int nwg,
                                                      uint32_t value_bytes, const float* __restrict__ value,
                                                      const float* __restrict__ loc, const float* __restrict__ attn,
                                                      const float* __restrict__ gout, float* __restrict__ gvalue,
-                                                     float* __restrict__ gloc, float* __restrict__ gattn)
+                                                     float* __restrict__ gloc, float* __restrict__ gattn,
+                                                     MsdaSortCfg C, const int* __restrict__ boff,
+                                                     const int* __restrict__ rank, int4* __restrict__ rec)
 {
     __shared__ u32x4 rec_o[MS_REC_MAX];
     __shared__ float4 rec_f[MS_REC_MAX];
@@ -84,12 +172,14 @@ __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int 
         const int Hl = G.H[l], Wl = G.W[l];
         u32x4 o = {MS_OOB, MS_OOB, MS_OOB, MS_OOB};
         float fa = 0.f, fb = 0.f;
-        const double x = (double)uv.x * Wl - 0.5, y = (double)uv.y * Hl - 0.5;
-        if (valid && x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl) {
-            const double fx = floor(x), fy = floor(y);
-            fa = (float)(x - fx);
-            fb = (float)(y - fy);
-            const int x0 = (int)fx, y0 = (int)fy;
+        int x0, y0;
+        if (msda_corner(uv, Wl, Hl, x0, y0, fa, fb) && valid) {
+            if constexpr (SORTED) {
+                const int bk = C.pstart[l] + (y0 + 1) * (Wl + 1) + x0 + 1;
+                const int pos = boff[(long)pair * (C.Sp + 1) + bk] + rank[item * LP + i];
+                rec[((long)pair * G.q << LPlog) + pos] = make_int4(q, __float_as_int(A), __float_as_int(fa),
+                                                                   __float_as_int(fb));
+            }
             // byte offset of cell (y0, x0) of this image and head (modulo 2^32:
             // only the offsets of cells inside the level are used)
             const long row = (long)n * G.S + G.start[l] + (long)y0 * Wl + x0;
@@ -106,10 +196,10 @@ __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int 
     }
     __syncthreads();
 
-    // ---- phase 2: lane = (query, channel)
+    // ---- phase 2: lane = (query, V channels)
     {
-        const int D = 1 << Dlog;
-        const int qi = tid >> Dlog, c = tid & (D - 1);
+        const int LPQ = G.dh / V;   // lanes per query
+        const int qi = tid / LPQ, c = tid - qi * LPQ;
         const int q = q0 + qi;
         const bool live = qi < QT && q < G.q;
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)value, (short)0, (int)value_bytes,
@@ -117,35 +207,68 @@ __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int 
         const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)gvalue, (short)0,
                                                                             gvalue ? (int)value_bytes : 0, 0x00020000);
         const long item = ((long)n * G.q + (live ? q : 0)) * G.m + h;
-        const float g = live ? gout[item * G.dh + c] : 0.f;
-        const uint32_t cb = 4u * c;
+        float g[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) g[k] = live ? gout[item * G.dh + V * c + k] : 0.f;
+        const uint32_t cb = 4u * V * c;
         const int r0 = (live ? qi : 0) << LPlog;
         // Lanes of a query that is past the end still take part in the
-        // reductions (with g = 0) and write nothing.
-        for (int i = 0; i < LP; ++i) {
-            const u32x4 o = rec_o[r0 + i];
-            const float4 f = rec_f[r0 + i];
-            const float a = f.x, bb = f.y, A = f.z;
-            const float v00 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, o.x + cb, 0, 0));
-            const float v01 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, o.y + cb, 0, 0));
-            const float v10 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, o.z + cb, 0, 0));
-            const float v11 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, o.w + cb, 0, 0));
-            const float wa = 1.f - a, wb = 1.f - bb;
-            const float w00 = wa * wb, w01 = a * wb, w10 = wa * bb, w11 = a * bb;
-            if (gvalue && live) {
-                const float Ag = A * g;
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * w00, gr, o.x + cb, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * w01, gr, o.y + cb, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * w10, gr, o.z + cb, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * w11, gr, o.w + cb, 0, 0);
+        // reductions (with g = 0) and write nothing.  The corners of U
+        // samples are loaded before any is used (U = 4 for the gather, whose
+        // loop is otherwise latency-bound; the scatter is bound by its atomics).
+        constexpr int U = V == 4 ? 4 : 1;
+        for (int i0 = 0; i0 < LP; i0 += U) {
+            float vv[U][4][V];
+            float4 ff[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = i0 + u < LP;
+                const u32x4 o = in ? rec_o[r0 + i0 + u] : u32x4{MS_OOB, MS_OOB, MS_OOB, MS_OOB};
+                ff[u] = in ? rec_f[r0 + i0 + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+                load_v<V>(vr, o.x + cb, vv[u][0]);
+                load_v<V>(vr, o.y + cb, vv[u][1]);
+                load_v<V>(vr, o.z + cb, vv[u][2]);
+                load_v<V>(vr, o.w + cb, vv[u][3]);
+                if constexpr (U == 1) {
+                    if (gvalue && live) {
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            const float Ag = ff[u].z * g[k];
+                            const float a = ff[u].x, bb = ff[u].y;
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * ((1.f - a) * (1.f - bb)), gr,
+                                                                            o.x + cb + 4 * k, 0, 0);
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * (a * (1.f - bb)), gr,
+                                                                            o.y + cb + 4 * k, 0, 0);
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * ((1.f - a) * bb), gr,
+                                                                            o.z + cb + 4 * k, 0, 0);
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(Ag * (a * bb), gr, o.w + cb + 4 * k,
+                                                                            0, 0);
+                        }
+                    }
+                }
             }
-            const float s = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
-            const float dA = lane_sum(g * s, D);
-            const float da = lane_sum(g * (wb * (v01 - v00) + bb * (v11 - v10)), D);
-            const float db = lane_sum(g * (wa * (v10 - v00) + a * (v11 - v01)), D);
-            if (live && c == 0) {
-                const int l = i / G.P;
-                rec_f[r0 + i] = make_float4(A * da * (float)G.W[l], A * db * (float)G.H[l], A, dA);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u;
+                const float a = ff[u].x, bb = ff[u].y, A = ff[u].z;
+                const float* v00 = vv[u][0];
+                const float* v01 = vv[u][1];
+                const float* v10 = vv[u][2];
+                const float* v11 = vv[u][3];
+                const float wa = 1.f - a, wb = 1.f - bb;
+                const float w00 = wa * wb, w01 = a * wb, w10 = wa * bb, w11 = a * bb;
+                float sA = 0.f, sa = 0.f, sb = 0.f;
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    sA += g[k] * (w00 * v00[k] + w01 * v01[k] + w10 * v10[k] + w11 * v11[k]);
+                    sa += g[k] * (wb * (v01[k] - v00[k]) + bb * (v11[k] - v10[k]));
+                    sb += g[k] * (wa * (v10[k] - v00[k]) + a * (v11[k] - v01[k]));
+                }
+                const float dA = row_sum(sA, LPQ), da = row_sum(sa, LPQ), db = row_sum(sb, LPQ);
+                if (live && c == 0 && i < LP) {
+                    const int l = i / G.P;
+                    rec_f[r0 + i] = make_float4(A * da * (float)G.W[l], A * db * (float)G.H[l], A, dA);
+                }
             }
         }
     }
@@ -257,38 +380,393 @@ __global__ __launch_bounds__(256) void fill_zero_f32(float* __restrict__ p, long
     }
 }
 
+// One thread per sample: count the sample into its bucket; the count before
+// it is its rank (-1 for a sample with no corner inside its level).
+__global__ __launch_bounds__(256) void msda_bwd_count(MsdaGeom G, MsdaSortCfg C, int LPlog,
+                                                      const float* __restrict__ loc, int* __restrict__ cnt,
+                                                      int* __restrict__ rank)
+{
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= (G.n * G.q * G.m << LPlog)) return;
+    const int item = s >> LPlog, i = s & ((1 << LPlog) - 1);
+    const int h = item % G.m, n = item / (G.q * G.m);
+    const int l = i / G.P;
+    const float2 uv = *reinterpret_cast<const float2*>(loc + (long)s * 2);
+    int x0, y0, r = -1;
+    float fa, fb;
+    if (msda_corner(uv, G.W[l], G.H[l], x0, y0, fa, fb)) {
+        const int bk = C.pstart[l] + (y0 + 1) * (G.W[l] + 1) + x0 + 1;
+        r = atomicAdd(cnt + (long)(n * G.m + h) * (C.Sp + 1) + bk, 1);
+    }
+    rank[s] = r;
+}
+
+// The same counts and ranks, aggregated in LDS first: a workgroup of 1024
+// threads takes CQ_SAMPLES samples of one pair (CQ_SAMPLES / LP consecutive
+// queries), counts them per bucket with LDS atomics (the returned value is
+// the rank among the workgroup's samples), adds each nonzero bucket count to
+// the global one with a single atomic (which returns the workgroup's base),
+// and writes base + local rank.  Queries that are neighbours in the map
+// share coarse-level buckets, so this replaces most global atomics on
+// crowded addresses by LDS ones.  LDS: Sp ints.
+constexpr int CQ_SPT = 16;                  // samples per thread
+constexpr int CQ_SAMPLES = 1024 * CQ_SPT;   // samples per workgroup
+
+__global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortCfg C, int LPlog, int chunks,
+                                                           const float* __restrict__ loc, int* __restrict__ cnt,
+                                                           int* __restrict__ rank)
+{
+    extern __shared__ int lc[];
+    const int pair = blockIdx.x / chunks, ck = blockIdx.x - pair * chunks;
+    const int n = pair / G.m, h = pair - n * G.m;
+    const int t = threadIdx.x;
+    for (int b = t; b < C.Sp; b += 1024) lc[b] = 0;
+    __syncthreads();
+    const int LP = 1 << LPlog;
+    int bk[CQ_SPT], lr[CQ_SPT];
+#pragma unroll
+    for (int k = 0; k < CQ_SPT; ++k) {
+        const int sl = ck * CQ_SAMPLES + k * 1024 + t;
+        const int q = sl >> LPlog, i = sl & (LP - 1);
+        bk[k] = -1;
+        lr[k] = 0;
+        if (q < G.q) {
+            const int l = i / G.P;
+            const long gs = (((long)n * G.q + q) * G.m + h) * LP + i;
+            const float2 uv = *reinterpret_cast<const float2*>(loc + gs * 2);
+            int x0, y0;
+            float fa, fb;
+            if (msda_corner(uv, G.W[l], G.H[l], x0, y0, fa, fb)) {
+                bk[k] = C.pstart[l] + (y0 + 1) * (G.W[l] + 1) + x0 + 1;
+                lr[k] = atomicAdd(lc + bk[k], 1);
+            }
+        }
+    }
+    __syncthreads();
+    int* gc = cnt + (long)pair * (C.Sp + 1);
+    for (int b = t; b < C.Sp; b += 1024) {
+        const int c = lc[b];
+        if (c) lc[b] = atomicAdd(gc + b, c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CQ_SPT; ++k) {
+        const int sl = ck * CQ_SAMPLES + k * 1024 + t;
+        const int q = sl >> LPlog, i = sl & (LP - 1);
+        if (q < G.q) rank[(((long)n * G.q + q) * G.m + h) * LP + i] = bk[k] >= 0 ? lc[bk[k]] + lr[k] : -1;
+    }
+}
+
+// In-place exclusive prefix sum of `len` counts per pair, one workgroup of
+// 1024 threads per pair, each thread over a contiguous run.
+__global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int len)
+{
+    __shared__ int wsum[16];
+    int* p = cnt + (long)blockIdx.x * len;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int per = (len + 1023) / 1024;
+    const int lo = min(len, t * per), hi = min(len, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += p[i];
+    int v = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wv] = v;
+    __syncthreads();
+    if (t < 64) {
+        int w = t < 16 ? wsum[t] : 0;
+        for (int o = 1; o < 16; o <<= 1) {
+            const int u = __shfl_up(w, o, 64);
+            if (lane >= o) w += u;
+        }
+        if (t < 16) wsum[t] = w;
+    }
+    __syncthreads();
+    int run = (wv ? wsum[wv - 1] : 0) + v - sum;
+    for (int i = lo; i < hi; ++i) {
+        const int c = p[i];
+        p[i] = run;
+        run += c;
+    }
+}
+
+// grad_value by cells: a group of LPC = head_dim/4 lanes reads a batch of
+// 2*LPC records (two a lane) while the previous batch's grad_out slices are
+// in flight.  A level whose cells expect long runs gives each cell gpc groups
+// (interleaved batches), summed through LDS at the end.
+template <int LPC>
+__global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C, int LPlog,
+                                                      const int* __restrict__ boff, const int4* __restrict__ rec,
+                                                      const float* __restrict__ gout, uint32_t gout_bytes,
+                                                      float* __restrict__ gvalue)
+{
+    __shared__ float4 stage[256];
+    __shared__ float4 part[256];
+    const int b = blockIdx.x;
+    int k = 0;
+    while (k + 1 < G.L && b >= C.blk_start[k + 1]) ++k;
+    const int l = G.L - 1 - k;
+    const int local = b - C.blk_start[k];
+    const int nb = C.blk_start[k + 1] - C.blk_start[k];
+    const int r = (local & 7) * (nb >> 3) + (local >> 3);   // each XCD sweeps a contiguous range
+    const int wpp = C.wg_per_pair[l];
+    const int pair = r / wpp;
+    if (pair >= G.n * G.m) return;
+    const int n = pair / G.m, h = pair - n * G.m;
+    const int gpc = C.gpc[l];
+    const int t = threadIdx.x, grp = t / LPC, j = t - grp * LPC;
+    const int slot = grp / gpc, gi = grp - slot * gpc;
+    const int Wl = G.W[l];
+    const int cell = (r - pair * wpp) * (256 / (LPC * gpc)) + slot;
+    const bool live = cell < Wl * G.H[l];
+    const int y = live ? cell / Wl : 0, x = live ? cell - y * Wl : 0;
+    // Runs: samples with y0 = y-1 (this cell is their lower corner row), then
+    // y0 = y (upper); within each, x0 = x-1 (right corner) before x0 = x (left).
+    const int* po = boff + (long)pair * (C.Sp + 1) + C.pstart[l] + y * (Wl + 1) + x;
+    const int a0 = po[0], a1 = po[1], a2 = po[2];
+    const int c0 = po[Wl + 1], c1 = po[Wl + 2], c2 = po[Wl + 3];
+    const int n0 = live ? a2 - a0 : 0;
+    const int ntot = live ? n0 + c2 - c0 : 0;
+    const int4* pr = rec + ((long)pair * G.q << LPlog);
+    const uint32_t rowb = (uint32_t)G.m * G.dh * 4u;
+    const uint32_t gbase = (uint32_t)((long)n * G.q * G.m + h) * (uint32_t)(G.dh * 4) + 16u * j;
+    const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)gout, (short)0, (int)gout_bytes,
+                                                                        0x00020000);
+    // A batch is 2*LPC run positions: lane j holds positions k0+j and
+    // k0+LPC+j, so 2*LPC grad_out slices are in flight per group.
+    const int step = gpc * 2 * LPC;
+    // record index of run position tt, and whether it lies in the upper run
+    auto where = [&](int tt, bool& upper) {
+        upper = tt < n0;
+        return upper ? a0 + tt : c0 + tt - n0;
+    };
+    auto fetch = [&](int tt, int4& e) {
+        bool up;
+        const int idx = where(tt, up);
+        if (tt < ntot) e = pr[idx];
+    };
+    // (grad_out byte offset, weight) of run position tt with record e
+    auto weigh = [&](int tt, const int4& e, uint32_t& go, float& w) {
+        w = 0.f;
+        go = MS_OOB;   // past the end of grad_out: reads zero
+        if (tt < ntot) {
+            bool upper;
+            const int idx = where(tt, upper);
+            const float fa = __int_as_float(e.z), fb = __int_as_float(e.w);
+            const float wx = (upper ? idx < a1 : idx < c1) ? fa : 1.f - fa;
+            const float wy = upper ? fb : 1.f - fb;
+            w = __int_as_float(e.y) * (wx * wy);
+            go = (uint32_t)e.x * rowb;
+        }
+    };
+    int4 e0 = make_int4(0, 0, 0, 0), e1 = e0;
+    fetch(gi * 2 * LPC + j, e0);
+    fetch(gi * 2 * LPC + LPC + j, e1);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = gi * 2 * LPC; k0 < ntot; k0 += step) {   // the same trip count for the whole group
+        float4 sw;
+        uint32_t go0, go1;
+        weigh(k0 + j, e0, go0, sw.y);
+        weigh(k0 + LPC + j, e1, go1, sw.w);
+        sw.x = __uint_as_float(go0);
+        sw.z = __uint_as_float(go1);
+        fetch(k0 + step + j, e0);
+        fetch(k0 + step + LPC + j, e1);
+        stage[t] = sw;
+        wave_lds_sync();
+#pragma unroll
+        for (int u = 0; u < LPC; ++u) {
+            const float4 p = stage[grp * LPC + u];
+            const uint32_t o0 = __float_as_uint(p.x), o1 = __float_as_uint(p.z);
+            const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(gr, o0 == MS_OOB ? o0 : o0 + gbase, 0, 0);
+            const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(gr, o1 == MS_OOB ? o1 : o1 + gbase, 0, 0);
+            acc.x = fmaf(p.y, __uint_as_float(v0.x), acc.x);
+            acc.y = fmaf(p.y, __uint_as_float(v0.y), acc.y);
+            acc.z = fmaf(p.y, __uint_as_float(v0.z), acc.z);
+            acc.w = fmaf(p.y, __uint_as_float(v0.w), acc.w);
+            acc.x = fmaf(p.w, __uint_as_float(v1.x), acc.x);
+            acc.y = fmaf(p.w, __uint_as_float(v1.y), acc.y);
+            acc.z = fmaf(p.w, __uint_as_float(v1.z), acc.z);
+            acc.w = fmaf(p.w, __uint_as_float(v1.w), acc.w);
+        }
+        wave_lds_sync();
+    }
+    if (gpc > 1) {   // uniform over the workgroup
+        part[t] = acc;
+        __syncthreads();
+        if (gi == 0)
+            for (int u = 1; u < gpc; ++u) {
+                const float4 p = part[t + u * LPC];
+                acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+            }
+    }
+    if (live && gi == 0)
+        *reinterpret_cast<float4*>(gvalue + (((long)n * G.S + G.start[l] + cell) * G.m + h) * G.dh + 4 * j) = acc;
+}
+
+// Queries per workgroup of the tiled kernel: 256 lanes of V channels, at most
+// MS_REC_MAX sample records.
+int tile_queries(const MsdaGeom& G, int V)
+{
+    return std::min(256 / (G.dh / V), MS_REC_MAX / (G.L * G.P));
+}
+
+// Shapes the tiled kernel takes (LPlog, Dlog filled in).
+bool tile_shape(const MsdaGeom& G, const float* loc, const float* gloc, int* LPlog, int* Dlog)
+{
+    const int LP = G.L * G.P;
+    const long value_bytes = (long)G.n * G.S * G.m * G.dh * 4;
+    const bool aligned = (uintptr_t)loc % 8 == 0 && (!gloc || (uintptr_t)gloc % 8 == 0);
+    const bool pow2 = (LP & (LP - 1)) == 0 && LP <= 32 && (G.dh & (G.dh - 1)) == 0 && G.dh <= 64;
+    if (!aligned || !pow2 || value_bytes >= (1L << 31) - 64) return false;
+    const int QT = tile_queries(G, 1);   // the smaller of the two tilings
+    if ((long)G.n * G.m * ((G.q + QT - 1) / QT) >= (1L << 30)) return false;
+    *LPlog = 0;
+    *Dlog = 0;
+    while ((1 << *LPlog) < LP) ++*LPlog;
+    while ((1 << *Dlog) < G.dh) ++*Dlog;
+    return true;
+}
+
+// Workspace of the gather: offsets [pairs][Sp+1], ranks [samples], records [samples] (16 B).
+struct SortWs {
+    long off_bytes, rank_bytes, rec_bytes;
+    long total() const { return off_bytes + rank_bytes + rec_bytes; }
+};
+
+bool sort_layout(const MsdaGeom& G, MsdaSortCfg* C, SortWs* W)
+{
+    if (G.dh < 4 || G.dh > 64) return false;
+    const long gout_bytes = (long)G.n * G.q * G.m * G.dh * 4;
+    if (gout_bytes >= (1L << 31) - 64) return false;
+    long Sp = 0;
+    for (int l = 0; l < G.L; ++l) {
+        C->pstart[l] = (int)Sp;
+        Sp += (long)(G.H[l] + 1) * (G.W[l] + 1);
+    }
+    const long pairs = (long)G.n * G.m;
+    if (pairs * (Sp + 1) >= (1L << 31)) return false;
+    C->Sp = (int)Sp;
+    const int lpc = G.dh / 4;
+    long blk = 0;
+    for (int k = 0; k < G.L; ++k) {
+        const int l = G.L - 1 - k;
+        C->blk_start[k] = (int)blk;
+        // Records a cell of this level expects if the samples spread evenly
+        // (len_q * points samples per pair land on the level, 4 corners each).
+        const double expect = 4.0 * G.q * G.P / ((double)G.H[l] * G.W[l]);
+        int gpc = 1;
+        while (gpc < 256 / lpc && expect > 64.0 * gpc) gpc *= 2;   // about 64 records a group
+        C->gpc[l] = gpc;
+        const int cpw = 256 / (lpc * gpc);
+        C->wg_per_pair[l] = (int)(((long)G.H[l] * G.W[l] + cpw - 1) / cpw);
+        blk += (pairs * C->wg_per_pair[l] + 7) & ~7L;
+        if (blk >= (1L << 31)) return false;
+    }
+    C->blk_start[G.L] = (int)blk;
+    const long ns = pairs * G.q * G.L * G.P;
+    W->off_bytes = (pairs * (Sp + 1) * 4 + 255) & ~255L;
+    W->rank_bytes = (ns * 4 + 255) & ~255L;
+    W->rec_bytes = ns * 16;
+    return true;
+}
+
+template <int LPC>
+void launch_cells(const MsdaGeom& G, const MsdaSortCfg& C, int LPlog, const int* boff, const int4* rec,
+                  const float* gout, float* gvalue, hipStream_t s)
+{
+    const uint32_t gout_bytes = (uint32_t)((long)G.n * G.q * G.m * G.dh * 4);
+    msda_bwd_cells<LPC><<<dim3((unsigned)C.blk_start[G.L]), dim3(256), 0, s>>>(G, C, LPlog, boff, rec, gout,
+                                                                               gout_bytes, gvalue);
+}
+
 }  // namespace
 
+size_t msda_backward_workspace(const MsdaGeom& G)
+{
+    MsdaSortCfg C;
+    SortWs W;
+    int LPlog, Dlog;
+    // Alignment of loc does not change the answer here; the launch re-checks it.
+    if (!tile_shape(G, nullptr, nullptr, &LPlog, &Dlog) || !sort_layout(G, &C, &W)) return 0;
+    return (size_t)W.total();
+}
+
 hipError_t launch_msda_backward(const MsdaGeom& G, const float* value, const float* loc, const float* attn,
-                                const float* gout, float* gvalue, float* gloc, float* gattn, hipStream_t s)
+                                const float* gout, float* gvalue, float* gloc, float* gattn, void* ws,
+                                size_t ws_bytes, hipStream_t s)
 {
     const long vcount = (long)G.n * G.S * G.m * G.dh;
+    const long items = (long)G.n * G.q * G.m;
+    const long value_bytes = vcount * 4;
+    int LPlog = 0, Dlog = 0;
+    MsdaSortCfg C = {};
+    SortWs W = {};
+    if (tile_shape(G, loc, gloc, &LPlog, &Dlog)) {
+        const bool sorted = gvalue && ws && sort_layout(G, &C, &W) && (long)ws_bytes >= W.total() &&
+                            (uintptr_t)ws % 16 == 0 && (uintptr_t)gvalue % 16 == 0 && (uintptr_t)gout % 16 == 0;
+        int* boff = nullptr;
+        int* rank = nullptr;
+        int4* rec = nullptr;
+        if (sorted) {
+            boff = (int*)ws;
+            rank = (int*)((char*)ws + W.off_bytes);
+            rec = (int4*)((char*)ws + W.off_bytes + W.rank_bytes);
+            const long nb = (long)G.n * G.m * (C.Sp + 1);
+            fill_zero_f32<<<dim3((unsigned)std::min((nb / 4 + 255) / 256 + 1, 65536L)), dim3(256), 0, s>>>(
+                (float*)boff, nb);
+            int lds_limit = 65536, num_cus = 256;
+            device_limits(&lds_limit, &num_cus);
+            const int lds = C.Sp * 4;
+            const long chunks = (((long)G.q << LPlog) + CQ_SAMPLES - 1) / CQ_SAMPLES;
+            if (lds <= std::min(lds_limit, 96 * 1024) && (long)G.n * G.m * chunks < (1L << 31) &&
+                hipFuncSetAttribute((const void*)msda_bwd_count_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds) == hipSuccess) {
+                msda_bwd_count_lds<<<dim3((unsigned)(G.n * G.m * chunks)), dim3(1024), lds, s>>>(
+                    G, C, LPlog, (int)chunks, loc, boff, rank);
+            } else {
+                const long ns = items << LPlog;
+                msda_bwd_count<<<dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s>>>(G, C, LPlog, loc, boff,
+                                                                                         rank);
+            }
+            msda_bwd_scan<<<dim3((unsigned)(G.n * G.m)), dim3(1024), 0, s>>>(boff, C.Sp + 1);
+        } else if (gvalue) {
+            fill_zero_f32<<<dim3((unsigned)std::min((vcount / 4 + 255) / 256 + 1, 65536L)), dim3(256), 0, s>>>(
+                gvalue, vcount);
+        }
+        const int V = sorted ? 4 : 1;   // the gather needs head_dim >= 4
+        const int QT = tile_queries(G, V);
+        const int tiles = (G.q + QT - 1) / QT;
+        const long nwg = (long)G.n * G.m * tiles;
+        const dim3 grid((unsigned)((nwg + 7) & ~7L)), blk((unsigned)(QT * G.dh / V));
+        float* gv_tile = sorted ? nullptr : gvalue;
+#define MS_TILE(SM, SO, VV)                                                                                      \
+    msda_bwd_tile<SM, SO, VV><<<grid, blk, 0, s>>>(G, LPlog, Dlog, QT, tiles, (int)nwg, (uint32_t)value_bytes, \
+                                                   value, loc, attn, gout, gv_tile, gloc, gattn, C, boff, rank, rec)
+        if (G.softmax) {
+            if (sorted) MS_TILE(true, true, 4);
+            else MS_TILE(true, false, 1);
+        } else {
+            if (sorted) MS_TILE(false, true, 4);
+            else MS_TILE(false, false, 1);
+        }
+#undef MS_TILE
+        if (sorted) {
+            switch (G.dh / 4) {
+            case 1: launch_cells<1>(G, C, LPlog, boff, rec, gout, gvalue, s); break;
+            case 2: launch_cells<2>(G, C, LPlog, boff, rec, gout, gvalue, s); break;
+            case 4: launch_cells<4>(G, C, LPlog, boff, rec, gout, gvalue, s); break;
+            case 8: launch_cells<8>(G, C, LPlog, boff, rec, gout, gvalue, s); break;
+            default: launch_cells<16>(G, C, LPlog, boff, rec, gout, gvalue, s); break;
+            }
+        }
+        return hipGetLastError();
+    }
     if (gvalue) {
         const long blocks = std::min((vcount / 4 + 255) / 256 + 1, 65536L);
         fill_zero_f32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(gvalue, vcount);
-    }
-    const long items = (long)G.n * G.q * G.m;
-    const int LP = G.L * G.P;
-    const long value_bytes = vcount * 4;
-    const bool aligned = (uintptr_t)loc % 8 == 0 && (!gloc || (uintptr_t)gloc % 8 == 0);
-    const bool pow2 = (LP & (LP - 1)) == 0 && LP <= 32 && (G.dh & (G.dh - 1)) == 0 && G.dh <= 64;
-    if (aligned && pow2 && value_bytes < (1L << 31) - 64) {
-        int LPlog = 0, Dlog = 0;
-        while ((1 << LPlog) < LP) ++LPlog;
-        while ((1 << Dlog) < G.dh) ++Dlog;
-        const int QT = std::min(256 / G.dh, MS_REC_MAX / LP);
-        const int tiles = (G.q + QT - 1) / QT;
-        const long nwg = (long)G.n * G.m * tiles;
-        if (nwg < (1L << 30)) {
-            const dim3 grid((unsigned)((nwg + 7) & ~7L)), blk((unsigned)(QT * G.dh));
-            if (G.softmax)
-                msda_bwd_tile<true><<<grid, blk, 0, s>>>(G, LPlog, Dlog, QT, tiles, (int)nwg, (uint32_t)value_bytes,
-                                                         value, loc, attn, gout, gvalue, gloc, gattn);
-            else
-                msda_bwd_tile<false><<<grid, blk, 0, s>>>(G, LPlog, Dlog, QT, tiles, (int)nwg, (uint32_t)value_bytes,
-                                                          value, loc, attn, gout, gvalue, gloc, gattn);
-            return hipGetLastError();
-        }
     }
     const dim3 grid((unsigned)((items + 255) / 256));
     if (G.softmax)

@@ -191,6 +191,56 @@ def test_msda_backward_validation():
     assert call(grads=(0, 0, 0)) == B.DCN_OK
 
 
+def test_msda_backward_workspace_size_and_validation():
+    """Workspace of the per-cell gather: 4 bytes per bucket of a (H_l+1) x
+    (W_l+1) grid per level, image and head (plus one per pair), 20 bytes per
+    sample, each part rounded up to 256 bytes; 0 where the shape has no gather
+    path.  msda_backward_ws refuses a missing, short or misaligned one."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+
+    def size(shp, **over):
+        d = dict(n=2, len_q=7, heads=3, head_dim=8, levels=len(shp) // 2, points=2, softmax=1, dtype=B.DCN_F32)
+        d.update(over)
+        out = ctypes.c_size_t(123)
+        st = L.msda_backward_workspace_size(ctypes.byref(B.MsdaDesc(**d)), (ctypes.c_int32 * len(shp))(*shp),
+                                            ctypes.byref(out))
+        return st, out.value
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    buckets = (4 + 1) * (5 + 1) + (2 + 1) * (3 + 1)
+    samples = 2 * 7 * 3 * 2 * 2
+    assert size((4, 5, 2, 3)) == (B.DCN_OK, up(2 * 3 * (buckets + 1) * 4) + up(samples * 4) + samples * 16)
+    enc = (100, 134, 50, 67, 25, 34, 13, 17)
+    st, nb = size(enc, n=8, len_q=17821, heads=8, head_dim=32, points=4)
+    assert st == B.DCN_OK and 360e6 < nb < 380e6
+    assert size((4, 5, 2, 3), head_dim=36) == (B.DCN_OK, 0)     # not a power of two
+    assert size((4, 5, 2, 3), head_dim=2) == (B.DCN_OK, 0)      # under 4 channels
+    assert size((4, 5, 2, 3), points=3) == (B.DCN_OK, 0)        # 6 samples per head
+    assert size((4, 5, 2, 3), dtype=B.DCN_F16) == (B.DCN_OK, 0)
+    assert size((4, 5, 2, 3), levels=0)[0] == B.DCN_ERR_INVALID
+    assert L.msda_backward_workspace_size(ctypes.byref(B.MsdaDesc(1, 3, 2, 8, 2, 2, 1, B.DCN_F32)),
+                                          (ctypes.c_int32 * 4)(4, 5, 2, 3), None) == B.DCN_ERR_INVALID
+
+    shapes = (ctypes.c_int32 * 4)(4, 5, 2, 3)
+    desc = B.MsdaDesc(1, 3, 2, 8, 2, 2, 1, B.DCN_F32)
+    need = ctypes.c_size_t(0)
+    assert L.msda_backward_workspace_size(ctypes.byref(desc), shapes, ctypes.byref(need)) == B.DCN_OK
+    ins = [vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000)]
+
+    def call(grads=(0x5000, 0x6000, 0x7000), ws=0x100000, nbytes=None):
+        g = [vp(p) if p else None for p in grads]
+        return L.msda_backward_ws(ctypes.byref(desc), shapes, *ins, *g, vp(ws) if ws else None,
+                                  need.value if nbytes is None else nbytes, None)
+
+    assert call(ws=0) == B.DCN_ERR_INVALID                           # grad_value needs the workspace
+    assert call(nbytes=need.value - 1) == B.DCN_ERR_INVALID
+    assert call(ws=0x100010) == B.DCN_ERR_UNSUPPORTED                # not 256-byte aligned
+    assert call(grads=(0, 0, 0), ws=0) == B.DCN_OK                   # nothing requested, nothing enqueued
+
+
 def test_torch_wrappers_refuse_cpu_tensors():
     import torch
     import sparse_deformable_sampling_amd as sds

@@ -566,12 +566,15 @@ def check_msda_bwd(sds, name, n, shapes, q, heads, dh, points, softmax=True, see
     d = synth.msda_inputs(n, shapes, q, heads, dh, points, offset_std=offset_std, seed=seed, ref=ref)
     g = synth.store(np.random.default_rng(seed + 1000).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
     v, loc, attn, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
-    say(name, (n, shapes, q, heads, dh, points), softmax)
-    gv, gl, ga = sds.msda_backward(v, shapes, loc, attn, go, softmax=softmax)
-    torch.cuda.synchronize()
     rv, rl, ra = oracle.msda_backward(d["value"], shapes, d["loc"], d["attn"], g, softmax=softmax)
-    errs = (rel_err(to_host(gv), rv), rel_err(to_host(gl), rl), rel_err(to_host(ga), ra))
-    assert all(e <= t for e, t in zip(errs, MSDA_BWD_TOL)), (name, softmax, errs)
+    errs = []
+    for gather in (True, False):   # grad_value gathered per cell / scattered with atomics
+        say(name, (n, shapes, q, heads, dh, points), "softmax", softmax, "gather", gather)
+        gv, gl, ga = sds.msda_backward(v, shapes, loc, attn, go, softmax=softmax, gather=gather)
+        torch.cuda.synchronize()
+        e = (rel_err(to_host(gv), rv), rel_err(to_host(gl), rl), rel_err(to_host(ga), ra))
+        assert all(x <= t for x, t in zip(e, MSDA_BWD_TOL)), (name, softmax, gather, e)
+        errs.append(e)
     return errs
 
 
@@ -596,6 +599,31 @@ def test_msda_backward_shapes(sds, n, shapes, q, heads, dh, points):
         check_msda_bwd(sds, "msda-bwd", n, shapes, q, heads, dh, points, softmax=softmax, seed=53, offset_std=3.0)
 
 
+def test_msda_backward_crowded_cells(sds):
+    """Every sample of an (image, head) pair in one bucket per level: the
+    gather's runs are thousands of records long (len_q * points per level),
+    against the oracle and the atomic scatter; a second pair reads nothing
+    inside (all samples far outside), so its grad_value must come back zero."""
+    import torch
+    shapes = [(12, 10), (6, 5), (3, 3)]
+    n, q, heads, dh, points = 1, 1500, 2, 32, 2
+    d = synth.msda_inputs(n, shapes, q, heads, dh, points, seed=61)
+    loc = d["loc"].copy()
+    loc[0, :, 0] = [0.43, 0.57]          # head 0: one point on every level
+    loc[0, :, 1] = [-3.0, 0.5]           # head 1: outside everywhere
+    d["loc"] = synth.store(loc, "f32")
+    g = synth.store(np.random.default_rng(7).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
+    v, lc, at, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
+    rv, rl, ra = oracle.msda_backward(d["value"], shapes, d["loc"], d["attn"], g, softmax=True)
+    for gather in (True, False):
+        say("msda-bwd-crowded", "gather", gather)
+        got = sds.msda_backward(v, shapes, lc, at, go, gather=gather)
+        torch.cuda.synchronize()
+        for t, ref, tol in zip(got, (rv, rl, ra), MSDA_BWD_TOL):
+            assert rel_err(to_host(t), ref) <= tol, gather
+        assert np.all(to_host(got[0])[0, :, 1] == 0.0)
+
+
 def test_msda_backward_far_outside_and_partial_outputs(sds):
     import torch
     shapes = [(6, 5), (3, 4)]
@@ -609,20 +637,22 @@ def test_msda_backward_far_outside_and_partial_outputs(sds):
     g = synth.store(np.random.default_rng(5).standard_normal((n, q, heads, dh)).astype(np.float32), "f32")
     v, lc, at, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
     rv, rl, ra = oracle.msda_backward(d["value"], shapes, d["loc"], d["attn"], g, softmax=True)
-    say("msda-bwd-partial")
-    full = sds.msda_backward(v, shapes, lc, at, go)
-    torch.cuda.synchronize()
-    for got, ref, tol in zip(full, (rv, rl, ra), MSDA_BWD_TOL):
-        assert rel_err(to_host(got), ref) <= tol
-    assert np.all(to_host(full[1])[0, 3, 1, 0, 2] == 0.0)
-    for need in [(True, False, False), (False, True, False), (False, False, True)]:
-        got = sds.msda_backward(v, shapes, lc, at, go, need_value=need[0], need_loc=need[1], need_attn=need[2])
+    for gather in (True, False):
+        say("msda-bwd-partial", "gather", gather)
+        full = sds.msda_backward(v, shapes, lc, at, go, gather=gather)
         torch.cuda.synchronize()
-        for flag, t, ref, tol in zip(need, got, (rv, rl, ra), MSDA_BWD_TOL):
-            if flag:
-                assert rel_err(to_host(t), ref) <= tol
-            else:
-                assert t is None
+        for got, ref, tol in zip(full, (rv, rl, ra), MSDA_BWD_TOL):
+            assert rel_err(to_host(got), ref) <= tol
+        assert np.all(to_host(full[1])[0, 3, 1, 0, 2] == 0.0)
+        for need in [(True, False, False), (False, True, False), (False, False, True)]:
+            got = sds.msda_backward(v, shapes, lc, at, go, need_value=need[0], need_loc=need[1], need_attn=need[2],
+                                    gather=gather)
+            torch.cuda.synchronize()
+            for flag, t, ref, tol in zip(need, got, (rv, rl, ra), MSDA_BWD_TOL):
+                if flag:
+                    assert rel_err(to_host(t), ref) <= tol
+                else:
+                    assert t is None
 
 
 # ---------------------------------------------------------------- DCNv4 front-end
