@@ -42,11 +42,12 @@
 //  - msda_bwd_scan: exclusive prefix sum of the counts, one workgroup per pair.
 //  - the tiled kernel writes each sample's record (query, A, a, b) at
 //    offset + rank, alongside grad_loc and grad_attn.
-//  - msda_bwd_cells: a group of head_dim/4 lanes per cell, 4 channels a lane;
-//    the group reads its two runs of records in batches (one record per lane,
-//    the corner weight formed by the lane that read it, broadcast through
-//    LDS) and the matching 16-byte slices of grad_out, and stores the sum.
-//    Coarse levels, whose cells have the longest runs, are dispatched first.
+//  - msda_bwd_cells: a group of head_dim/4 lanes per block of 4 adjacent
+//    cells of a row, 4 channels a lane; the group reads the block's two runs
+//    of records in batches (one record per lane, the 4 cells' weights formed
+//    by the lane that read it, broadcast through LDS) and the matching
+//    16-byte slices of grad_out, and stores the 4 sums.  Coarse levels, whose
+//    cells have the longest runs, are dispatched first.
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -64,7 +65,7 @@ struct MsdaSortCfg {
     int Sp;                                // buckets per pair: sum of (H_l+1)(W_l+1); offsets hold Sp+1
     int pstart[MSDA_MAX_LEVELS];           // first bucket of level l within a pair
     int wg_per_pair[MSDA_MAX_LEVELS];      // cell-kernel workgroups per pair at level l
-    int gpc[MSDA_MAX_LEVELS];              // lane groups per cell at level l (a power of two)
+    int gpc[MSDA_MAX_LEVELS];              // lane groups per block of cells at level l (a power of two)
     int blk_start[MSDA_MAX_LEVELS + 1];    // first cell-kernel workgroup of the k-th level taken (coarsest
                                            // first), each a multiple of 8; the last is the grid size
 };
@@ -492,18 +493,28 @@ __global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int
     }
 }
 
-// grad_value by cells: a group of LPC = head_dim/4 lanes reads a batch of
-// 2*LPC records (two a lane) while the previous batch's grad_out slices are
-// in flight.  A level whose cells expect long runs gives each cell gpc groups
-// (interleaved batches), summed through LDS at the end.
+// grad_value by cells.  A group of LPC = head_dim/4 lanes (4 channels a
+// lane) owns a block of CB adjacent cells of one row, x = xs .. xs+CB-1.
+// Their samples lie in the buckets px = xs .. xs+CB (px = x0 + 1) of two
+// bucket rows (py = y: the cells are the samples' lower corners, weight b;
+// py = y+1: upper corners, 1-b), i.e. two contiguous runs of records.  A
+// sample of bucket px adds (1-a) of itself to cell px-1 and a to cell px, so
+// each record is read once for the whole block (CB+1 bucket columns instead
+// of 2*CB for single cells).  Per batch every lane reads one record, finds
+// its bucket from the run boundaries and forms the weights of the CB cells;
+// the records' grad_out slices are then read and summed, the next batch's
+// records already in flight.  A level whose blocks expect long runs gives
+// each block gpc groups (interleaved batches), summed through LDS.
+constexpr int CB = 4;
+
 template <int LPC>
 __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C, int LPlog,
                                                       const int* __restrict__ boff, const int4* __restrict__ rec,
                                                       const float* __restrict__ gout, uint32_t gout_bytes,
                                                       float* __restrict__ gvalue)
 {
-    __shared__ float4 stage[256];
-    __shared__ float4 part[256];
+    __shared__ float stage[CB + 1][256];   // per lane: grad_out offset, then the CB weights
+    __shared__ float4 part[CB][256];
     const int b = blockIdx.x;
     int k = 0;
     while (k + 1 < G.L && b >= C.blk_start[k + 1]) ++k;
@@ -519,91 +530,92 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
     const int t = threadIdx.x, grp = t / LPC, j = t - grp * LPC;
     const int slot = grp / gpc, gi = grp - slot * gpc;
     const int Wl = G.W[l];
-    const int cell = (r - pair * wpp) * (256 / (LPC * gpc)) + slot;
-    const bool live = cell < Wl * G.H[l];
-    const int y = live ? cell / Wl : 0, x = live ? cell - y * Wl : 0;
-    // Runs: samples with y0 = y-1 (this cell is their lower corner row), then
-    // y0 = y (upper); within each, x0 = x-1 (right corner) before x0 = x (left).
-    const int* po = boff + (long)pair * (C.Sp + 1) + C.pstart[l] + y * (Wl + 1) + x;
-    const int a0 = po[0], a1 = po[1], a2 = po[2];
-    const int c0 = po[Wl + 1], c1 = po[Wl + 2], c2 = po[Wl + 3];
-    const int n0 = live ? a2 - a0 : 0;
-    const int ntot = live ? n0 + c2 - c0 : 0;
+    const int nbx = (Wl + CB - 1) / CB;
+    const int blk = (r - pair * wpp) * (256 / (LPC * gpc)) + slot;
+    const bool live = blk < nbx * G.H[l];
+    const int y = live ? blk / nbx : 0, xs = live ? (blk - y * nbx) * CB : 0;
+    // run boundaries: bnd[row][i] = first record of bucket px = xs + i (i = 0 .. CB+1,
+    // clamped to the row's end W+1, which is where the next row starts)
+    const int* po = boff + (long)pair * (C.Sp + 1) + C.pstart[l] + y * (Wl + 1);
+    int bu[CB + 2], bl[CB + 2];
+#pragma unroll
+    for (int i = 0; i < CB + 2; ++i) {
+        const int px = min(xs + i, Wl + 1);
+        bu[i] = po[px];
+        bl[i] = po[Wl + 1 + px];
+    }
+    const int n0 = live ? bu[CB + 1] - bu[0] : 0;
+    const int ntot = live ? n0 + bl[CB + 1] - bl[0] : 0;
     const int4* pr = rec + ((long)pair * G.q << LPlog);
     const uint32_t rowb = (uint32_t)G.m * G.dh * 4u;
     const uint32_t gbase = (uint32_t)((long)n * G.q * G.m + h) * (uint32_t)(G.dh * 4) + 16u * j;
     const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)gout, (short)0, (int)gout_bytes,
                                                                         0x00020000);
-    // A batch is 2*LPC run positions: lane j holds positions k0+j and
-    // k0+LPC+j, so 2*LPC grad_out slices are in flight per group.
-    const int step = gpc * 2 * LPC;
-    // record index of run position tt, and whether it lies in the upper run
-    auto where = [&](int tt, bool& upper) {
-        upper = tt < n0;
-        return upper ? a0 + tt : c0 + tt - n0;
-    };
-    auto fetch = [&](int tt, int4& e) {
-        bool up;
-        const int idx = where(tt, up);
-        if (tt < ntot) e = pr[idx];
-    };
-    // (grad_out byte offset, weight) of run position tt with record e
-    auto weigh = [&](int tt, const int4& e, uint32_t& go, float& w) {
-        w = 0.f;
-        go = MS_OOB;   // past the end of grad_out: reads zero
+    const int step = gpc * LPC;
+    auto index = [&](int tt) { return tt < n0 ? bu[0] + tt : bl[0] + tt - n0; };
+    int4 e = make_int4(0, 0, 0, 0);
+    if (gi * LPC + j < ntot) e = pr[index(gi * LPC + j)];
+    float4 acc[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = gi * LPC; k0 < ntot; k0 += step) {   // the same trip count for the whole group
+        const int tt = k0 + j;
+        float w[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) w[c] = 0.f;
+        uint32_t go = MS_OOB;   // past the end of grad_out: reads zero
         if (tt < ntot) {
-            bool upper;
-            const int idx = where(tt, upper);
+            const bool upper = tt < n0;
+            const int idx = index(tt);
+            int kb = 0;   // bucket of the record: px = xs + kb
+#pragma unroll
+            for (int i = 1; i <= CB; ++i) kb += idx >= (upper ? bu[i] : bl[i]);
             const float fa = __int_as_float(e.z), fb = __int_as_float(e.w);
-            const float wx = (upper ? idx < a1 : idx < c1) ? fa : 1.f - fa;
-            const float wy = upper ? fb : 1.f - fb;
-            w = __int_as_float(e.y) * (wx * wy);
+            const float Aw = __int_as_float(e.y) * (upper ? fb : 1.f - fb);
+            const float wl = Aw * (1.f - fa), wr = Aw * fa;   // to cells px-1 and px
+#pragma unroll
+            for (int c = 0; c < CB; ++c) w[c] = c == kb - 1 ? wl : (c == kb ? wr : 0.f);
             go = (uint32_t)e.x * rowb;
         }
-    };
-    int4 e0 = make_int4(0, 0, 0, 0), e1 = e0;
-    fetch(gi * 2 * LPC + j, e0);
-    fetch(gi * 2 * LPC + LPC + j, e1);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = gi * 2 * LPC; k0 < ntot; k0 += step) {   // the same trip count for the whole group
-        float4 sw;
-        uint32_t go0, go1;
-        weigh(k0 + j, e0, go0, sw.y);
-        weigh(k0 + LPC + j, e1, go1, sw.w);
-        sw.x = __uint_as_float(go0);
-        sw.z = __uint_as_float(go1);
-        fetch(k0 + step + j, e0);
-        fetch(k0 + step + LPC + j, e1);
-        stage[t] = sw;
+        if (tt + step < ntot) e = pr[index(tt + step)];
+        stage[0][t] = __uint_as_float(go);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) stage[c + 1][t] = w[c];
         wave_lds_sync();
 #pragma unroll
         for (int u = 0; u < LPC; ++u) {
-            const float4 p = stage[grp * LPC + u];
-            const uint32_t o0 = __float_as_uint(p.x), o1 = __float_as_uint(p.z);
-            const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(gr, o0 == MS_OOB ? o0 : o0 + gbase, 0, 0);
-            const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(gr, o1 == MS_OOB ? o1 : o1 + gbase, 0, 0);
-            acc.x = fmaf(p.y, __uint_as_float(v0.x), acc.x);
-            acc.y = fmaf(p.y, __uint_as_float(v0.y), acc.y);
-            acc.z = fmaf(p.y, __uint_as_float(v0.z), acc.z);
-            acc.w = fmaf(p.y, __uint_as_float(v0.w), acc.w);
-            acc.x = fmaf(p.w, __uint_as_float(v1.x), acc.x);
-            acc.y = fmaf(p.w, __uint_as_float(v1.y), acc.y);
-            acc.z = fmaf(p.w, __uint_as_float(v1.z), acc.z);
-            acc.w = fmaf(p.w, __uint_as_float(v1.w), acc.w);
+            const int src = grp * LPC + u;
+            const uint32_t o = __float_as_uint(stage[0][src]);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, o == MS_OOB ? o : o + gbase, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const float ww = stage[c + 1][src];
+                acc[c].x = fmaf(ww, __uint_as_float(v.x), acc[c].x);
+                acc[c].y = fmaf(ww, __uint_as_float(v.y), acc[c].y);
+                acc[c].z = fmaf(ww, __uint_as_float(v.z), acc[c].z);
+                acc[c].w = fmaf(ww, __uint_as_float(v.w), acc[c].w);
+            }
         }
         wave_lds_sync();
     }
     if (gpc > 1) {   // uniform over the workgroup
-        part[t] = acc;
+#pragma unroll
+        for (int c = 0; c < CB; ++c) part[c][t] = acc[c];
         __syncthreads();
         if (gi == 0)
-            for (int u = 1; u < gpc; ++u) {
-                const float4 p = part[t + u * LPC];
-                acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
-            }
+            for (int u = 1; u < gpc; ++u)
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    const float4 p = part[c][t + u * LPC];
+                    acc[c].x += p.x; acc[c].y += p.y; acc[c].z += p.z; acc[c].w += p.w;
+                }
     }
-    if (live && gi == 0)
-        *reinterpret_cast<float4*>(gvalue + (((long)n * G.S + G.start[l] + cell) * G.m + h) * G.dh + 4 * j) = acc;
+    if (live && gi == 0) {
+        float* dst = gvalue + (((long)n * G.S + G.start[l] + (long)y * Wl + xs) * G.m + h) * G.dh + 4 * j;
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            if (xs + c < Wl) *reinterpret_cast<float4*>(dst + (long)c * G.m * G.dh) = acc[c];
+    }
 }
 
 // Queries per workgroup of the tiled kernel: 256 lanes of V channels, at most
@@ -654,14 +666,17 @@ bool sort_layout(const MsdaGeom& G, MsdaSortCfg* C, SortWs* W)
     for (int k = 0; k < G.L; ++k) {
         const int l = G.L - 1 - k;
         C->blk_start[k] = (int)blk;
-        // Records a cell of this level expects if the samples spread evenly
-        // (len_q * points samples per pair land on the level, 4 corners each).
-        const double expect = 4.0 * G.q * G.P / ((double)G.H[l] * G.W[l]);
+        // Records a block of CB cells of this level reads if the samples
+        // spread evenly: len_q * points samples per pair land on the level,
+        // one record each in a bucket, and a block reads CB+1 of its row's
+        // bucket columns in two bucket rows.
+        const double expect = 2.0 * G.q * G.P * (CB + 1) / ((double)(G.H[l] + 1) * (G.W[l] + 1));
         int gpc = 1;
         while (gpc < 256 / lpc && expect > 64.0 * gpc) gpc *= 2;   // about 64 records a group
         C->gpc[l] = gpc;
-        const int cpw = 256 / (lpc * gpc);
-        C->wg_per_pair[l] = (int)(((long)G.H[l] * G.W[l] + cpw - 1) / cpw);
+        const int bpw = 256 / (lpc * gpc);   // blocks per workgroup
+        const long blocks = (long)G.H[l] * ((G.W[l] + CB - 1) / CB);
+        C->wg_per_pair[l] = (int)((blocks + bpw - 1) / bpw);
         blk += (pairs * C->wg_per_pair[l] + 7) & ~7L;
         if (blk >= (1L << 31)) return false;
     }
