@@ -526,10 +526,12 @@ def main():
         secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
-        r = msda_bwd_runner(torch)
-        secondary[r.name] = summarize(r, time_steps(torch, r, 20, 3), kernel_ms(torch, r, 20))
-        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
-        del r
+        for gather in (True, False):
+            r = msda_bwd_runner(torch, gather=gather)
+            k = 20 if gather else 5
+            secondary[r.name] = summarize(r, time_steps(torch, r, k, 2), kernel_ms(torch, r, k))
+            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+            del r
         torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
