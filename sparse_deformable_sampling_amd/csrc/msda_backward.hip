@@ -409,9 +409,10 @@ __global__ __launch_bounds__(256) void msda_bwd_count(MsdaGeom G, MsdaSortCfg C,
 // the global one with a single atomic (which returns the workgroup's base),
 // and writes base + local rank.  Queries that are neighbours in the map
 // share coarse-level buckets, so this replaces most global atomics on
-// crowded addresses by LDS ones.  LDS: Sp ints.
-constexpr int CQ_SPT = 16;                  // samples per thread
+// crowded addresses by LDS ones.  LDS: Sp ints (Sp < 2^15).
+constexpr int CQ_SPT = 8;                   // samples per thread
 constexpr int CQ_SAMPLES = 1024 * CQ_SPT;   // samples per workgroup
+static_assert(CQ_SAMPLES <= (1 << 15), "local ranks are packed into 15 bits");
 
 __global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortCfg C, int LPlog, int chunks,
                                                            const float* __restrict__ loc, int* __restrict__ cnt,
@@ -424,13 +425,13 @@ __global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortC
     for (int b = t; b < C.Sp; b += 1024) lc[b] = 0;
     __syncthreads();
     const int LP = 1 << LPlog;
-    int bk[CQ_SPT], lr[CQ_SPT];
+    // bucket * 2^15 + local rank, or -1: Sp < 2^15 (LDS) and ranks < CQ_SAMPLES <= 2^15
+    int br[CQ_SPT];
 #pragma unroll
     for (int k = 0; k < CQ_SPT; ++k) {
         const int sl = ck * CQ_SAMPLES + k * 1024 + t;
         const int q = sl >> LPlog, i = sl & (LP - 1);
-        bk[k] = -1;
-        lr[k] = 0;
+        br[k] = -1;
         if (q < G.q) {
             const int l = i / G.P;
             const long gs = (((long)n * G.q + q) * G.m + h) * LP + i;
@@ -438,8 +439,8 @@ __global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortC
             int x0, y0;
             float fa, fb;
             if (msda_corner(uv, G.W[l], G.H[l], x0, y0, fa, fb)) {
-                bk[k] = C.pstart[l] + (y0 + 1) * (G.W[l] + 1) + x0 + 1;
-                lr[k] = atomicAdd(lc + bk[k], 1);
+                const int bk = C.pstart[l] + (y0 + 1) * (G.W[l] + 1) + x0 + 1;
+                br[k] = (bk << 15) | atomicAdd(lc + bk, 1);
             }
         }
     }
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortC
     for (int k = 0; k < CQ_SPT; ++k) {
         const int sl = ck * CQ_SAMPLES + k * 1024 + t;
         const int q = sl >> LPlog, i = sl & (LP - 1);
-        if (q < G.q) rank[(((long)n * G.q + q) * G.m + h) * LP + i] = bk[k] >= 0 ? lc[bk[k]] + lr[k] : -1;
+        if (q < G.q) rank[(((long)n * G.q + q) * G.m + h) * LP + i] = br[k] >= 0 ? lc[br[k] >> 15] + (br[k] & 0x7fff) : -1;
     }
 }
 
@@ -736,7 +737,8 @@ hipError_t launch_msda_backward(const MsdaGeom& G, const float* value, const flo
             device_limits(&lds_limit, &num_cus);
             const int lds = C.Sp * 4;
             const long chunks = (((long)G.q << LPlog) + CQ_SAMPLES - 1) / CQ_SAMPLES;
-            if (lds <= std::min(lds_limit, 96 * 1024) && (long)G.n * G.m * chunks < (1L << 31) &&
+            // the packed (bucket, rank) of the LDS count needs Sp < 2^15
+            if (C.Sp < (1 << 15) && lds <= std::min(lds_limit, 96 * 1024) && (long)G.n * G.m * chunks < (1L << 31) &&
                 hipFuncSetAttribute((const void*)msda_bwd_count_lds, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds) == hipSuccess) {
                 msda_bwd_count_lds<<<dim3((unsigned)(G.n * G.m * chunks)), dim3(1024), lds, s>>>(

@@ -599,6 +599,19 @@ def test_msda_backward_shapes(sds, n, shapes, q, heads, dh, points):
         check_msda_bwd(sds, "msda-bwd", n, shapes, q, heads, dh, points, softmax=softmax, seed=53, offset_std=3.0)
 
 
+@pytest.mark.parametrize("dh,q,shapes", [
+    (4, 700, [(5, 9), (2, 3)]),       # one lane per cell block; 64 groups per block on the 2x3 level
+    (8, 600, [(6, 5), (1, 1)]),       # a 1x1 level: every sample shares the four buckets around it
+    (16, 900, [(5, 4), (2, 2)]),
+    (64, 500, [(7, 6), (3, 2)]),      # 16 lanes per block, up to 16 groups per block
+])
+def test_msda_backward_gather_many_samples_per_cell(sds, dh, q, shapes):
+    """Gather path with head_dim 4..64 and levels small enough that a block
+    of cells is split over several lane groups (summed through LDS), against
+    the oracle and the atomic scatter."""
+    check_msda_bwd(sds, "msda-bwd-split", 2, shapes, q, 2, dh, 2, softmax=True, seed=67, offset_std=1.0)
+
+
 def test_msda_backward_crowded_cells(sds):
     """Every sample of an (image, head) pair in one bucket per level: the
     gather's runs are thousands of records long (len_q * points per level),
