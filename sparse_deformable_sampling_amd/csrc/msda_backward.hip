@@ -58,7 +58,9 @@ namespace dcn {
 namespace {
 
 constexpr uint32_t MS_OOB = 0x80000000u;
-constexpr int MS_REC_MAX = 1024;
+// Sample records per workgroup of the tiled kernel: up to 512 (16 KB of LDS),
+// more only where one query's samples need it (see tile_queries).
+constexpr int MS_REC_MAX = 512;
 
 // Buckets of the value-gradient gather (see above).
 struct MsdaSortCfg {
@@ -139,8 +141,10 @@ __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int 
                                                      MsdaSortCfg C, const int* __restrict__ boff,
                                                      const int* __restrict__ rank, int4* __restrict__ rec)
 {
-    __shared__ u32x4 rec_o[MS_REC_MAX];
-    __shared__ float4 rec_f[MS_REC_MAX];
+    // LDS: QT*LP corner offsets, then QT*LP (a, b, A) / gradient records
+    extern __shared__ __align__(16) unsigned char lds[];
+    u32x4* rec_o = reinterpret_cast<u32x4*>(lds);
+    float4* rec_f = reinterpret_cast<float4*>(lds + (size_t)(QT << LPlog) * 16);
     const int nwg_pad = (nwg + 7) & ~7;
     const int b = blockIdx.x;
     const int L = (b & 7) * (nwg_pad >> 3) + (b >> 3);
@@ -215,9 +219,9 @@ __global__ __launch_bounds__(256) void msda_bwd_tile(MsdaGeom G, int LPlog, int 
         const int r0 = (live ? qi : 0) << LPlog;
         // Lanes of a query that is past the end still take part in the
         // reductions (with g = 0) and write nothing.  The corners of U
-        // samples are loaded before any is used (U = 4 for the gather, whose
+        // samples are loaded before any is used (U = 2 for the gather, whose
         // loop is otherwise latency-bound; the scatter is bound by its atomics).
-        constexpr int U = V == 4 ? 4 : 1;
+        constexpr int U = V == 4 ? 2 : 1;
         for (int i0 = 0; i0 < LP; i0 += U) {
             float vv[U][4][V];
             float4 ff[U];
@@ -619,11 +623,16 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
     }
 }
 
-// Queries per workgroup of the tiled kernel: 256 lanes of V channels, at most
-// MS_REC_MAX sample records.
+// Queries per workgroup of the tiled kernel: at most 256 lanes of V channels
+// and MS_REC_MAX sample records, but at least one query's samples per thread
+// row (the softmax shuffles of phases 1 and 3 span them): up to 1024 records
+// at 32 samples per head.
 int tile_queries(const MsdaGeom& G, int V)
 {
-    return std::min(256 / (G.dh / V), MS_REC_MAX / (G.L * G.P));
+    const int LP = G.L * G.P, LPQ = G.dh / V;
+    int QT = std::min(256 / LPQ, MS_REC_MAX / LP);
+    if (QT * LPQ < LP) QT = LP / LPQ;
+    return QT;
 }
 
 // Shapes the tiled kernel takes (LPlog, Dlog filled in).
@@ -759,9 +768,10 @@ hipError_t launch_msda_backward(const MsdaGeom& G, const float* value, const flo
         const long nwg = (long)G.n * G.m * tiles;
         const dim3 grid((unsigned)((nwg + 7) & ~7L)), blk((unsigned)(QT * G.dh / V));
         float* gv_tile = sorted ? nullptr : gvalue;
-#define MS_TILE(SM, SO, VV)                                                                                      \
-    msda_bwd_tile<SM, SO, VV><<<grid, blk, 0, s>>>(G, LPlog, Dlog, QT, tiles, (int)nwg, (uint32_t)value_bytes, \
-                                                   value, loc, attn, gout, gv_tile, gloc, gattn, C, boff, rank, rec)
+        const size_t lds = (size_t)QT * G.L * G.P * 32;
+#define MS_TILE(SM, SO, VV)                                                                                        \
+    msda_bwd_tile<SM, SO, VV><<<grid, blk, lds, s>>>(G, LPlog, Dlog, QT, tiles, (int)nwg, (uint32_t)value_bytes, \
+                                                     value, loc, attn, gout, gv_tile, gloc, gattn, C, boff, rank, rec)
         if (G.softmax) {
             if (sorted) MS_TILE(true, true, 4);
             else MS_TILE(true, false, 1);
