@@ -738,3 +738,53 @@ def test_frontend_feeds_the_core(sds, dtype):
     err = rel_err(to_host(out), ref)
     say("  err chain core", dtype, "%.3e" % err)
     assert err <= TOL[dtype]
+
+
+# ---------------------------------------------------------------- streams
+
+
+def test_ops_follow_the_current_stream(sds):
+    """Every wrapper enqueues on torch's current stream.  Inputs are produced
+    on a side stream (of default priority), the ops run on it, and only that
+    stream is waited for: a kernel launched elsewhere would race the copies.
+    Results must equal those of the default stream (the forward bit for bit,
+    the backward within the bars, its atomics being order-dependent)."""
+    import torch
+    n, h, w, c, g = 4, 20, 24, 64, 4
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f16", seed=71)
+    fe = synth.frontend_inputs(n, h, w, c, g, dtype="f16", seed=72)
+    go = synth.store(np.random.default_rng(73).standard_normal((n, h, w, c)).astype(np.float32), "f16")
+    shapes = [(12, 10), (6, 5)]
+    m = synth.msda_inputs(2, shapes, 150, 4, 32, 4, seed=74)
+    mg = np.random.default_rng(75).standard_normal((2, 150, 4, 32)).astype(np.float32)
+    base = {k: to_dev(d[k], "f16") for k in ("x", "offset", "mask")}
+    base.update({"go": to_dev(go, "f16"), "v": to_dev(m["value"], "f32"), "loc": to_dev(m["loc"], "f32"),
+                 "attn": to_dev(m["attn"], "f32"), "mg": to_dev(mg, "f32")})
+    base.update({"fe_" + k: to_dev(fe[k], "f16") for k in FRONT_KEYS})
+    torch.cuda.synchronize()
+
+    def run(t):
+        out = {"fwd": sds.dcn_forward(t["x"], t["offset"], t["mask"], group=g)}
+        out["bwd"] = sds.dcn_backward(t["x"], t["offset"], t["mask"], t["go"], group=g)
+        out["om"] = sds.dcnv4_offset_mask(*(t["fe_" + k] for k in FRONT_KEYS), group=g)
+        out["msda"] = sds.msda_forward(t["v"], shapes, t["loc"], t["attn"])
+        out["msda_bwd"] = sds.msda_backward(t["v"], shapes, t["loc"], t["attn"], t["mg"])
+        return out
+
+    say("streams: default")
+    ref = run(base)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say("streams: side")
+    with torch.cuda.stream(side):
+        for _ in range(3):   # repeat: a race would show on some pass
+            t = {k: v.clone() for k, v in base.items()}
+            got = run(t)
+            side.synchronize()
+            assert torch.equal(got["fwd"], ref["fwd"])
+            assert torch.equal(got["om"][0], ref["om"][0]) and torch.equal(got["om"][1], ref["om"][1])
+            assert torch.equal(got["msda"], ref["msda"])
+            for a, b in zip(got["bwd"], ref["bwd"]):
+                assert rel_err(to_host(a), to_host(b)) <= TOL["f16"]
+            for a, b in zip(got["msda_bwd"], ref["msda_bwd"]):
+                assert rel_err(to_host(a), to_host(b)) <= 1e-5
