@@ -448,8 +448,8 @@ def cpu_baseline_threads(seconds, max_threads=16):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the operator shards "
-              "over the batch with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (the operator would "
+              "shard over the batch with no exchange between GPUs)", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
