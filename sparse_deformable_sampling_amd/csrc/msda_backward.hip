@@ -464,11 +464,21 @@ __global__ __launch_bounds__(1024) void msda_bwd_count_lds(MsdaGeom G, MsdaSortC
 }
 
 // In-place exclusive prefix sum of `len` counts per pair, one workgroup of
-// 1024 threads per pair, each thread over a contiguous run.
+// 1024 threads per pair, each thread over a contiguous run.  STAGED: the
+// pair's counts pass through LDS (len ints), so that global memory is read
+// and written with coalesced accesses.
+template <bool STAGED>
 __global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int len)
 {
     __shared__ int wsum[16];
-    int* p = cnt + (long)blockIdx.x * len;
+    extern __shared__ int stg[];
+    int* g = cnt + (long)blockIdx.x * len;
+    int* p = g;
+    if constexpr (STAGED) {
+        for (int i = threadIdx.x; i < len; i += 1024) stg[i] = g[i];
+        __syncthreads();
+        p = stg;
+    }
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int per = (len + 1023) / 1024;
     const int lo = min(len, t * per), hi = min(len, lo + per);
@@ -495,6 +505,10 @@ __global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int
         const int c = p[i];
         p[i] = run;
         run += c;
+    }
+    if constexpr (STAGED) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < len; i += 1024) g[i] = stg[i];
     }
 }
 
@@ -757,7 +771,13 @@ hipError_t launch_msda_backward(const MsdaGeom& G, const float* value, const flo
                 msda_bwd_count<<<dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s>>>(G, C, LPlog, loc, boff,
                                                                                          rank);
             }
-            msda_bwd_scan<<<dim3((unsigned)(G.n * G.m)), dim3(1024), 0, s>>>(boff, C.Sp + 1);
+            const int scan_lds = (C.Sp + 1) * 4;
+            if (scan_lds <= std::min(lds_limit, 128 * 1024) &&
+                hipFuncSetAttribute((const void*)msda_bwd_scan<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    scan_lds) == hipSuccess)
+                msda_bwd_scan<true><<<dim3((unsigned)(G.n * G.m)), dim3(1024), scan_lds, s>>>(boff, C.Sp + 1);
+            else
+                msda_bwd_scan<false><<<dim3((unsigned)(G.n * G.m)), dim3(1024), 0, s>>>(boff, C.Sp + 1);
         } else if (gvalue) {
             fill_zero_f32<<<dim3((unsigned)std::min((vcount / 4 + 255) / 256 + 1, 65536L)), dim3(256), 0, s>>>(
                 gvalue, vcount);
