@@ -51,11 +51,16 @@ __device__ __forceinline__ float lane_sum(float v, int width)
     return v;
 }
 
-// Fixed-point image of t (|t| < 2^31): t rounded to the nearest integer, as
-// a two's-complement 64-bit integer.
+// Fixed-point image of t (|t| < 2^30): t rounded to a nearest integer (ties
+// up; within one unit where t + 1/2 is not exact), as a two's-complement
+// 64-bit integer.  One conversion instruction, floor(t + 1/2) to int32, where
+// rounding and converting separately take two; the compiler does not form it
+// from C, hence the one-instruction VALU asm (no memory access).
 __device__ __forceinline__ unsigned long long to_fixed(float t)
 {
-    return (unsigned long long)(long long)(int)__builtin_rintf(t);
+    int r;
+    asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(t));
+    return (unsigned long long)(long long)r;
 }
 
 // Widen N consecutive storage-type values (N * sizeof(T) a multiple of 8
