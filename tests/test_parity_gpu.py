@@ -788,3 +788,39 @@ def test_ops_follow_the_current_stream(sds):
                 assert rel_err(to_host(a), to_host(b)) <= TOL["f16"]
             for a, b in zip(got["msda_bwd"], ref["msda_bwd"]):
                 assert rel_err(to_host(a), to_host(b)) <= 1e-5
+
+
+def test_msda_backward_ws_reused_workspace(sds):
+    """One caller-owned workspace serves two msda_backward_ws calls in a row,
+    the second on a smaller problem: counts and records left by the first
+    must not leak into the second.  Both match the atomic scatter."""
+    import ctypes
+    import torch
+    from sparse_deformable_sampling_amd import _binding as B
+    L = B.lib()
+    cases = [(2, [(9, 11), (5, 6), (3, 3), (2, 2)], 300, 4, 32, 4, 81), (1, [(6, 7), (3, 4)], 90, 2, 16, 2, 82)]
+    sizes = []
+    for n, shapes, q, heads, dh, pts, _ in cases:
+        desc = B.MsdaDesc(n, q, heads, dh, len(shapes), pts, 1, B.DCN_F32)
+        shp = (ctypes.c_int32 * (2 * len(shapes)))(*[v for hw in shapes for v in hw])
+        nb = ctypes.c_size_t(0)
+        assert L.msda_backward_workspace_size(ctypes.byref(desc), shp, ctypes.byref(nb)) == B.DCN_OK
+        sizes.append(nb.value)
+    assert sizes[0] > sizes[1] > 0
+    ws = torch.empty((sizes[0],), dtype=torch.uint8, device="cuda")
+    for n, shapes, q, heads, dh, pts, seed in cases:
+        d = synth.msda_inputs(n, shapes, q, heads, dh, pts, seed=seed)
+        g = np.random.default_rng(seed).standard_normal((n, q, heads, dh)).astype(np.float32)
+        v, lc, at, go = (to_dev(a, "f32") for a in (d["value"], d["loc"], d["attn"], g))
+        desc = B.MsdaDesc(n, q, heads, dh, len(shapes), pts, 1, B.DCN_F32)
+        shp = (ctypes.c_int32 * (2 * len(shapes)))(*[x for hw in shapes for x in hw])
+        out = [torch.empty_like(v), torch.empty_like(lc), torch.empty_like(at)]
+        say("msda-bwd-ws-reuse", (n, shapes, q, heads, dh, pts))
+        st = L.msda_backward_ws(ctypes.byref(desc), shp, *(ctypes.c_void_p(t.data_ptr()) for t in (v, lc, at, go)),
+                                *(ctypes.c_void_p(t.data_ptr()) for t in out), ctypes.c_void_p(ws.data_ptr()),
+                                ctypes.c_size_t(sizes[0]), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == B.DCN_OK
+        ref = sds.msda_backward(v, shapes, lc, at, go, gather=False)
+        torch.cuda.synchronize()
+        for a, b, tol in zip(out, ref, MSDA_BWD_TOL):
+            assert rel_err(to_host(a), to_host(b)) <= tol
