@@ -37,9 +37,14 @@
 //    (x0, y0 >= -1 for a sample inside the level's extended range).  Cell
 //    (x, y) is a corner of the samples of buckets x0 in {x-1, x}, y0 in
 //    {y-1, y}: two runs of two adjacent buckets, contiguous in bucket order.
-//  - msda_bwd_count: one thread per sample, atomic count per bucket; the
-//    returned count is the sample's rank within its bucket.
-//  - msda_bwd_scan: exclusive prefix sum of the counts, one workgroup per pair.
+//  - msda_bwd_count_lds: a workgroup counts 8192 samples of one pair per
+//    bucket in LDS (the returned count is the rank among them), then adds
+//    each nonzero count to the pair's global count with one atomic, whose
+//    return is the workgroup's base; a sample's rank is base + local rank.
+//    msda_bwd_count, one global atomic per sample, serves pairs whose
+//    buckets do not fit in LDS.
+//  - msda_bwd_scan: exclusive prefix sum of the counts, one workgroup per
+//    pair, through LDS where the pair's counts fit.
 //  - the tiled kernel writes each sample's record (query, A, a, b) at
 //    offset + rank, alongside grad_loc and grad_attn.
 //  - msda_bwd_cells: a group of head_dim/4 lanes per block of 4 adjacent
