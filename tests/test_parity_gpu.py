@@ -591,6 +591,7 @@ def test_msda_backward_encoder_full(sds, softmax, ref):
     (2, [(9, 7), (5, 4)], 50, 5, 64, 2),         # tiled: 64 lanes per query
     (1, [(4, 4)], 9, 1, 1, 32),                  # tiled: one channel, 32 samples
     (3, [(7, 6), (4, 3), (2, 2), (1, 1)], 45, 2, 16, 8),
+    (1, [(5, 4), (3, 3)], 60, 2, 4, 16),         # 32 samples, one lane per query: 32 queries per workgroup
     (2, [(7, 9), (4, 5)], 23, 3, 36, 3),         # generic: 6 samples, head_dim 36
     (2, [(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 17, 2, 8, 2),   # generic: 10 samples
 ])
