@@ -825,3 +825,23 @@ def test_msda_backward_ws_reused_workspace(sds):
         torch.cuda.synchronize()
         for a, b, tol in zip(out, ref, MSDA_BWD_TOL):
             assert rel_err(to_host(a), to_host(b)) <= tol
+
+
+# ---------------------------------------------------------------- very wide rows
+
+
+@pytest.mark.parametrize("w", [1200, 3000])
+def test_very_wide_rows(sds, w):
+    """Rows thousands of pixels wide: the forward's LDS ring then holds fewer
+    groups (or no window at all, and the direct gather runs), the backward's
+    fixed-point window fewer rows, and the front-end's sliding window walks
+    a long row.  Forward f32/f16/bf16 with both modulations, backward f32 and
+    f16, front-end f16/bf16, all against the oracle."""
+    n, h, c, g = 1, 6, 64, 4
+    for dtype in ("f32", "f16", "bf16"):
+        for softmax in (False, True):
+            check_fwd(sds, "very-wide", n, h, w, c, g, dtype, softmax, seed=91)
+    for dtype in ("f32", "f16"):
+        check_bwd(sds, "bwd-very-wide", n, h, w, c, g, False, seed=92, dtype=dtype)
+    for dtype in ("f16", "bf16"):
+        check_frontend(sds, "frontend-very-wide", n, h, w, c, g, dtype, seed=93)
