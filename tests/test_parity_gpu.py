@@ -75,10 +75,12 @@ def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("c,g", [(4, 4), (12, 4), (15, 3), (16, 2), (32, 1), (64, 1), (256, 2), (24, 3)])
+@pytest.mark.parametrize("c,g", [(4, 4), (12, 4), (15, 3), (16, 2), (32, 1), (64, 1), (256, 2), (24, 3), (512, 1),
+                                 (1024, 2)])
 def test_channel_splits(sds, dtype, c, g):
     """Every D = C/G path: one channel, odd D, D not a multiple of the vector
-    width, vector widths exactly, several vectors per item."""
+    width, vector widths exactly, several vectors per item, and groups of 512
+    channels (split into up to 32 lane items of 64 bytes)."""
     for softmax in (False, True):
         check_fwd(sds, "split", 2, 9, 11, c, g, dtype, softmax, seed=3)
 
@@ -327,7 +329,7 @@ def test_backward_crop_against_finite_differences(sds, softmax):
         assert gx[ix] == pytest.approx(fd, rel=1e-4, abs=1e-4)
 
 
-@pytest.mark.parametrize("c,g", [(16, 4), (12, 4), (15, 3), (32, 1), (256, 2), (8, 8), (48, 2)])
+@pytest.mark.parametrize("c,g", [(16, 4), (12, 4), (15, 3), (32, 1), (256, 2), (8, 8), (48, 2), (512, 1)])
 def test_backward_channel_splits(sds, c, g):
     for softmax in (False, True):
         check_bwd(sds, "bwd-split", 2, 9, 11, c, g, softmax, seed=29)
