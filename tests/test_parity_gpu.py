@@ -487,7 +487,11 @@ def test_msda_mid_size(sds, q, dh, points, softmax, ref):
     check_msda(sds, "msda-mid", 2, MID_SHAPES, q, 8, dh, points, softmax=softmax, seed=43, ref=ref)
 
 
-@pytest.mark.parametrize("shapes,points", [([(1, 1)], 1), ([(5, 3)], 8), ([(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 2)])
+SIXTEEN_LEVELS = [(i % 5 + 1, i % 3 + 2) for i in range(16)]   # the most levels the library takes
+
+
+@pytest.mark.parametrize("shapes,points", [([(1, 1)], 1), ([(5, 3)], 8), ([(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 2),
+                                           (SIXTEEN_LEVELS, 2)])
 def test_msda_levels_points(sds, shapes, points):
     for softmax in (True, False):
         check_msda(sds, "msda-lp", 2, shapes, 17, 2, 8, points, softmax=softmax, seed=43, offset_std=4.0)
@@ -594,6 +598,7 @@ def test_msda_backward_encoder_full(sds, softmax, ref):
     (1, [(4, 4)], 9, 1, 1, 32),                  # tiled: one channel, 32 samples
     (3, [(7, 6), (4, 3), (2, 2), (1, 1)], 45, 2, 16, 8),
     (1, [(5, 4), (3, 3)], 60, 2, 4, 16),         # 32 samples, one lane per query: 32 queries per workgroup
+    (2, [(i % 5 + 1, i % 3 + 2) for i in range(16)], 40, 2, 8, 1),   # 16 levels, one point each
     (2, [(7, 9), (4, 5)], 23, 3, 36, 3),         # generic: 6 samples, head_dim 36
     (2, [(9, 7), (5, 4), (3, 2), (2, 1), (1, 1)], 17, 2, 8, 2),   # generic: 10 samples
 ])
