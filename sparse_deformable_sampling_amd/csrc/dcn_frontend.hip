@@ -23,13 +23,14 @@
 //  - dcn_offset_mask_wave (C up to 256, C/8 dividing 64): W_om in LDS once
 //    per workgroup, then each wave alone on its own 16-pixel blocks (see the
 //    comment above it);
-//  - dcn_offset_mask_k, the tile kernel for the other C: a workgroup of four
+//  - dcn_offset_mask_k, the tile kernel for the other C: a workgroup of eight
 //    waves takes TM = 16, 32 or 64 pixels, computes their depthwise 3x3 (a
 //    thread per (pixel, 8 channels), 16-byte loads, fp32 sums, d rounded
 //    once to the storage type) into an LDS tile A[TM][C] (rows C+8 elements
 //    apart, so that the 16 rows one operand read touches fall on distinct
-//    banks), and wave w takes the 16-output blocks w, w+4, ..., reading
-//    the weight rows straight from L2.
+//    banks), and wave w takes the 16-output blocks w, w+8, ..., reading
+//    the weight rows straight from L2 (eight waves, not four, so that fewer
+//    blocks wait on those reads one after another).
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -40,7 +41,7 @@ namespace dcn {
 
 namespace {
 
-constexpr int FT_THREADS = 256;
+constexpr int FT_THREADS = 512;
 constexpr int FT_LDS_TARGET = 80 * 1024;   // two workgroups per CU
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
@@ -82,7 +83,7 @@ struct FrontCfg {
     int lds_bytes;
     int mb;          // 16-pixel blocks per tile (TM = 16 * mb)
     int c8;          // 8-channel groups per row of A (KP / 8)
-    int dp, dc;      // item step of a thread: 256 = dp * c8 + dc
+    int dp, dc;      // item step of a thread: FT_THREADS = dp * c8 + dc
     uint32_t x_bytes;
     FastDiv div_w, div_h;
 };
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     const int npx = min(TM, F.npix - px0);
 
     // ---- depthwise 3x3 into A.  A thread's items are (pixel p, channels
-    // 8*cg..) for e = tid, tid + 256, ...; rows past the last pixel and
+    // 8*cg..) for e = tid, tid + FT_THREADS, ...; rows past the last pixel and
     // channels past C are written as zeros.  A neighbour outside the image
     // reads through an out-of-range buffer offset, which returns zeros.
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)F.x_bytes, 0x00020000);
@@ -210,12 +211,12 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     __syncthreads();
 
     // ---- NO x TM product om^T = W_om d^T: wave w takes output blocks w,
-    // w+4, ...; the A operand is 16 weight rows, the B operand 16 pixels of d.
+    // w+8, ...; the A operand is 16 weight rows, the B operand 16 pixels of d.
     // Lane l then holds outputs j0..j0+3 (j0 = 16*cb + 4*(l/16)) of pixel
     // 16*rb + l%16.
     const int kg = 8 * (lane >> 4);
     const bool quad = (NMASK & 3) == 0;   // 4 consecutive outputs of a pixel are 8-byte aligned in LDS
-    for (int cb = wave; cb < F.ncb; cb += 4) {
+    for (int cb = wave; cb < F.ncb; cb += FT_THREADS / 64) {
         const T* wrow = omw + (long)min(cb * 16 + (lane & 15), F.NO - 1) * C;   // rows past NO compute a copy, not stored
         f4_t acc[MB];
 #pragma unroll
