@@ -301,46 +301,50 @@ def msda_bwd_runner(torch, gather=True, seed=1):
 
 def time_steps(torch, r, steps, warmup):
     """Contract timing: warmup, then exactly `steps` launches bracketed by
-    synchronisation.  Returns wall ms per step."""
+    synchronisation.  One HIP event pair, recorded on the launch stream
+    around the same `steps` launches, gives the kernel's average launch
+    duration over the timed region, so the roofline describes the run the
+    headline rate comes from (and kernel time <= step time).
+    Returns (wall ms per step, event ms per launch)."""
     for i in range(warmup):
         r.launch(i)
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record(r.stream)
     for i in range(steps):
         r.launch(warmup + i)
+    b.record(r.stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, a.elapsed_time(b) / steps
 
 
-def kernel_ms(torch, r, steps):
-    """Launch durations from HIP events recorded on the launch stream.
-
-    The mean is one event pair around `steps` back-to-back launches divided by
-    `steps` (what the kernel sustains, the figure the roofline uses); the
-    median and percentiles come from a second pass with an event pair around
-    each launch, which also carries the event and dispatch latency."""
-    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(r.stream)
-    for i in range(steps):
-        r.launch(i)
-    b0.record(r.stream)
+def launch_spread(torch, r, steps):
+    """Median, p10 and p90 of single launches, each between its own event
+    pair on the launch stream (a separate pass after the timed region; each
+    figure also carries the event and dispatch latency of one launch)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(evs):
         a.record(r.stream)
         r.launch(i)
         b.record(r.stream)
     torch.cuda.synchronize()
-    mean = a0.elapsed_time(b0) / steps
     d = np.array([a.elapsed_time(b) for a, b in evs])
-    return float(mean), float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+    return float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+
+def measure(torch, r, steps, warmup):
+    ms_step, mean = time_steps(torch, r, steps, warmup)
+    return summarize(r, ms_step, (mean,) + launch_spread(torch, r, steps))
 
 
 def summarize(r, ms_step, kms):
     mean, med, p10, p90 = kms
     gbs = r.min_bytes / (mean * 1e-3) / 1e9
     return {"ms_per_step": round(ms_step, 5), "kernel_us_mean": round(mean * 1e3, 2),
-            "kernel_us_median": round(med * 1e3, 2), "kernel_us_p10": round(p10 * 1e3, 2),
-            "kernel_us_p90": round(p90 * 1e3, 2), "min_bytes": int(r.min_bytes),
+            "kernel_us_median_single": round(med * 1e3, 2), "kernel_us_p10_single": round(p10 * 1e3, 2),
+            "kernel_us_p90_single": round(p90 * 1e3, 2), "min_bytes": int(r.min_bytes),
             "gtaps_ch_per_s": round(r.units / (ms_step * 1e-3) / 1e9, 2),
             "achieved_gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
@@ -351,6 +355,7 @@ COPY_CALIB_BYTES = 256 << 20
 # is reported only while their hash matches the one recorded with it.
 HEADLINE_KERNEL_SOURCES = ["dcn_forward_ring.hip", "dcn_ring.h", "dcn_device.h", "dcn_launch.h"]
 HEADLINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dcn_fwd_ring_f16_stage1_traffic.txt")
+HEADLINE_KERNEL = "dcn_fwd_ring (f16, 3x3, DCNv4)"
 
 
 def kernel_source_hash(files=HEADLINE_KERNEL_SOURCES):
@@ -362,22 +367,26 @@ def kernel_source_hash(files=HEADLINE_KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the headline kernel from the committed
-    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
-    counter reads for a plain copy of known size), or None when there is no
-    summary or the kernel's sources have changed since it was taken."""
+def recorded_counters():
+    """(HBM bytes per launch, L2 hit rate) of the headline kernel from the
+    committed counter summary: FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the same counter reads for a plain copy of known size, and TCC_HIT /
+    (TCC_HIT + TCC_MISS).  Each is None when the summary lacks it or the
+    kernel's sources have changed since it was taken."""
     try:
         with open(HEADLINE_TRAFFIC_FILE) as fh:
             fields = dict(l.split(":", 1) for l in fh.read().splitlines() if ":" in l and not l.startswith(" "))
     except OSError:
-        return None
+        return None, None
     if fields.get("kernel_source_sha256", "").strip() != kernel_source_hash():
-        return None
-    try:
-        return int(fields["traffic_bytes_per_launch"].strip())
-    except (KeyError, ValueError):
-        return None
+        return None, None
+    out = []
+    for key, conv in (("traffic_bytes_per_launch", int), ("l2_hit_rate", float)):
+        try:
+            out.append(conv(fields[key].strip()))
+        except (KeyError, ValueError):
+            out.append(None)
+    return tuple(out)
 
 
 def copy_calib(torch, steps, warmup):
@@ -394,25 +403,87 @@ def copy_calib(torch, steps, warmup):
     return 0
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class pinned_core:
+    """Run the calling thread on one host core (the lowest it may use) for
+    the duration of a `with` block; the core's number is `.core`."""
+
+    def __enter__(self):
+        self.old = os.sched_getaffinity(0)
+        self.core = min(self.old)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.old)
+        return False
+
+
 def cpu_baseline(seconds):
-    """The CPU oracle as it stands (single-threaded C, double), timed on this
-    host over whole stage-1 DCNv4 f16 batches until `seconds` have passed."""
+    """The CPU oracle as it stands (single-threaded C, double), timed on one
+    pinned host core over whole stage-1 DCNv4 f16 batches until `seconds`
+    have passed."""
     import oracle
     from sparse_deformable_sampling_amd import synth
     n, h, w, c, g = STAGES["stage1"]
     d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f16", seed=1)
     oracle.dcn_forward(d["x"][:1], d["offset"][:1], d["mask"][:1], group=g, dtype="f16")  # load/compile
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, dtype="f16")
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    with pinned_core() as pin:
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, dtype="f16")
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
     units = runs * n * h * w * c * 9
     return {"value": round(units / el / 1e9, 4), "unit": "Gtaps*ch/s", "cores": 1, "kind": "oracle",
+            "pinned_core": pin.core, "cpu_model": cpu_model(),
             "sample": "%d full batch(es) of the headline workload (N=64 56x56x64 G=4, DCNv4, f16 inputs read "
-                      "as exact doubles) through the single-threaded C oracle, %.1f s" % (runs, el)}
+                      "as exact doubles) through the single-threaded C oracle on host core %d, %.1f s"
+                      % (runs, pin.core, el)}
+
+
+def tiny_line(torch, reps=200):
+    """The tiny DCNv3 f32 case (N=1, 8x8, C=16, G=2, offsets U(-2,2), logits
+    N(0,1) with softmax): latency-bound, so the GPU figure is the median of
+    single launches between event pairs, and the oracle's the median of 5
+    runs on one pinned host core."""
+    import oracle
+    from sparse_deformable_sampling_amd import _binding as B, synth
+    n, h, w, c, g = 1, 8, 8, 16, 2
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), offset=("uniform", -2.0, 2.0), dtype="f32", seed=1)
+    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, True, B.DCN_F32)
+    x, off, mask = (upload(torch, d[k], "f32") for k in ("x", "offset", "mask"))
+    out = torch.empty((n, h, w, c), device="cuda")
+    stream = torch.cuda.current_stream()
+    args = [(ctypes.byref(desc), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(off.data_ptr()),
+             ctypes.c_void_p(mask.data_ptr()), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))]
+    r = Runner("dcnv3_fwd_tiny_f32", args, B.lib().dcn_forward, n * h * w * c * 9, 0, stream)
+    for i in range(20):
+        r.launch(i)
+    torch.cuda.synchronize()
+    med, p10, p90 = launch_spread(torch, r, reps)
+    cpu = []
+    with pinned_core() as pin:
+        for _ in range(5):
+            t0 = time.perf_counter()
+            oracle.dcn_forward(d["x"], d["offset"], d["mask"], group=g, softmax=True)
+            cpu.append(time.perf_counter() - t0)
+    return {"gpu_us_median_single": round(med * 1e3, 2), "gpu_us_p10_single": round(p10 * 1e3, 2),
+            "gpu_us_p90_single": round(p90 * 1e3, 2), "single_launches": reps,
+            "cpu_oracle_us_median_of_5": round(float(np.median(cpu)) * 1e6, 2), "cpu_pinned_core": pin.core,
+            "taps_ch": n * h * w * c * 9}
 
 
 def cpu_baseline_threads(seconds, max_threads=16):
@@ -479,14 +550,11 @@ def main():
         else:
             parts = name.split("_")   # dcnv4_fwd_stage1_f16
             r = dcn_fwd_runner(torch, parts[2], parts[3], parts[0] == "dcnv3")
-        ms = time_steps(torch, r, args.steps, args.warmup)
-        print(json.dumps({"only": r.name, **summarize(r, ms, kernel_ms(torch, r, args.steps))}), flush=True)
+        print(json.dumps({"only": r.name, **measure(torch, r, args.steps, args.warmup)}), flush=True)
         return 0
 
     head = dcn_fwd_runner(torch, "stage1", "f16", False)
-    ms = time_steps(torch, head, args.steps, args.warmup)
-    kms = kernel_ms(torch, head, args.steps)
-    s = summarize(head, ms, kms)
+    s = measure(torch, head, args.steps, args.warmup)
     print("[bench] headline %s: %s" % (head.name, s), file=sys.stderr, flush=True)
     del head
 
@@ -498,43 +566,46 @@ def main():
                 ("dcnv4", "table10", "f32")]
         for kind, stage, dt in jobs:
             r = dcn_fwd_runner(torch, stage, dt, kind == "dcnv3")
-            secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
+            secondary[r.name] = measure(torch, r, 100, 10)
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
         bwd_jobs = [(True, "stage1", "f32"), (False, "stage1", "f32"), (False, "stage1", "f16"),
                     (False, "stage1", "bf16"), (False, "stage2", "f16"), (False, "stage3", "f16")]
         for softmax, stage, dt in bwd_jobs:
             r = dcn_bwd_runner(torch, softmax, stage=stage, dtype=dt)
-            secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+            secondary[r.name] = measure(torch, r, 50, 5)
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
         for stage, dt in (("table10", "f16"), ("table10", "bf16"), ("stage1", "f16"), ("stage2", "f16"),
                           ("stage3", "f16")):
             r = frontend_runner(torch, stage, dt)
-            secondary[r.name] = summarize(r, time_steps(torch, r, 100, 10), kernel_ms(torch, r, 100))
+            secondary[r.name] = measure(torch, r, 100, 10)
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
         r = module_runner(torch, "table10", "f16")
-        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        secondary[r.name] = measure(torch, r, 50, 5)
         secondary[r.name]["context_pages_a100_fp16_ms"] = 0.873
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
         r = msda_runner(torch)
-        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        secondary[r.name] = measure(torch, r, 50, 5)
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         r = msda_ref_runner(torch)
-        secondary[r.name] = summarize(r, time_steps(torch, r, 50, 5), kernel_ms(torch, r, 50))
+        secondary[r.name] = measure(torch, r, 50, 5)
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
         for gather in (True, False):
             r = msda_bwd_runner(torch, gather=gather)
             k = 20 if gather else 5
-            secondary[r.name] = summarize(r, time_steps(torch, r, k, 2), kernel_ms(torch, r, k))
+            secondary[r.name] = measure(torch, r, k, 2)
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
         torch.cuda.empty_cache()
 
+    tiny = tiny_line(torch)
+    print("[bench] tiny: %s" % tiny, file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    traffic, l2_hit = recorded_counters()
     line = {
         "metric": METRIC, "value": s["gtaps_ch_per_s"], "unit": "Gtaps*ch/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": s["ms_per_step"], "higher_is_better": True,
@@ -544,9 +615,13 @@ def main():
                    "softmax": 0, "accumulate": "f32", "x": "N(0,1)", "offsets": "N(0,1.5)", "mask": "N(0,1)",
                    "rotating_input_sets": n_sets(s["min_bytes"])},
         "roofline": {"bound": "hbm", "achieved": s["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": s["frac_of_hbm_peak"], "traffic": recorded_traffic(),
-                     "kernel": "dcn_fwd (f16, 3x3, DCNv4)", "kernel_us_mean": s["kernel_us_mean"],
-                     "kernel_us_median": s["kernel_us_median"], "algorithmic_bytes_per_launch": s["min_bytes"]},
+                     "frac": s["frac_of_hbm_peak"], "traffic": traffic, "l2_hit_rate": l2_hit,
+                     "kernel": HEADLINE_KERNEL, "kernel_us_mean": s["kernel_us_mean"],
+                     "kernel_us_median_single": s["kernel_us_median_single"],
+                     "algorithmic_bytes_per_launch": s["min_bytes"],
+                     "algorithmic_bytes": "(2*D + 3*K) * 2 B per (pixel, group) item: x read once, offsets, mask, "
+                                          "out written once; 118 B x 802816 items"},
+        "tiny_dcnv3_f32": tiny,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": None if args.no_cpu_baseline else cpu_baseline_threads(args.cpu_seconds),
         "secondary": secondary,

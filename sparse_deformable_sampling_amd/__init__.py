@@ -6,9 +6,15 @@ device memory and the current HIP stream, every step of the computation runs
 in libdcn's HIP kernels.  There is no CPU path: without the built library (or
 without a GPU) the calls raise.
 
-* ``dcn_forward``  -- DCNv3 (``softmax=True``) / DCNv4 (``softmax=False``) core op.
-* ``dcn_backward`` -- its gradients (f32).
-* ``msda_forward`` -- multi-scale deformable attention sampling core (f32).
+* ``dcn_forward``  -- DCNv3 (``softmax=True``) / DCNv4 (``softmax=False``) core op
+  (f32, f16, bf16; fp32 accumulation).
+* ``dcn_backward`` -- its gradients (f32, f16, bf16; an f16/bf16 grad_x is
+  summed in an fp32 workspace this wrapper allocates with torch).
+* ``dcnv4_offset_mask`` -- the DCNv4 front-end: depthwise 3x3, then the merged
+  offset/modulation linear (f16, bf16).
+* ``msda_forward`` / ``msda_forward_ref`` -- multi-scale deformable attention
+  sampling core, from given locations or from references (f32).
+* ``msda_backward`` -- its gradients (f32).
 * ``dcn_output_size`` -- output spatial size for a geometry.
 
 Layouts: x [n,h,w,c] (NHWC); offset [n,ho,wo,group,K,2] holding (dx, dy);

@@ -22,12 +22,20 @@
 //    element (neighbouring chunks share halo rows);
 //  - a contribution to a row outside the window (an offset beyond the halo)
 //    goes to grad_x with an fp32 atomic directly.
-// The scale 2^e is chosen per workgroup from the bound B = max over its items
-// of max_k |m_k| * max_c |g_c|, which no single contribution m_k w g_c (w <= 1)
-// can exceed: e makes B * 2^e < 2^30, so one contribution is one 32-bit
-// integer (a single conversion), resolving 2^-30 of B, and a cell's 64-bit
-// sum of fewer than 2^32 of them cannot overflow.  Non-finite inputs, or a B
-// outside [2^-60, 2^60), turn the fixed-point path off for that workgroup
+// The scale 2^e is chosen per workgroup from the item bounds
+// b = max_k |m_k| * max_c |g_c|, which no single contribution m_k w g_c
+// (w <= 1) of that item can exceed.  A pre-scan counts the workgroup's items
+// per binary exponent of b and takes for B = 2^E the smaller of the least
+// power of two that bounds all but about one item in a thousand and 64 times
+// the median item's bound (the margin keeps items of ordinary spread under
+// B, the median keeps outliers from setting it): e makes B * 2^e = 2^30,
+// so one contribution below B is one 32-bit integer (a single conversion),
+// resolving 2^-30 of B, and a cell's 64-bit sum of fewer than 2^32 of them
+// cannot overflow.  A lane whose tap could reach B (|m_k| times the largest
+// |g_c| of its channels) sends that tap's contributions to grad_x with fp32
+// atomics instead, so a few large modulations (DCNv4's are unbounded) do not
+// coarsen the rest of the workgroup's sums.  Non-finite inputs, or a B
+// outside [2^-60, 2^60], turn the fixed-point path off for that workgroup
 // (every contribution then takes the fp32 atomic).  Integer sums do not
 // depend on the order of the additions.
 // With f16/bf16 storage the inputs are widened to fp32 as they are read,
@@ -136,8 +144,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
     constexpr int ES = (int)sizeof(T);
     constexpr int KF = KH * KW;
     extern __shared__ unsigned long long acc[];   // [aw][w][d] fixed-point sums
-    __shared__ float red_s[16];
     __shared__ int red_bad[16];
+    __shared__ int hist[128];                     // items per binary exponent of their bound, + 63
+    __shared__ int E_s;
     const int K = KF ? KF : G.K;
     const int kh = KH ? KH : G.kh;
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -163,7 +172,8 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
     const int li = tid >> bc.lq_log, c4 = tid & (lq - 1);
 
     // ---- the bound B of this workgroup, and whether every input is finite
-    float part = 0.f;
+    for (int i = tid; i < 128; i += nthr) hist[i] = 0;
+    __syncthreads();
     int bad = 0;
     // Same lane layout as the main pass: lane (item, chunk) reads its CPL
     // channels of grad_out with 16-byte loads and every lq-th logit.
@@ -194,30 +204,48 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
             gm = fmaxf(gm, __shfl_xor(gm, o, 64));
         }
         if (SOFTMAX) ms = 1.f;
-        part = fmaxf(part, ms * gm);
+        if (c4 == 0) {
+            int ex = 0;
+            (void)frexpf(ms * gm, &ex);      // b < 2^ex (ex = 0 for b = 0)
+            atomicAdd(&hist[min(max(ex + 63, 0), 127)], 1);
+        }
     }
-    for (int o = 1; o < 64; o <<= 1) part = fmaxf(part, __shfl_xor(part, o, 64));
     for (int o = 1; o < 64; o <<= 1) bad |= __shfl_xor(bad, o, 64);
-    if ((tid & 63) == 0) {
-        red_s[tid >> 6] = part;
-        red_bad[tid >> 6] = bad;
-    }
+    if ((tid & 63) == 0) red_bad[tid >> 6] = bad;
     __syncthreads();
-    float B = 0.f;
     bad = 0;
-    for (int w = 0; w < (nthr + 63) / 64; ++w) {
-        B = fmaxf(B, red_s[w]);
-        bad |= red_bad[w];
+    for (int w = 0; w < (nthr + 63) / 64; ++w) bad |= red_bad[w];
+    // B = 2^E, from the histogram by one wave (lane i holds bins 2i, 2i+1;
+    // cum(b) = items in bins <= b, non-decreasing in b):
+    //   top: the least bin b with at most `allow` items above it;
+    //   med: the least bin b with cum(b) >= half of the items.
+    if (tid < 64) {
+        const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+        int incl = h0 + h1;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += t;
+        }
+        const int total = __shfl(incl, 63, 64);
+        const int cum0 = incl - h1, cum1 = incl;   // cum(2i), cum(2i+1)
+        const int allow = nitems >> 10, half = (total + 1) / 2;
+        // bin 127 satisfies both tests, so every ballot below has a set bit
+        const unsigned long long t0 = __ballot(total - cum0 <= allow), t1 = __ballot(total - cum1 <= allow);
+        const unsigned long long q0 = __ballot(cum0 >= half), q1 = __ballot(cum1 >= half);
+        auto least = [](unsigned long long even, unsigned long long odd) {
+            const int be = even ? 2 * __builtin_ctzll(even) : 128, bo = odd ? 2 * __builtin_ctzll(odd) + 1 : 128;
+            return min(be, bo);
+        };
+        if (tid == 0) E_s = min(least(t0, t1), least(q0, q1) + 6) - 63;
     }
-    const bool fixed = !bad && B >= 0x1p-60f && B < 0x1p60f;
-    int ex = 0;
-    if (fixed) (void)frexpf(B, &ex);        // B < 2^ex
-    const int e = 30 - ex;                   // B * 2^e < 2^30: rounding of the products cannot reach 2^31
-    const float tscale = ldexpf(1.f, e);
-    const double s_fix = ldexp(1.0, -e);    // value of one fixed-point unit
-
     for (int i = tid; i < bc.aw * rowe; i += nthr) acc[i] = 0ull;
     __syncthreads();
+    const int E = E_s;
+    const bool fixed = !bad && E >= -59 && E <= 60;
+    const float Bf = ldexpf(1.f, E);        // a tap of a lane reaching this takes the atomics
+    const int e = 30 - E;                    // B * 2^e = 2^30: rounding of a product below B stays below 2^31
+    const float tscale = ldexpf(1.f, e);
+    const double s_fix = ldexp(1.0, -e);    // value of one fixed-point unit
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)bc.x_bytes, 0x00020000);
     const long img = (long)n * H * W * C;
@@ -263,6 +291,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
             }
             float gc[CPL];
             load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, gc);
+            float gl = 0.f;                  // largest |g_c| of this lane's channels
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) gl = fmaxf(gl, fabsf(gc[j]));
             const T* ob = off + item * K * 2;
             const int bx = wo * G.sw - G.pw, by = r * G.sh - G.ph;
             float sdm = 0.f;
@@ -285,12 +316,13 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                     sdy = fmaf(gc[j], dvdb, sdy);
                 }
                 if (gx) {
+                    const bool small = fabsf(m[k]) * gl < Bf;   // every contribution of this tap below B
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         if (o4[q] == OOB) continue;   // corner outside the image
                         const int yc = y0 + (q >> 1), xc = x0 + (q & 1);
                         const float mw = m[k] * w4[q];
-                        if (fixed && yc >= lo && yc < lo + bc.aw) {
+                        if (fixed && small && yc >= lo && yc < lo + bc.aw) {
                             int slot = base_slot + (yc - lo);
                             slot -= slot >= bc.aw ? bc.aw : 0;
                             unsigned long long* dst = acc + slot * rowe + xc * pstr + CPL * c4;

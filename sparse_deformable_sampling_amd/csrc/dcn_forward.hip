@@ -70,11 +70,13 @@ struct Modulation<DT, 0, SOFTMAX> {
 };
 
 // Geometry of one tap: corner weights already multiplied by the modulation,
-// zero for a corner outside the map; `row` points at the top-left corner.
+// zero for a corner outside the map (`in` bit q set for a corner inside);
+// `base` points at the top-left corner.
 struct Tap {
     float w00, w01, w10, w11;
     long base;       // element index of corner (y0, x0), channel 0 of the image
     bool any;
+    unsigned in;     // bit q: corner q (00, 01, 10, 11) lies inside the map
 };
 
 __device__ __forceinline__ Tap tap_geometry(const Geom& G, int bx, int by, int kx, int ky, float dx, float dy,
@@ -97,6 +99,7 @@ __device__ __forceinline__ Tap tap_geometry(const Geom& G, int bx, int by, int k
     t.w11 = (cy1 && cx1) ? mb * b : 0.f;
     t.base = ((long)y0 * G.w + x0) * G.c;
     t.any = true;
+    t.in = (cy0 && cx0 ? 1u : 0u) | (cy0 && cx1 ? 2u : 0u) | (cy1 && cx0 ? 4u : 0u) | (cy1 && cx1 ? 8u : 0u);
     return t;
 }
 
@@ -257,7 +260,9 @@ __global__ __launch_bounds__(256) void dcn_fwd_generic(Geom G, const typename El
             const float w[4] = {tp.w00, tp.w01, tp.w10, tp.w11};
             const long o[4] = {0, G.c, rowc, rowc + G.c};
             for (int q = 0; q < 4; ++q) {
-                if (w[q] == 0.f) continue;
+                // a corner outside the map is skipped; one inside is summed
+                // even at weight zero (0 * non-finite x is NaN, as in the sum's definition)
+                if (!(tp.in >> q & 1u)) continue;
                 for (int i = 0; i < nc; ++i) acc[i] = fmaf(w[q], to_f32(r[o[q] + i]), acc[i]);
             }
         }

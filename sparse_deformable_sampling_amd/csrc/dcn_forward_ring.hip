@@ -10,10 +10,10 @@
 // so gathering 36 corners per output from L1 runs far below HBM speed; the
 // LDS serves random 16-byte reads several times faster.  Each workgroup
 // therefore owns one image, a set of GS channel groups and a chunk of output
-// rows.  It keeps a ring of input rows of those groups in LDS (one zero
-// column on each side, plus a mirror of slot 0 after the last slot so the row
-// below any slot is the next slot in memory) and walks down the chunk TR
-// output rows per step:
+// rows.  It keeps a ring of input rows of those groups in LDS (two zero
+// columns on the left, one on the right, plus a mirror of slot 0 after the
+// last slot so the row below any slot is the next slot in memory) and walks
+// down the chunk TR output rows per step:
 //   - the rows a step may read through LDS form the window [lo, lo + NW): the
 //     3x3 footprint of its output rows plus HY halo rows above and below for
 //     the learned offsets;
@@ -23,7 +23,11 @@
 //     whole LDS goes to the ring);
 //   - a sample whose two rows fall outside the window (|dy| > HY) is given
 //     zero weight in the LDS pass and read with global loads in a tail pass by
-//     the lanes that need it.
+//     the lanes that need it;
+//   - a tap that reads nothing through LDS (outside the map, or in the tail)
+//     points at LDS address 0, the two left-hand zero columns of slots 0
+//     and 1, so its four corners read zeros: a zero weight times a
+//     non-finite x elsewhere would otherwise turn the sum into NaN.
 // Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
 // accumulation; 16-byte vector stores, one writer per output element.  A
@@ -138,11 +142,11 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             const uint32_t c = (uint32_t)(wave + i * nwaves) * 1024u;
             if (row_src[i] != OOB) {
                 const uint32_t src = inside ? base + row_src[i] : OOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + slot * rc.pitch + rc.pb + c), 16, src,
-                                                         0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + slot * rc.pitch + 2 * rc.pb + c), 16,
+                                                         src, 0, 0, 0);
                 if (slot == 0)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + rc.R * rc.pitch + rc.pb + c), 16,
-                                                             src, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ring + rc.R * rc.pitch + 2 * rc.pb + c),
+                                                             16, src, 0, 0, 0);
             }
         }
     };
@@ -191,12 +195,14 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         }
     };
 
-    // Zero the two border columns of every ring slot, mirror included (never written again).
+    // Zero the border columns of every ring slot, mirror included (never
+    // written again): LDS columns 0, 1 (image columns -2, -1) and W+2 (image
+    // column W).
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < (rc.R + 1) * 2 * rc.cpp; i += nthr) {
-            const int slot = i / (2 * rc.cpp), j = i - slot * 2 * rc.cpp;
-            const uint32_t col_off = j < rc.cpp ? 16u * j : (uint32_t)(G.w + 1) * rc.pb + 16u * (j - rc.cpp);
+        for (int i = tid; i < (rc.R + 1) * 3 * rc.cpp; i += nthr) {
+            const int slot = i / (3 * rc.cpp), j = i - slot * 3 * rc.cpp;
+            const uint32_t col_off = j < 2 * rc.cpp ? 16u * j : (uint32_t)(G.w + 2) * rc.pb + 16u * (j - 2 * rc.cpp);
             *reinterpret_cast<u32x4*>(ring + slot * rc.pitch + col_off) = z;
         }
     }
@@ -205,7 +211,9 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    const uint32_t gbyte = (uint32_t)gl * gsize;
+    // Byte offset of this lane's group within LDS column 1 (image column -1):
+    // a tap's left corners sit at column xs + 1 for xs = x0 + 1.
+    const uint32_t gbyte = (uint32_t)gl * gsize + (uint32_t)rc.pb;
     const float lim = 16777216.0f;
     // Window-relative row and LDS column of each tap's top-left corner before
     // the offset (they do not change from step to step).
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 const float ty = fminf(fmaxf(G.scale * dyk, -lim), lim);
                 const float fx = floorf(tx), fy = floorf(ty);
                 const float a = tx - fx, b = ty - fy;
-                const int xs = bxk[kx] + (int)fx;                   // LDS column of the left corners
+                const int xs = bxk[kx] + (int)fx;                   // x0 + 1 (LDS column of the left corners - 1)
                 const int yi = byk[ky] + (int)fy;                   // window row of the top corners
                 const bool colok = (unsigned)xs <= (unsigned)G.w;   // image column in [-1, W-1]
                 const bool inwin = (unsigned)yi < (unsigned)(rc.nw - 1);
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 uint32_t s0 = (uint32_t)(slot_lo + yi);
                 s0 = min(s0, s0 - (uint32_t)rc.R);                  // wrap once
                 const uint32_t addr = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
-                Ak = use ? addr : 0u;
+                Ak = use ? addr : 0u;   // LDS columns 0, 1 of slots 0, 1: zeros
                 const float mm = use ? m[k] : 0.f;
                 const float ma = mm * (1.f - a), mb = mm * a;
                 w00 = ma * (1.f - b);
@@ -541,7 +549,9 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
             const int threads = (items_step + 63) / 64 * 64;
             const int pb = gs * G.d * es;
             const int cpp = pb / 16;
-            const long pitch = (long)(G.w + 2) * pb + 80;   // 5 bank groups of skew: nearby rows spread over the banks
+            // W image columns, two zero columns left and one right, and 5 bank
+            // groups of skew so that nearby rows spread over the banks.
+            const long pitch = (long)(G.w + 3) * pb + 80;
             const int nwaves = threads / 64;
             const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
             if (row_iters > 4) continue;   // ROW_IT

@@ -13,7 +13,7 @@ struct RingCfg {
     int gsets;        // group sets per image (= groups / gs)
     int pb;           // bytes of one pixel in LDS (gs groups)
     int cpp;          // 16-byte chunks per LDS pixel (pb / 16)
-    int pitch;        // bytes of one ring row: (w + 2) pixels (zero column each side) + 80 bytes of bank skew
+    int pitch;        // bytes of one ring row: (w + 3) pixels (two zero columns left, one right) + 80 bytes of bank skew
     int R;            // ring rows (slot R, one more, mirrors slot 0)
     int nw;           // window rows a step may read through LDS
     int hy;           // halo rows above and below the footprint

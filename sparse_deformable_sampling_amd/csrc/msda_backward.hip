@@ -529,6 +529,13 @@ __global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int
 // the records' grad_out slices are then read and summed, the next batch's
 // records already in flight.  A level whose blocks expect long runs gives
 // each block gpc groups (interleaved batches), summed through LDS.
+// A coarse cell gathers thousands of terms (about 1300 per head on the
+// 13x17 level of the encoder shape), so the sums are kept in fp64: a term is
+// the product of two fp32 values, exact in fp64, and the sum then carries
+// about 2^-53 of relative error per term instead of 2^-24, so a cell's
+// gradient comes out within one fp32 rounding of the exact sum of its terms.
+// fp64 FMAs issue at the rate of non-packed fp32 ones on this chip, and the
+// kernel is bound by its loads.
 constexpr int CB = 4;
 
 template <int LPC>
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
                                                       float* __restrict__ gvalue)
 {
     __shared__ float stage[CB + 1][256];   // per lane: grad_out offset, then the CB weights
-    __shared__ float4 part[CB][256];
+    __shared__ double part[4][256];        // one cell's partial sums per lane, reduced cell by cell
     const int b = blockIdx.x;
     int k = 0;
     while (k + 1 < G.L && b >= C.blk_start[k + 1]) ++k;
@@ -579,9 +586,11 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
     auto index = [&](int tt) { return tt < n0 ? bu[0] + tt : bl[0] + tt - n0; };
     int4 e = make_int4(0, 0, 0, 0);
     if (gi * LPC + j < ntot) e = pr[index(gi * LPC + j)];
-    float4 acc[CB];
+    double acc[CB][4];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] = 0.0;
     for (int k0 = gi * LPC; k0 < ntot; k0 += step) {   // the same trip count for the whole group
         const int tt = k0 + j;
         float w[CB];
@@ -611,34 +620,37 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
             const int src = grp * LPC + u;
             const uint32_t o = __float_as_uint(stage[0][src]);
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, o == MS_OOB ? o : o + gbase, 0, 0);
+            const double gv[4] = {(double)__uint_as_float(v.x), (double)__uint_as_float(v.y),
+                                  (double)__uint_as_float(v.z), (double)__uint_as_float(v.w)};
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const float ww = stage[c + 1][src];
-                acc[c].x = fmaf(ww, __uint_as_float(v.x), acc[c].x);
-                acc[c].y = fmaf(ww, __uint_as_float(v.y), acc[c].y);
-                acc[c].z = fmaf(ww, __uint_as_float(v.z), acc[c].z);
-                acc[c].w = fmaf(ww, __uint_as_float(v.w), acc[c].w);
+                const double ww = (double)stage[c + 1][src];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[c][i] = fma(ww, gv[i], acc[c][i]);
             }
         }
         wave_lds_sync();
     }
     if (gpc > 1) {   // uniform over the workgroup
 #pragma unroll
-        for (int c = 0; c < CB; ++c) part[c][t] = acc[c];
-        __syncthreads();
-        if (gi == 0)
-            for (int u = 1; u < gpc; ++u)
+        for (int c = 0; c < CB; ++c) {
 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    const float4 p = part[c][t + u * LPC];
-                    acc[c].x += p.x; acc[c].y += p.y; acc[c].z += p.z; acc[c].w += p.w;
-                }
+            for (int i = 0; i < 4; ++i) part[i][t] = acc[c][i];
+            __syncthreads();
+            if (gi == 0)
+                for (int u = 1; u < gpc; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[c][i] += part[i][t + u * LPC];
+            __syncthreads();
+        }
     }
     if (live && gi == 0) {
         float* dst = gvalue + (((long)n * G.S + G.start[l] + (long)y * Wl + xs) * G.m + h) * G.dh + 4 * j;
 #pragma unroll
         for (int c = 0; c < CB; ++c)
-            if (xs + c < Wl) *reinterpret_cast<float4*>(dst + (long)c * G.m * G.dh) = acc[c];
+            if (xs + c < Wl)
+                *reinterpret_cast<float4*>(dst + (long)c * G.m * G.dh) =
+                    make_float4((float)acc[c][0], (float)acc[c][1], (float)acc[c][2], (float)acc[c][3]);
     }
 }
 
