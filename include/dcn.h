@@ -54,7 +54,8 @@
  *
  * Ownership and streams: every tensor pointer is a DEVICE pointer owned by the
  * caller (except msda_forward's spatial_shapes, a HOST array).  The library
- * allocates and frees nothing.  `stream` is a hipStream_t (NULL: the null
+ * allocates and frees nothing; its one device buffer of its own is the static
+ * scratch array of dcn_backward_noalloc.  `stream` is a hipStream_t (NULL: the null
  * stream); every call only enqueues work on it and returns, and results are
  * ready when the stream is.  Calls are thread-safe.
  *
@@ -141,6 +142,25 @@ dcn_status dcn_backward_workspace_size(const dcn_desc* desc, size_t* bytes);
 dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
                            const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * dcn_backward_ws with no workspace argument.  The fp32 sums of an f16/bf16
+ * grad_x live in a device array the library owns, 64 MiB per GPU (held from
+ * the first call on that GPU until the process ends), so grad_x may have at
+ * most 16 Mi elements (n*h*w*c <= 16777216); a larger f16/bf16 grad_x is
+ * DCN_ERR_INVALID before anything is enqueued.  f32, or grad_x NULL, uses no
+ * scratch.  The call allocates nothing: it enqueues the same kernels as
+ * dcn_backward_ws (the scratch is zero-filled by a kernel on `stream`, not
+ * by a memset).  Its first call on a device looks up the array's address
+ * (hipGetSymbolAddress, which may load the library's code object): make that
+ * first call outside any graph capture.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap in time on one GPU (different streams,
+ * or threads) race and must be serialised by the caller.  Everything else,
+ * arguments and results included, is as dcn_backward_ws. */
+dcn_status dcn_backward_noalloc(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                                void* stream);
 
 /* DCNv4 front-end: the offsets and modulation of the core op computed from
  * the module input x ("DCNv4: Unbounded Weights", "1. Remove Softmax": the

@@ -30,7 +30,7 @@ class MsdaDesc(ctypes.Structure):
 
 
 EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "dcn_backward_workspace_size", "dcn_backward_ws",
-           "dcn_offset_mask",
+           "dcn_backward_noalloc", "dcn_offset_mask",
            "msda_forward", "msda_forward_ref", "msda_backward", "msda_backward_workspace_size", "msda_backward_ws",
            "dcn_status_str", "dcn_last_error")
 
@@ -58,6 +58,8 @@ def lib():
     L.dcn_backward_workspace_size.restype = ctypes.c_int
     L.dcn_backward_ws.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.dcn_backward_ws.restype = ctypes.c_int
+    L.dcn_backward_noalloc.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dcn_backward_noalloc.restype = ctypes.c_int
     L.msda_forward.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp]
     L.msda_forward.restype = ctypes.c_int
     L.dcn_offset_mask.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]

@@ -133,13 +133,12 @@ static int64_t backward_ws_bytes(const dcn_desc* d)
     return d->dtype == DCN_F32 ? 0 : (int64_t)d->n * d->h * d->w * d->c * 4;
 }
 
-static dcn_status backward_impl(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
-                                const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
-                                void* workspace, size_t workspace_bytes, void* stream)
+// Pointer checks of a backward call (the geometry is already valid).
+static dcn_status check_backward_ptrs(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                      const void* grad_out, const void* grad_x, const void* grad_offset,
+                                      const void* grad_mask)
 {
-    dcn::Geom G;
-    dcn_status st = make_geom(desc, &G);
-    if (st != DCN_OK) return st;
+    dcn_status st;
     const size_t es = elem_size(desc->dtype);
     if ((st = check_ptr(x, "x", es)) || (st = check_ptr(offset, "offset", es)) ||
         (st = check_ptr(mask, "mask", es)) || (st = check_ptr(grad_out, "grad_out", es)))
@@ -147,6 +146,17 @@ static dcn_status backward_impl(const dcn_desc* desc, const void* x, const void*
     if (grad_x && (uintptr_t)grad_x % es) return fail(DCN_ERR_UNSUPPORTED, "grad_x is not aligned");
     if (grad_offset && (uintptr_t)grad_offset % es) return fail(DCN_ERR_UNSUPPORTED, "grad_offset is not aligned");
     if (grad_mask && (uintptr_t)grad_mask % es) return fail(DCN_ERR_UNSUPPORTED, "grad_mask is not aligned");
+    return DCN_OK;
+}
+
+static dcn_status backward_impl(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    if ((st = check_backward_ptrs(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask))) return st;
     const int64_t need = grad_x ? backward_ws_bytes(desc) : 0;
     if (need > 0) {
         if (!workspace)
@@ -184,6 +194,60 @@ dcn_status dcn_backward_ws(const dcn_desc* desc, const void* x, const void* offs
 {
     return backward_impl(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, workspace,
                          workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch for dcn_backward_noalloc: the fp32 sums of an f16/bf16 grad_x, in a
+// device array the library owns (one copy per GPU, held until the process
+// ends).  Host code never uses the array's name as an address: its device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device and kept (concurrent first calls store the same address).
+dcn_status scratch_ptr(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DCN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DCN_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev, kMaxDevices);
+    void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail(DCN_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+    }
+    *out = p;
+    return DCN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dcn_status dcn_backward_noalloc(const dcn_desc* desc, const void* x, const void* offset, const void* mask,
+                                const void* grad_out, void* grad_x, void* grad_offset, void* grad_mask, void* stream)
+{
+    dcn::Geom G;
+    dcn_status st = make_geom(desc, &G);
+    if (st != DCN_OK) return st;
+    if ((st = check_backward_ptrs(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask))) return st;
+    const int64_t need = grad_x ? backward_ws_bytes(desc) : 0;
+    if (need > (int64_t)kScratchBytes)
+        return fail(DCN_ERR_INVALID, "dcn_backward_noalloc: grad_x needs %lld bytes of fp32 sums, more than the "
+                    "%zu bytes of its static scratch (use dcn_backward_ws)", (long long)need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_ptr(&ws)) != DCN_OK) return st;
+    return backward_impl(desc, x, offset, mask, grad_out, grad_x, grad_offset, grad_mask, ws,
+                         need > 0 ? kScratchBytes : 0, stream);
 }
 
 dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_weight, const void* dw_bias,

@@ -135,6 +135,27 @@ def test_backward_workspace_and_nulls():
     assert st == B.DCN_OK
 
 
+def test_backward_noalloc_rejects_beyond_its_scratch():
+    """dcn_backward_noalloc keeps f16/bf16 grad_x sums in a 64 MiB static
+    array: 16 Mi elements fit, one more is refused before anything is
+    enqueued (and before the array's address is looked up); invalid
+    arguments are refused as by dcn_backward_ws."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+    ins = (vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000))
+    desc = B.make_desc(1, 4097, 4096, 1, 1, dtype=B.DCN_F16)   # 16 Mi + 4096 elements
+    st = L.dcn_backward_noalloc(ctypes.byref(desc), *ins, vp(0x5000), None, None, None)
+    assert st == B.DCN_ERR_INVALID and b"scratch" in L.dcn_last_error()
+    desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_BF16)
+    st = L.dcn_backward_noalloc(ctypes.byref(desc), vp(0x1000), None, vp(0x3000), vp(0x4000), vp(0x5000), None,
+                                None, None)
+    assert st == B.DCN_ERR_INVALID
+    st = L.dcn_backward_noalloc(ctypes.byref(desc), *ins, vp(0x5001), None, None, None)
+    assert st == B.DCN_ERR_UNSUPPORTED
+    # nothing requested: a valid no-op, no launch and no scratch
+    assert L.dcn_backward_noalloc(ctypes.byref(desc), *ins, None, None, None, None) == B.DCN_OK
+
+
 def test_msda_validation():
     L = B.lib()
     vp = ctypes.c_void_p
