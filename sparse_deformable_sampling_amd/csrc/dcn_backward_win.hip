@@ -25,7 +25,9 @@
 // The scale 2^e is chosen per workgroup from the item bounds
 // b = max_k |m_k| * max_c |g_c|, which no single contribution m_k w g_c
 // (w <= 1) of that item can exceed.  A pre-scan counts the workgroup's items
-// per binary exponent of b and takes for B = 2^E the smaller of the least
+// per binary exponent of b (one item in eight, spread over the chunk: the
+// bound only sets the resolution, since any tap above B is routed to the
+// atomics) and takes for B = 2^E the smaller of the least
 // power of two that bounds all but about one item in a thousand and 64 times
 // the median item's bound (the margin keeps items of ordinary spread under
 // B, the median keeps outliers from setting it): e makes B * 2^e = 2^30,
@@ -34,10 +36,12 @@
 // cannot overflow.  A lane whose tap could reach B (|m_k| times the largest
 // |g_c| of its channels) sends that tap's contributions to grad_x with fp32
 // atomics instead, so a few large modulations (DCNv4's are unbounded) do not
-// coarsen the rest of the workgroup's sums.  Non-finite inputs, or a B
-// outside [2^-60, 2^60], turn the fixed-point path off for that workgroup
-// (every contribution then takes the fp32 atomic).  Integer sums do not
-// depend on the order of the additions.
+// coarsen the rest of the workgroup's sums.  A tap whose |m_k| or any of the
+// lane's |g_c| is not finite fails that test too (its bound is NaN or Inf),
+// so non-finite values reach grad_x through fp32 atomics as they would
+// through any sum; non-finite values in the sampled items, or a B outside
+// [2^-59, 2^60], turn the fixed-point path off for the whole workgroup.
+// Integer sums do not depend on the order of the additions.
 // With f16/bf16 storage the inputs are widened to fp32 as they are read,
 // grad_offset and grad_mask are rounded once (to nearest even) as they are
 // stored, and grad_x is summed into an fp32 buffer that the caller converts.
@@ -178,8 +182,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
     // Same lane layout as the main pass: lane (item, chunk) reads its CPL
     // channels of grad_out with 16-byte loads and every lq-th logit.
     const int nitems = (r_end - r_begin) * G.wo;
-    for (int it0 = 0; it0 < nitems; it0 += bc.ip) {
-        const int it = it0 + li;
+    constexpr int SAMPLE = 8;         // one item in SAMPLE
+    for (int it0 = 0; it0 * SAMPLE < nitems; it0 += bc.ip) {
+        const int it = (it0 + li) * SAMPLE;
         if (it >= nitems) continue;   // whole items only: the reductions below stay within one item
         const long pix = ((long)n * G.ho + r_begin + it / G.wo) * G.wo + it % G.wo;
         const long item = pix * G.g + g;
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
         }
         const int total = __shfl(incl, 63, 64);
         const int cum0 = incl - h1, cum1 = incl;   // cum(2i), cum(2i+1)
-        const int allow = nitems >> 10, half = (total + 1) / 2;
+        const int allow = total >> 10, half = (total + 1) / 2;
         // bin 127 satisfies both tests, so every ballot below has a set bit
         const unsigned long long t0 = __ballot(total - cum0 <= allow), t1 = __ballot(total - cum1 <= allow);
         const unsigned long long q0 = __ballot(cum0 >= half), q1 = __ballot(cum1 >= half);
@@ -291,9 +296,17 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
             }
             float gc[CPL];
             load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, gc);
-            float gl = 0.f;                  // largest |g_c| of this lane's channels
+            // Largest |g_c| of this lane's channels; NaN when one of them is
+            // NaN (fmaxf would drop it), so that such a lane fails the
+            // fixed-point test below.
+            float gl = 0.f;
+            bool gnan = false;
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) gl = fmaxf(gl, fabsf(gc[j]));
+            for (int j = 0; j < CPL; ++j) {
+                gl = fmaxf(gl, fabsf(gc[j]));
+                gnan |= gc[j] != gc[j];
+            }
+            if (gnan) gl = __builtin_nanf("");
             const T* ob = off + item * K * 2;
             const int bx = wo * G.sw - G.pw, by = r * G.sh - G.ph;
             float sdm = 0.f;
@@ -336,6 +349,10 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                         }
                     }
                 }
+                // A sample outside the map (all four corners outside) is not
+                // read at all: its channel sums are exactly zero, whatever
+                // grad_out holds (0 * Inf would otherwise make them NaN).
+                if ((o4[0] & o4[1] & o4[2] & o4[3] & OOB) != 0u) sm = sdx = sdy = 0.f;
                 sm = lane_sum(sm, lq);
                 sdx = lane_sum(sdx, lq);
                 sdy = lane_sum(sdy, lq);

@@ -356,6 +356,52 @@ def test_backward_modulation_outliers(sds, outliers):
     assert max(errs) <= TOL["f32"], errs
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n,h,w", [(2, 20, 24), (64, 56, 56)])
+def test_backward_non_finite_grad_out_and_mask(sds, dtype, n, h, w):
+    """A few NaN and +-Inf values in grad_out and in the (DCNv4) mask: the
+    gradients they reach are NaN/Inf as in the oracle, and every other
+    element keeps the bar.  The fixed-point sums of grad_x choose their scale
+    from a sample of the items, so a non-finite value outside the sample must
+    still reach grad_x (through the fp32 atomics); (64, 56, 56) is the stage-1
+    shape, where one workgroup covers a whole (image, group) plane."""
+    import torch
+    c, g = 64, 4
+    d = synth.dcn_inputs(n, h, w, c, g, (h, w), dtype="f32", seed=47, grad=True)
+    rng = np.random.default_rng(49)
+    go, mask = d["grad_out"].copy(), d["mask"].copy()
+    for arr, cnt in ((go, 6), (mask, 4)):
+        flat = arr.reshape(-1)
+        idx = rng.choice(flat.size, size=cnt, replace=False)
+        flat[idx] = [np.nan, np.inf, -np.inf, np.nan, np.inf, -np.inf][:cnt]
+    d["grad_out"], d["mask"] = go, mask
+    for k in ("x", "offset", "mask", "grad_out"):
+        d[k] = synth.store(d[k], dtype)
+    say("bwd-non-finite", dtype, (n, h, w))
+    outs = sds.dcn_backward(*(to_dev(d[k], dtype) for k in ("x", "offset", "mask", "grad_out")), group=g,
+                            softmax=False)
+    torch.cuda.synchronize()
+    refs = oracle.dcn_backward(d["x"], d["offset"], d["mask"], d["grad_out"], group=g, softmax=False, dtype=dtype)
+    for name, t, ref in zip(("grad_x", "grad_offset", "grad_mask"), outs, refs):
+        got = to_host(t)
+        # grad_x terms are m_k * w * g_c: zero in fp32 exactly when zero in
+        # fp64, so NaN (0 * Inf) and +-Inf fall on the same elements.  A
+        # grad_offset or grad_mask term multiplies g_c by a corner difference
+        # or an interpolated value that can be exactly 0 in one precision and
+        # tiny in the other, so there only the finite elements must agree
+        # (NaN and Inf may trade places).
+        if name == "grad_x":
+            assert np.array_equal(np.isnan(got), np.isnan(ref)), name
+            assert np.array_equal(np.isinf(got), np.isinf(ref)), name
+            assert np.array_equal(np.signbit(got[np.isinf(ref)]), np.signbit(ref[np.isinf(ref)])), name
+        assert np.array_equal(np.isfinite(got), np.isfinite(ref)), name
+        fin = np.isfinite(ref)
+        assert fin.mean() > 0.9, name
+        e = rel_err(got[fin], ref[fin])
+        say("  err", "bwd-non-finite", dtype, name, "%.3e" % e)
+        assert e <= TOL[dtype], (name, e)
+
+
 @pytest.mark.parametrize("softmax", [True, False])
 def test_backward_crop_against_finite_differences(sds, softmax):
     """The 8x8 top-left crop of image 0 of the stage-1 inputs, as its own
