@@ -116,6 +116,18 @@ __device__ __forceinline__ Sample sample_geometry(const MsdaGeom& G, const MsdaS
     return s;
 }
 
+// Padding of value cells `byte` and `byte + 1` (byte offsets into the [n][S]
+// mask): bit 0 for the first, bit 1 for the second (a nonzero byte is padded).
+// One 8-byte load from the dword that holds the first byte covers both; a
+// dword past the mask reads zero, and neither cell is then used.
+__device__ __forceinline__ uint32_t pad_pair(__amdgpu_buffer_rsrc_t pr, uint32_t byte)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(pr, byte & ~3u, 0, 0);
+    const uint32_t two = __builtin_amdgcn_alignbit(w.y, w.x, (byte & 3u) * 8u);   // the two bytes, low first
+    return ((two & 0xffu) != 0u ? 1u : 0u) | ((two & 0xff00u) != 0u ? 2u : 0u);
+}
+
 // Joint softmax statistics of one head's L*P logits.
 __device__ __forceinline__ void head_stats(const float* a, int LP, bool softmax, float& mx, float& inv)
 {
@@ -222,11 +234,12 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
                                                      MsdaSrc src, const float* __restrict__ attn,
                                                      float* __restrict__ out)
 {
-    // LDS: QT*LP corner offsets, QT*LP weights, this image's valid ratios (references only)
+    // LDS: QT*LP corner offsets, QT*LP weights, and (references only) per level
+    // the image's valid ratio times the level's extent, (r_w W_l, r_h H_l)
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4* rec_o = reinterpret_cast<u32x4*>(lds);
     float4* rec_w = reinterpret_cast<float4*>(lds + (size_t)(QT << LPlog) * 16);
-    float2* rat = reinterpret_cast<float2*>(lds + (size_t)(QT << LPlog) * 32);
+    double* rsc = reinterpret_cast<double*>(lds + (size_t)(QT << LPlog) * 32);
     const int nwg_pad = (nwg + 7) & ~7;
     const int b = blockIdx.x;
     const int L = (b & 7) * (nwg_pad >> 3) + (b >> 3);
@@ -239,13 +252,19 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
     const uint32_t unit = (uint32_t)G.m * G.dh * 4u;   // bytes from one value row to the next
 
     if constexpr (REF != 0) {
-        if (tid < G.L)
-            rat[tid] = src.ratio ? make_float2(src.ratio[((long)n * G.L + tid) * 2], src.ratio[((long)n * G.L + tid) * 2 + 1])
-                                 : make_float2(1.f, 1.f);
+        if (tid < 2 * G.L) {
+            const int l = tid >> 1, ax = tid & 1;   // ax 0: width, 1: height
+            const double r = src.ratio ? (double)src.ratio[((long)n * G.L + l) * 2 + ax] : 1.0;
+            rsc[tid] = r * (double)(ax ? G.H[l] : G.W[l]);   // exact: a 24-bit by <= 24-bit product
+        }
         __syncthreads();
     }
 
     // ---- phase 1: sample records
+    // The padding mask (references only) through a buffer resource: two cell
+    // pairs per sample, (y0, x0..x0+1) and (y0+1, x0..x0+1), one 8-byte load each.
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)src.pad, (short)0, (int)((((long)G.n * G.S) + 3) & ~3L), 0x00020000);
     const int nsamp = QT << LPlog;
     for (int s = tid; s < nsamp; s += nthr) {
         const int qi = s >> LPlog, i = s & (LP - 1);
@@ -266,9 +285,28 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
         const int Hl = G.H[l], Wl = G.W[l];
         u32x4 o = {MS_OOB, MS_OOB, MS_OOB, MS_OOB};
         float4 w = {0.f, 0.f, 0.f, 0.f};
-        double u, v;
-        sample_uv<REF>(G, src, n, qc, item, l, i, u, v, rat);
-        const double x = u * Wl - 0.5, y = v * Hl - 0.5;
+        // Pixel coordinates x = u W_l - 1/2, y = v H_l - 1/2, in fp64.  With a
+        // reference, u W_l is written out: x = x_ref (r_w W_l) + dx for a point,
+        // x = (r_w W_l)(x_ref + dx w / (2P)) for a box (the offset term of u
+        // times W_l), each one or two fp64 FMAs of exact products.
+        double x, y;
+        {
+            const float2 t = *reinterpret_cast<const float2*>(src.loc + (item * LP + i) * 2);
+            if constexpr (REF == 0) {
+                x = (double)t.x * Wl - 0.5;
+                y = (double)t.y * Hl - 0.5;
+            } else {
+                const float* r = src.ref + ((long)n * G.q + qc) * REF;
+                const double sw = rsc[2 * l], sh = rsc[2 * l + 1];
+                if constexpr (REF == 2) {
+                    x = fma((double)r[0], sw, (double)t.x - 0.5);
+                    y = fma((double)r[1], sh, (double)t.y - 0.5);
+                } else {
+                    x = fma(sw, fma((double)t.x * (double)r[2], G.half_inv_p, (double)r[0]), -0.5);
+                    y = fma(sh, fma((double)t.y * (double)r[3], G.half_inv_p, (double)r[1]), -0.5);
+                }
+            }
+        }
         if (valid && x > -1.0 && x < (double)Wl && y > -1.0 && y < (double)Hl) {
             const double fx = floor(x), fy = floor(y);
             const float a = (float)(x - fx), bb = (float)(y - fy);
@@ -281,11 +319,15 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
             const uint32_t base = (uint32_t)(row * G.m + h) * (uint32_t)(G.dh * 4);
             const uint32_t down = (uint32_t)Wl * unit;
             const bool cx0 = x0 >= 0, cx1 = x0 + 1 < Wl, cy0 = y0 >= 0, cy1 = y0 + 1 < Hl;
-            const long cell = (long)G.start[l] + (long)y0 * Wl + x0;
-            o.x = (cy0 && cx0 && !padded(src, G, n, cell)) ? base : MS_OOB;
-            o.y = (cy0 && cx1 && !padded(src, G, n, cell + 1)) ? base + unit : MS_OOB;
-            o.z = (cy1 && cx0 && !padded(src, G, n, cell + Wl)) ? base + down : MS_OOB;
-            o.w = (cy1 && cx1 && !padded(src, G, n, cell + Wl + 1)) ? base + down + unit : MS_OOB;
+            uint32_t padm = 0;   // bits: 00, 01, 10, 11 corners padded
+            if (REF != 0 && src.pad) {
+                const uint32_t byte = (uint32_t)((long)n * G.S + G.start[l] + (long)y0 * Wl + x0);
+                padm = pad_pair(pr, byte) | (pad_pair(pr, byte + (uint32_t)Wl) << 2);
+            }
+            o.x = (cy0 && cx0 && !(padm & 1u)) ? base : MS_OOB;
+            o.y = (cy0 && cx1 && !(padm & 2u)) ? base + unit : MS_OOB;
+            o.z = (cy1 && cx0 && !(padm & 4u)) ? base + down : MS_OOB;
+            o.w = (cy1 && cx1 && !(padm & 8u)) ? base + down + unit : MS_OOB;
         }
         rec_o[s] = o;
         rec_w[s] = w;
@@ -386,7 +428,7 @@ hipError_t launch_src(const MsdaGeom& G, const float* value, const MsdaSrc& src,
         const long nwg = (long)G.n * G.m * tiles;
         if (nwg < (1L << 30)) {
             const dim3 grid((unsigned)((nwg + 7) & ~7L)), blk((unsigned)(QT * LQ));
-            const size_t lds = (size_t)QT * LP * 32 + MSDA_MAX_LEVELS * sizeof(float2);
+            const size_t lds = (size_t)QT * LP * 32 + MSDA_MAX_LEVELS * 2 * sizeof(double);
             if (G.softmax)
                 msda_fwd_tile<true, REF><<<grid, blk, lds, s>>>(G, LPlog, LQlog, QT, tiles, (int)nwg,
                                                                 (uint32_t)value_bytes, value, src, attn, out);
