@@ -54,6 +54,20 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                  "-shared-libsan"]
+
+
+def build_sanitized(path: str, cc: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """Compile the C oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    into ``path`` (clang, so that it shares one sanitizer runtime with the
+    sanitized host build of libdcn).  The process that loads it must preload
+    that runtime; ORACLE_LIB_PATH=path makes this module load it."""
+    subprocess.check_call([cc, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off"] +
+                          SANITIZE_FLAGS + ["-o", path, _SRC, "-lm"])
+    return path
+
+
 class _Dcn(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in
                 ("n", "h", "w", "c", "group", "kernel_h", "kernel_w", "stride_h", "stride_w",
@@ -69,8 +83,10 @@ class _Msda(ctypes.Structure):
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
+        # ORACLE_LIB_PATH names another build of dcn_oracle.c (the sanitized
+        # one); the default is the gcc build above.
+        path = os.environ.get("ORACLE_LIB_PATH") or build(force=False)
+        lib = ctypes.CDLL(path)
         pd = ctypes.POINTER(ctypes.c_double)
         lib.oracle_dcn_out_size.argtypes = [ctypes.POINTER(_Dcn), ctypes.POINTER(ctypes.c_int),
                                             ctypes.POINTER(ctypes.c_int)]

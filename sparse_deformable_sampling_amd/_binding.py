@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdcn.so")
+# LIBDCN_PATH names another build of the same library (the sanitized host
+# build the CPU tests load); the default is the in-tree libdcn.so.
+LIB_PATH = os.environ.get("LIBDCN_PATH") or os.path.join(HERE, "libdcn.so")
 
 DCN_OK, DCN_ERR_INVALID, DCN_ERR_UNSUPPORTED, DCN_ERR_HIP = 0, 1, 2, 3
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
@@ -42,7 +44,7 @@ def lib():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(LIB_PATH) and "LIBDCN_PATH" not in os.environ:
         from . import build as _build
         _build.build()
     L = ctypes.CDLL(LIB_PATH)

@@ -37,5 +37,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(path: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer in
+    its host code only (argument checks, planning, launch set-up); the device
+    code is built as usual.  A process loads it with the compiler's
+    libclang_rt.asan preloaded and LIBDCN_PATH=path."""
+    host = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-shared-libsan"]
+    subprocess.check_call([HIPCC] + flags + host + ["-I", os.path.join(ROOT, "include"), "-o", path] + sources())
+    return path
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too)."""
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return found[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
