@@ -17,7 +17,7 @@ import numpy as np
 
 # stream ids, one per tensor
 X, OFFSET, MASK, GRAD_OUT, VALUE, REF, MSDA_OFFSET, ATTN, VALID = 1, 2, 3, 4, 5, 6, 7, 8, 9
-DW_WEIGHT, DW_BIAS, OM_WEIGHT, OM_BIAS = 10, 11, 12, 13
+DW_WEIGHT, DW_BIAS, OM_WEIGHT, OM_BIAS, MODULE_VALUE = 10, 11, 12, 13, 14
 
 DTYPES = ("f32", "f16", "bf16")
 
@@ -88,6 +88,36 @@ def frontend_inputs(n, h, w, c, group, taps=9, dtype="f16", seed=1):
             "dw_bias": store(normal((c,), 0.1, seed, DW_BIAS), dtype),
             "om_weight": store(normal((no, c), float(c) ** -0.5, seed, OM_WEIGHT), dtype),
             "om_bias": store(normal((no,), 0.1, seed, OM_BIAS), dtype)}
+
+
+def frontend_exact_inputs(n, h, w, c, group, taps=9, dtype="f16", seed=1):
+    """Front-end inputs whose depthwise sums and offset/mask outputs are all
+    exactly representable in f16 and bf16, so that no rounding happens
+    between the front-end and the core op: x integers in [-2, 2], depthwise
+    weights in {-1, -1/2, 0, 1/2, 1} and bias in {-1/2, 0, 1/2} (sums are
+    multiples of 1/2 below 19 in magnitude); each linear row has two nonzero
+    weights in {+-1/64, +-1/32} and a bias k/128 with |k| <= 32 (outputs are
+    multiples of 1/128 below 3/2 in magnitude)."""
+    no = group * taps * 3
+    rng = _rng(seed, OM_WEIGHT)
+    omw = np.zeros((no, c), np.float32)
+    for j in range(no):
+        cols = rng.choice(c, size=min(2, c), replace=False)
+        omw[j, cols] = rng.choice([-1 / 32, -1 / 64, 1 / 64, 1 / 32], size=cols.size)
+    return {"x": store(_rng(seed, X).integers(-2, 3, size=(n, h, w, c)).astype(np.float32), dtype),
+            "dw_weight": store(_rng(seed, DW_WEIGHT).choice([-1.0, -0.5, 0.0, 0.5, 1.0], size=(3, 3, c))
+                               .astype(np.float32), dtype),
+            "dw_bias": store(_rng(seed, DW_BIAS).choice([-0.5, 0.0, 0.5], size=(c,)).astype(np.float32), dtype),
+            "om_weight": store(omw, dtype),
+            "om_bias": store((_rng(seed, OM_BIAS).integers(-32, 33, size=(no,)) / 128.0).astype(np.float32), dtype)}
+
+
+def module_inputs(n, h, w, c, group, dtype="f16", seed=1):
+    """The front-end inputs (frontend_inputs) plus the core op's value tensor
+    ~ N(0,1) [n,h,w,c] (the input projection's output in a DCNv4 module)."""
+    d = frontend_inputs(n, h, w, c, group, dtype=dtype, seed=seed)
+    d["value"] = store(normal((n, h, w, c), 1.0, seed, MODULE_VALUE), dtype)
+    return d
 
 
 def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype="f32", seed=1, ref="uniform"):
