@@ -164,49 +164,20 @@ def frontend_runner(torch, stage, dtype, seed=1):
     return r
 
 
-def fused_runner(torch, stage, dtype, seed=1):
-    """DCNv4 front-end and core op in one launch (dcn_forward_fused):
-    min_bytes counts the module input, the value tensor, the weights and the
-    output once (the offsets and mask never reach memory)."""
-    from sparse_deformable_sampling_amd import _binding as B, synth
-    n, h, w, c, g = STAGES[stage]
-    d = synth.module_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
-    es = ES[dtype]
-    min_bytes = es * (sum(d[k].size for k in FRONT_KEYS) + 2 * n * h * w * c)
-    code = {"f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
-    desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, False, code)
-    base = [upload(torch, d[k], dtype) for k in FRONT_KEYS + ("value",)]
-    stream = torch.cuda.current_stream()
-    args, keep = [], []
-    for i in range(n_sets(min_bytes)):
-        ins = [base[0].clone()] + base[1:5] + [base[5].clone()] if i else base
-        out = torch.empty((n, h, w, c), dtype=ins[0].dtype, device="cuda")
-        keep += ins + [out]
-        x, dww, dwb, omw, omb, value = ins
-        args.append((ctypes.byref(desc),) + tuple(ctypes.c_void_p(t.data_ptr()) for t in (x, value, dww, dwb, omw, omb,
-                                                                                          out)) +
-                    (ctypes.c_void_p(stream.cuda_stream),))
-    r = Runner("dcnv4_fused_%s_%s" % (stage, dtype), args, B.lib().dcn_forward_fused, n * h * w * c * 9, min_bytes,
-               stream)
-    r.keep = keep
-    return r
-
-
-def module_runner(torch, stage="table10", dtype="f16", seed=1, fused=False):
+def module_runner(torch, stage="table10", dtype="f16", seed=1):
     """The whole DCNv4 module forward, as the pages measure it (Table 10):
     value = input_proj(x) and out = output_proj(core(...)) as plain library
     GEMMs (torch.mm on the same stream), the front-end and the core in
-    libdcn: two launches (dcn_offset_mask, dcn_forward) or, with fused, one
-    (dcn_forward_fused).  min_bytes sums each step's own reads and writes
-    once, x read once: 6*P*C elements for P pixels, plus 2*P*G*K*3 for the
-    offsets and mask written and read between the two launches (weights
-    aside)."""
+    libdcn (dcn_offset_mask, then dcn_forward).  min_bytes sums each step's
+    own reads and writes once, x read once: 6*P*C elements for P pixels,
+    plus 2*P*G*K*3 for the offsets and mask written and read between the
+    two launches (weights aside)."""
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, h, w, c, g = STAGES[stage]
     d = synth.frontend_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
     es = ES[dtype]
     P = n * h * w
-    min_bytes = es * (6 * P * c + (0 if fused else 2 * P * g * 27))
+    min_bytes = es * (6 * P * c + 2 * P * g * 27)
     code = {"f16": B.DCN_F16, "bf16": B.DCN_BF16}[dtype]
     desc = B.make_desc(n, h, w, c, g, 3, 1, 1, 1, 1.0, False, code)
     fe = [upload(torch, d[k], dtype) for k in FRONT_KEYS]
@@ -228,20 +199,16 @@ def module_runner(torch, stage="table10", dtype="f16", seed=1, fused=False):
 
     def step(t):
         torch.mm(t["x"].view(P, c), w_in, out=t["value"])
-        if fused:
-            st = L.dcn_forward_fused(ctypes.byref(desc), vp(t["x"].data_ptr()), vp(t["value"].data_ptr()),
-                                     *(vp(a.data_ptr()) for a in fe[1:]), vp(t["y"].data_ptr()), sp)
-        else:
-            st = L.dcn_offset_mask(ctypes.byref(desc), vp(t["x"].data_ptr()), *(vp(a.data_ptr()) for a in fe[1:]),
-                                   vp(t["off"].data_ptr()), vp(t["mask"].data_ptr()), sp)
-            if st == 0:
-                st = L.dcn_forward(ctypes.byref(desc), vp(t["value"].data_ptr()), vp(t["off"].data_ptr()),
-                                   vp(t["mask"].data_ptr()), vp(t["y"].data_ptr()), sp)
+        st = L.dcn_offset_mask(ctypes.byref(desc), vp(t["x"].data_ptr()), *(vp(a.data_ptr()) for a in fe[1:]),
+                               vp(t["off"].data_ptr()), vp(t["mask"].data_ptr()), sp)
+        if st == 0:
+            st = L.dcn_forward(ctypes.byref(desc), vp(t["value"].data_ptr()), vp(t["off"].data_ptr()),
+                               vp(t["mask"].data_ptr()), vp(t["y"].data_ptr()), sp)
         torch.mm(t["y"], w_out, out=t["out"])
         return st
 
-    r = Runner("dcnv4_module_%s%s_%s" % ("fused_" if fused else "", stage, dtype), [(t,) for t in sets], step,
-               n * h * w * c * 9, min_bytes, stream)
+    r = Runner("dcnv4_module_%s_%s" % (stage, dtype), [(t,) for t in sets], step, n * h * w * c * 9, min_bytes,
+               stream)
     r.keep = (fe, w_in, w_out, sets)
     return r
 
@@ -571,12 +538,8 @@ def main():
             parts = name.split("_")   # dcnv4_offset_mask_table10_f16
             r = frontend_runner(torch, parts[3], parts[4])
         elif name.startswith("dcnv4_module"):
-            parts = name.split("_")   # dcnv4_module_table10_f16, dcnv4_module_fused_table10_f16
-            fused = parts[2] == "fused"
-            r = module_runner(torch, parts[3 if fused else 2], parts[4 if fused else 3], fused=fused)
-        elif name.startswith("dcnv4_fused"):
-            parts = name.split("_")   # dcnv4_fused_table10_f16
-            r = fused_runner(torch, parts[2], parts[3])
+            parts = name.split("_")   # dcnv4_module_table10_f16
+            r = module_runner(torch, parts[2], parts[3])
         elif name.startswith("msda_bwd"):
             r = msda_bwd_runner(torch, gather="atomic" not in name)
         elif name.startswith("msda_fwd_ref"):
@@ -621,17 +584,11 @@ def main():
             secondary[r.name] = measure(torch, r, 100, 10)
             print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
             del r
-        for dt in ("f16", "bf16"):
-            r = fused_runner(torch, "table10", dt)
-            secondary[r.name] = measure(torch, r, 100, 10)
-            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
-            del r
-        for fused in (False, True):
-            r = module_runner(torch, "table10", "f16", fused=fused)
-            secondary[r.name] = measure(torch, r, 50, 5)
-            secondary[r.name]["context_pages_a100_fp16_ms"] = 0.873
-            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
-            del r
+        r = module_runner(torch, "table10", "f16")
+        secondary[r.name] = measure(torch, r, 50, 5)
+        secondary[r.name]["context_pages_a100_fp16_ms"] = 0.873
+        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+        del r
         r = msda_runner(torch)
         secondary[r.name] = measure(torch, r, 50, 5)
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)

@@ -182,22 +182,6 @@ dcn_status dcn_backward_noalloc(const dcn_desc* desc, const void* x, const void*
 dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_weight, const void* dw_bias,
                            const void* om_weight, const void* om_bias, void* offset, void* mask, void* stream);
 
-/* dcn_offset_mask followed by dcn_forward in one launch ("DCNv4: Unbounded
- * Weights", "1. Remove Softmax" and Table 10's whole-module timing): out =
- * core op on value ([n][h][w][c], the input projection's output) with the
- * offsets and mask the front-end computes from x_in ([n][h][w][c], the module
- * input), which never reach memory.  The front-end's arithmetic and
- * roundings are those of dcn_offset_mask (d and each offset and mask value
- * rounded to desc->dtype).  DCNv4 only: softmax 0, f16 or bf16, a 3x3 kernel
- * of stride 1, padding 1 and dilation 1, c % 8 == 0, and groups of at most 32
- * channels; otherwise, or when the window and staging area do not fit in
- * LDS, DCN_ERR_UNSUPPORTED.  x_in, value, dw_weight, dw_bias, om_weight and
- * out must be 16-byte aligned, om_bias 2-byte aligned; all are device
- * pointers owned by the caller. */
-dcn_status dcn_forward_fused(const dcn_desc* desc, const void* x_in, const void* value, const void* dw_weight,
-                             const void* dw_bias, const void* om_weight, const void* om_bias, void* out,
-                             void* stream);
-
 /* Multi-scale deformable attention sampling core (see above).
  * spatial_shapes: HOST array [levels][2] = (H_l, W_l), each >= 1.
  * value, loc, attn, out: device pointers in f32.  Element counts below 2^31. */

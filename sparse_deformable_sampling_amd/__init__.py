@@ -27,7 +27,7 @@ import ctypes
 
 from . import _binding as _b
 
-__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "dcnv4_offset_mask", "dcnv4_forward_fused", "msda_forward", "msda_forward_ref",
+__all__ = ["dcn_output_size", "dcn_forward", "dcn_backward", "dcnv4_offset_mask", "msda_forward", "msda_forward_ref",
            "msda_backward", "DcnError"]
 
 DcnError = _b.DcnError
@@ -147,29 +147,6 @@ def dcnv4_offset_mask(x, dw_weight, dw_bias, om_weight, om_bias, group, kernel=3
     _b.check(_b.lib().dcn_offset_mask(ctypes.byref(desc), _ptr(x), _ptr(dw_weight), _ptr(dw_bias), _ptr(om_weight),
                                       _ptr(om_bias), _ptr(offset), _ptr(mask), _stream(dev)))
     return offset, mask
-
-
-def dcnv4_forward_fused(x_in, value, dw_weight, dw_bias, om_weight, om_bias, group, out=None):
-    """DCNv4 front-end and core op in one launch: the core op (3x3, stride 1,
-    padding 1, no softmax) on value [n,h,w,c] with the offsets and mask that
-    dcnv4_offset_mask would compute from x_in [n,h,w,c].  f16 or bf16."""
-    dev = _check_tensors(x_in, value, dw_weight, dw_bias, om_weight, om_bias)
-    n, h, w, c = x_in.shape
-    if tuple(value.shape) != (n, h, w, c) or value.dtype != x_in.dtype:
-        raise ValueError("value must have x_in's shape and dtype")
-    if tuple(dw_weight.shape) != (3, 3, c) or tuple(dw_bias.shape) != (c,) or \
-            tuple(om_weight.shape) != (group * 27, c) or tuple(om_bias.shape) != (group * 27,):
-        raise ValueError("dw_weight [3,3,c], dw_bias [c], om_weight [group*27, c], om_bias [group*27] expected")
-    if out is None:
-        out = _torch().empty_like(value)
-    else:
-        _check_tensors(value, out)
-        if tuple(out.shape) != (n, h, w, c):
-            raise ValueError("out must be %s" % ((n, h, w, c),))
-    desc = _b.make_desc(n, h, w, c, group, 3, 1, 1, 1, 1.0, False, _dtype_code(value))
-    _b.check(_b.lib().dcn_forward_fused(ctypes.byref(desc), _ptr(x_in), _ptr(value), _ptr(dw_weight), _ptr(dw_bias),
-                                        _ptr(om_weight), _ptr(om_bias), _ptr(out), _stream(dev)))
-    return out
 
 
 def msda_forward(value, spatial_shapes, loc, attn, softmax=True, out=None):

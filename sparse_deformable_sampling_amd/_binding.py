@@ -32,7 +32,7 @@ class MsdaDesc(ctypes.Structure):
 
 
 EXPORTS = ("dcn_output_size", "dcn_forward", "dcn_backward", "dcn_backward_workspace_size", "dcn_backward_ws",
-           "dcn_backward_noalloc", "dcn_offset_mask", "dcn_forward_fused",
+           "dcn_backward_noalloc", "dcn_offset_mask",
            "msda_forward", "msda_forward_ref", "msda_backward", "msda_backward_workspace_size", "msda_backward_ws",
            "dcn_status_str", "dcn_last_error")
 
@@ -66,8 +66,6 @@ def lib():
     L.msda_forward.restype = ctypes.c_int
     L.dcn_offset_mask.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]
     L.dcn_offset_mask.restype = ctypes.c_int
-    L.dcn_forward_fused.argtypes = [ctypes.POINTER(DcnDesc), vp, vp, vp, vp, vp, vp, vp, vp]
-    L.dcn_forward_fused.restype = ctypes.c_int
     L.msda_forward_ref.argtypes = [ctypes.POINTER(MsdaDesc), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp, vp,
                                    vp, vp, vp, vp, vp]
     L.msda_forward_ref.restype = ctypes.c_int

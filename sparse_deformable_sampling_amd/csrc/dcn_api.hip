@@ -275,38 +275,6 @@ dcn_status dcn_offset_mask(const dcn_desc* desc, const void* x, const void* dw_w
                                                   mask, (hipStream_t)stream));
 }
 
-dcn_status dcn_forward_fused(const dcn_desc* desc, const void* x_in, const void* value, const void* dw_weight,
-                             const void* dw_bias, const void* om_weight, const void* om_bias, void* out, void* stream)
-{
-    dcn::Geom G;
-    dcn_status st = make_geom(desc, &G);
-    if (st != DCN_OK) return st;
-    if (desc->dtype == DCN_F32) return fail(DCN_ERR_UNSUPPORTED, "dcn_forward_fused supports f16 and bf16");
-    if (desc->softmax) return fail(DCN_ERR_UNSUPPORTED, "dcn_forward_fused is the DCNv4 path (softmax = 0)");
-    if (G.kh != 3 || G.kw != 3 || G.sh != 1 || G.sw != 1 || G.ph != 1 || G.pw != 1 || G.dh != 1 || G.dw != 1)
-        return fail(DCN_ERR_UNSUPPORTED, "dcn_forward_fused needs a 3x3 kernel, stride 1, padding 1, dilation 1");
-    if (G.c % 8) return fail(DCN_ERR_UNSUPPORTED, "dcn_forward_fused needs c %% 8 == 0");
-    if ((st = check_ptr(x_in, "x_in", 16)) || (st = check_ptr(value, "value", 16)) ||
-        (st = check_ptr(dw_weight, "dw_weight", 16)) || (st = check_ptr(dw_bias, "dw_bias", 16)) ||
-        (st = check_ptr(om_weight, "om_weight", 16)) || (st = check_ptr(om_bias, "om_bias", 2)) ||
-        (st = check_ptr(out, "out", 16)))
-        return st;
-    if ((int64_t)G.c * G.g * G.K * 3 >= kMaxElems) return fail(DCN_ERR_INVALID, "an element count reaches 2^31");
-    int lds_limit = 65536, num_cus = 256;
-    dcn::device_limits(&lds_limit, &num_cus);
-    dcn::RingCfg rc;
-    dcn::FrontArgs fa;
-    if (!dcn::plan_ring_fused(G, desc->dtype, lds_limit, num_cus, &rc, &fa))
-        return fail(DCN_ERR_UNSUPPORTED, "dcn_forward_fused: groups wider than 64 bytes, or the window and the "
-                    "staging area do not fit in LDS");
-    fa.xin = x_in;
-    fa.dww = dw_weight;
-    fa.dwb = dw_bias;
-    fa.omw = om_weight;
-    fa.omb = om_bias;
-    return hip_status(dcn::launch_dcn_forward_fused(G, rc, fa, desc->dtype, value, out, (hipStream_t)stream));
-}
-
 // Validation shared by the MSDA entry points; fills G on success.
 static dcn_status msda_geom(const msda_desc* d, const int32_t* shapes, dcn::MsdaGeom& G)
 {

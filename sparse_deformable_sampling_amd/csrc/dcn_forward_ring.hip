@@ -83,61 +83,10 @@ __device__ __forceinline__ float h2f(uint32_t h16)
     return __uint_as_float(h16 << 16);
 }
 
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-// Front-end helpers of the fused kernel.  One 16x16x32 product-accumulate
-// (a: 16 weight rows, b: 16 pixels; lane l holds row / column l%16, k block
-// l/16, and ends with outputs 4*(l/16)..+3 of pixel l%16).
-template <int DT>
-__device__ __forceinline__ f4_t fe_mfma(u32x4 a, u32x4 b, f4_t c)
-{
-    if constexpr (DT == DT_F16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c, 0,
-                                                      0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c, 0,
-                                                       0, 0);
-}
-
-// acc[u] += w[u] * x[u] over 8 storage-type values of each.
-template <int DT>
-__device__ __forceinline__ void fe_fma8(u32x4 w, u32x4 x, float* acc)
-{
-    const uint32_t a[4] = {w.x, w.y, w.z, w.w}, b[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(h2f<DT>(a[i] & 0xffffu), h2f<DT>(b[i] & 0xffffu), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(h2f<DT>(a[i] >> 16), h2f<DT>(b[i] >> 16), acc[2 * i + 1]);
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t fe_pack2(float a, float b)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<DT>(a)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<DT>(b)) << 16);
-}
-
-// NCBM > 0: the fused kernel.  The offsets and mask are not read from
-// memory: each step's are computed in the workgroup from the module input
-// by the DCNv4 front-end ("DCNv4: Unbounded Weights", "1. Remove Softmax":
-// a depthwise 3x3 convolution, then one linear layer to the G*K*3 offsets
-// and modulation scalars) and staged in LDS, 56 bytes per item (the 18
-// offset and 9 mask values of its group, one pad).  Wave w takes units
-// (16-column strip, pair of output rows) w, w + 8, ...; a lane computes the
-// depthwise sums of one pixel column for 8 channels of one 32-channel k step
-// straight into the matrix-core operand layout (lane l: pixel l%16, channels
-// 8*(l/16)..+7 of the step), rounds them to the storage type like the
-// two-kernel path, and multiplies them with the set's 28*gs linear rows
-// (NCBM 16-row blocks, read from L2) on the matrix cores.  A step's
-// front-end runs after its core work, for the next step; the core reads the
-// staging area at the start of a step, before a barrier that frees it.
-template <int DT, int KH, int KW, bool SOFTMAX, int NCH, int WMAX, int NCBM = 0>
+template <int DT, int KH, int KW, bool SOFTMAX, int NCH, int WMAX>
 __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX / 4, WMAX / 4))) void dcn_fwd_ring(
     Geom G, RingCfg rc, const typename Elem<DT>::T* __restrict__ x, const typename Elem<DT>::T* __restrict__ off,
-    const typename Elem<DT>::T* __restrict__ mask, typename Elem<DT>::T* __restrict__ out, FrontArgs fa)
+    const typename Elem<DT>::T* __restrict__ mask, typename Elem<DT>::T* __restrict__ out)
 {
     using T = typename Elem<DT>::T;
     constexpr int ES = sizeof(T);
@@ -146,10 +95,6 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     constexpr uint32_t K2B = KF * 2 * ES;    // offset bytes of one item
     constexpr uint32_t KMB = KF * ES;        // mask bytes of one item
     static_assert(KF > 0, "ring kernel is instantiated for fixed kernels");
-    constexpr bool FUSED = NCBM > 0;
-    constexpr uint32_t SB = 56;              // staging bytes per item (fused)
-    constexpr int FR = DT == DT_F16 ? 2 : 1; // output rows per front-end unit (bf16: registers)
-    static_assert(!FUSED || (ES == 2 && !SOFTMAX && KF == 9 && WMAX == 8), "fused kernel: DCNv4, 3x3, f16/bf16");
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* ring = lds;
 
@@ -250,149 +195,6 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         }
     };
 
-    // Fused: the front-end of step st into the staging area (see above).
-    unsigned char* stage = lds + fa.s_off;
-    auto front = [&](int st) {
-        if constexpr (FUSED) {
-            const __amdgpu_buffer_rsrc_t xir =
-                __builtin_amdgcn_make_buffer_rsrc((void*)fa.xin, (short)0, (int)rc.x_bytes, 0x00020000);
-            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)fa.omw, (short)0, G.g * KF * 3 * G.c * ES, 0x00020000);
-            const __amdgpu_buffer_rsrc_t dwr =
-                __builtin_amdgcn_make_buffer_rsrc((void*)fa.dww, (short)0, 9 * G.c * ES, 0x00020000);
-            const __amdgpu_buffer_rsrc_t dbr =
-                __builtin_amdgcn_make_buffer_rsrc((void*)fa.dwb, (short)0, G.c * ES, 0x00020000);
-            const __amdgpu_buffer_rsrc_t obr =
-                __builtin_amdgcn_make_buffer_rsrc((void*)fa.omb, (short)0, G.g * KF * 3 * ES, 0x00020000);
-            const int r0 = r_begin + st * rc.tr;
-            const int nrow = min(rc.tr, r_end - r0);
-            const int nstrip = (G.w + 15) >> 4;
-            const int units = nstrip * ((nrow + FR - 1) / FR);
-            const int p = lane & 15, kq = lane >> 4;
-            // linear row of set row j: offsets (g*K + k)*2 + 0/1 at j%28 < 18,
-            // mask g*K + k after all G*K*2 offsets at 18 <= j%28 < 27
-            auto lin_row = [&](int j) -> int {
-                const int q = j % 28, gg = g0 + j / 28;
-                if (j / 28 >= rc.gs || q == 27) return -1;
-                return q < 18 ? gg * 18 + q : G.g * 18 + gg * 9 + (q - 18);
-            };
-            uint32_t arow[NCBM];
-#pragma unroll
-            for (int cb = 0; cb < NCBM; ++cb) {
-                const int lr = cb < fa.ncb ? lin_row(cb * 16 + p) : -1;
-                arow[cb] = lr < 0 ? OOB : (uint32_t)lr * (uint32_t)G.c * ES;
-            }
-            const uint32_t colB = (uint32_t)G.c * ES;
-#pragma unroll 1
-            for (int u = wave; u < units; u += nwaves) {
-                const int rp = u / nstrip, sx = u - rp * nstrip;
-                const int ra = r0 + FR * rp;
-                const int xc = sx * 16 + p;
-                // the sums start from the linear layer's bias of the lane's
-                // four outputs (zero for pad rows)
-                f4_t acc[FR][NCBM];
-#pragma unroll
-                for (int cb = 0; cb < NCBM; ++cb) {
-                    f4_t b;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int lr = cb < fa.ncb ? lin_row(cb * 16 + 4 * kq + i) : -1;
-                        b[i] = h2f<DT>(__builtin_amdgcn_raw_buffer_load_b16(obr, lr < 0 ? OOB : (uint32_t)lr * ES, 0, 0));
-                    }
-#pragma unroll
-                    for (int rr = 0; rr < FR; ++rr) acc[rr][cb] = b;
-                }
-#pragma unroll 1
-                for (int ks = 0; ks < fa.ks; ++ks) {
-                    const int ch = ks * 32 + kq * 8;
-                    const bool chv = ch < G.c;
-                    u32x4 af[NCBM];
-#pragma unroll
-                    for (int cb = 0; cb < NCBM; ++cb)
-                        af[cb] = __builtin_amdgcn_raw_buffer_load_b128(
-                            wr, (arow[cb] != OOB && chv) ? arow[cb] + (uint32_t)ch * ES : OOB, 0, 0);
-                    u32x4 wt[9];
-#pragma unroll
-                    for (int t = 0; t < 9; ++t)
-                        wt[t] = __builtin_amdgcn_raw_buffer_load_b128(dwr, chv ? (uint32_t)(t * G.c + ch) * ES : OOB, 0,
-                                                                      0);
-                    float d[FR][8];
-                    {
-                        const u32x4 bz = __builtin_amdgcn_raw_buffer_load_b128(dbr, chv ? (uint32_t)ch * ES : OOB, 0, 0);
-                        const uint32_t bw[4] = {bz.x, bz.y, bz.z, bz.w};
-#pragma unroll
-                        for (int rr = 0; rr < FR; ++rr)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                d[rr][2 * i] = h2f<DT>(bw[i] & 0xffffu);
-                                d[rr][2 * i + 1] = h2f<DT>(bw[i] >> 16);
-                            }
-                    }
-                    // input rows ra-1 .. ra+FR: output row ra+rr takes taps
-                    // from rows rr .. rr+2, zero outside the image; all the
-                    // reads in flight before the sums
-                    u32x4 X[FR + 2][3];
-#pragma unroll
-                    for (int i = 0; i < FR + 2; ++i) {
-                        const int yy = ra - 1 + i;
-                        const bool rowok = chv && (unsigned)yy < (unsigned)G.h;
-#pragma unroll
-                        for (int j = 0; j < 3; ++j) {
-                            const int xx = xc - 1 + j;
-                            const bool ok = rowok && (unsigned)xx < (unsigned)G.w;
-                            X[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                                xir, ok ? n * img_bytes + (uint32_t)yy * row_bytes + (uint32_t)xx * colB + (uint32_t)ch * ES
-                                        : OOB,
-                                0, 0);
-                        }
-                    }
-                    // weights stay packed until their use (widened all at once
-                    // they would take 72 registers)
-#pragma unroll
-                    for (int i = 0; i < FR + 2; ++i) {
-#pragma unroll
-                        for (int j = 0; j < 3; ++j) {
-#pragma unroll
-                            for (int rr = 0; rr < FR; ++rr) {
-                                if (i < rr || i > rr + 2) continue;
-                                u32x4 w = wt[(i - rr) * 3 + j];
-                                asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-                                fe_fma8<DT>(w, X[i][j], d[rr]);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int rr = 0; rr < FR; ++rr) {
-                        const u32x4 bv = {fe_pack2<DT>(d[rr][0], d[rr][1]), fe_pack2<DT>(d[rr][2], d[rr][3]),
-                                          fe_pack2<DT>(d[rr][4], d[rr][5]), fe_pack2<DT>(d[rr][6], d[rr][7])};
-#pragma unroll
-                        for (int cb = 0; cb < NCBM; ++cb) acc[rr][cb] = fe_mfma<DT>(af[cb], bv, acc[rr][cb]);
-                    }
-                }
-                // outputs 4*kq + 16*cb .. +3 of pixel (row, xc): one 8-byte
-                // write into the item's staging row (28 = 7 * 4 keeps a quad
-                // within one group)
-                if (xc < G.w) {
-#pragma unroll
-                    for (int rr = 0; rr < FR; ++rr) {
-                        const int rl2 = FR * rp + rr;
-                        if (rl2 >= nrow) continue;
-#pragma unroll
-                        for (int cb = 0; cb < NCBM; ++cb) {
-                            const int j0 = cb * 16 + 4 * kq;
-                            const int gl2 = j0 / 28, q0 = j0 - gl2 * 28;
-                            if (cb >= fa.ncb || gl2 >= rc.gs) continue;
-                            const f4_t v = acc[rr][cb];
-                            const int item_s = rl2 * (G.wo * rc.gs) + xc * rc.gs + gl2;
-                            *reinterpret_cast<uint2*>(stage + item_s * SB + q0 * 2) =
-                                make_uint2(fe_pack2<DT>(v[0], v[1]), fe_pack2<DT>(v[2], v[3]));
-                        }
-                    }
-                }
-            }
-        }
-    };
-
     // Zero the border columns of every ring slot, mirror included (never
     // written again): LDS columns 0, 1 (image columns -2, -1) and W+2 (image
     // column W).
@@ -405,8 +207,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         }
     }
     for (int rr = 0; rr < rc.nw; ++rr) load_row(lo0 + rr);
-    if constexpr (FUSED) front(0);
-    else load_offsets(0);
+    load_offsets(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -435,24 +236,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         // in flight.
         float dx[KF], dy[KF], m[KF];
         uint32_t pc[KF];
-        if constexpr (FUSED) {
-            // this lane's item from the staging area, which is free for the
-            // next step's front-end once every wave has passed the barrier
-            const unsigned char* sp = stage + (uint32_t)min(tid, rc.tr * items_row - 1) * SB;
-            uint32_t sw[14];
-#pragma unroll
-            for (int i = 0; i < 7; ++i) {
-                const uint2 v = *reinterpret_cast<const uint2*>(sp + 8 * i);
-                sw[2 * i] = v.x;
-                sw[2 * i + 1] = v.y;
-            }
-#pragma unroll
-            for (int k = 0; k < KF; ++k) {
-                pc[k] = sw[k];
-                m[k] = h2f<DT>((k & 1) ? sw[9 + (k >> 1)] >> 16 : sw[9 + (k >> 1)] & 0xffffu);
-            }
-            __syncthreads();
-        } else if constexpr (ES == 4) {
+        if constexpr (ES == 4) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
                 dx[k] = __uint_as_float(po[2 * k]);
@@ -472,7 +256,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
 
         // ---- the next step's new rows go straight to LDS, its offsets to registers
         if (s + 1 < nsteps) {
-            if constexpr (!FUSED) load_offsets(s + 1);
+            load_offsets(s + 1);
             for (int rr = 0; rr < adv; ++rr) load_row(lo + rc.nw + rr);
         }
 
@@ -622,20 +406,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                     fb &= fb - 1u;
                     const int kx = k / KH, ky = k - kx * KH;
                     float dxk, dyk, mk;
-                    if constexpr (FUSED) {
-                        // the tap's offsets and mask from registers (a select
-                        // chain: a dynamic index would move them to scratch)
-                        uint32_t pk = pc[0];
-                        float mk0 = m[0];
-#pragma unroll
-                        for (int j = 1; j < KF; ++j) {
-                            pk = k == j ? pc[j] : pk;
-                            mk0 = k == j ? m[j] : mk0;
-                        }
-                        dxk = h2f<DT>(pk & 0xffffu);
-                        dyk = h2f<DT>(pk >> 16);
-                        mk = mk0;
-                    } else if constexpr (ES == 4) {
+                    if constexpr (ES == 4) {
                         const uint32_t o = item * K2B + 8u * k;
                         dxk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, o, 0, 0));
                         dyk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, o + 4u, 0, 0));
@@ -674,9 +445,6 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
 #pragma unroll
             for (int q = 0; q < NCH; ++q) store_vec<DT>(op + q * V, acc + q * V);
         }
-        if constexpr (FUSED) {
-            if (s + 1 < nsteps) front(s + 1);
-        }
 
         __builtin_amdgcn_s_waitcnt(0);   // this wave's buffer-to-LDS loads have landed
         __syncthreads();
@@ -692,7 +460,7 @@ hipError_t launch_one(const Geom& G, const RingCfg& rc, const void* x, const voi
     const hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, rc.lds_bytes);
     if (e != hipSuccess) return e;
     fn<<<dim3(rc.nwg), dim3(rc.threads), rc.lds_bytes, s>>>(G, rc, (const T*)x, (const T*)off, (const T*)mask,
-                                                             (T*)out, FrontArgs{});
+                                                             (T*)out);
     return hipGetLastError();
 }
 
@@ -718,49 +486,7 @@ hipError_t launch_ring_typed(const Geom& G, const RingCfg& rc, const void* x, co
     return hipErrorInvalidValue;
 }
 
-template <int DT, int NCHV, int NCBM>
-hipError_t launch_fused_one(const Geom& G, const RingCfg& rc, const FrontArgs& fa, const void* value, void* out,
-                            hipStream_t s)
-{
-    using T = typename Elem<DT>::T;
-    auto* fn = dcn_fwd_ring<DT, 3, 3, false, NCHV, 8, NCBM>;
-    const hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, rc.lds_bytes);
-    if (e != hipSuccess) return e;
-    fn<<<dim3(rc.nwg), dim3(rc.threads), rc.lds_bytes, s>>>(G, rc, (const T*)value, nullptr, nullptr, (T*)out, fa);
-    return hipGetLastError();
-}
-
-template <int DT, int NCHV>
-hipError_t launch_fused_nch(const Geom& G, const RingCfg& rc, const FrontArgs& fa, const void* value, void* out,
-                            hipStream_t s)
-{
-    if (fa.ncb <= 2) return launch_fused_one<DT, NCHV, 2>(G, rc, fa, value, out, s);
-    if (fa.ncb <= 4) return launch_fused_one<DT, NCHV, 4>(G, rc, fa, value, out, s);
-    return hipErrorInvalidValue;
-}
-
-template <int DT>
-hipError_t launch_fused_typed(const Geom& G, const RingCfg& rc, const FrontArgs& fa, const void* value, void* out,
-                              hipStream_t s)
-{
-    switch (G.d * 2 / 16) {
-        case 1: return launch_fused_nch<DT, 1>(G, rc, fa, value, out, s);
-        case 2: return launch_fused_nch<DT, 2>(G, rc, fa, value, out, s);
-        case 4: return launch_fused_nch<DT, 4>(G, rc, fa, value, out, s);
-    }
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
-
-hipError_t launch_dcn_forward_fused(const Geom& G, const RingCfg& rc, const FrontArgs& fa, int dtype,
-                                    const void* value, void* out, hipStream_t s)
-{
-    if (G.softmax || G.d * 2 % 16 != 0) return hipErrorInvalidValue;
-    if (dtype == DT_F16) return launch_fused_typed<DT_F16>(G, rc, fa, value, out, s);
-    if (dtype == DT_BF16) return launch_fused_typed<DT_BF16>(G, rc, fa, value, out, s);
-    return hipErrorInvalidValue;
-}
 
 hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
                                    const void* mask, void* out, hipStream_t s)
@@ -778,17 +504,13 @@ hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, 
 
 // Choose the group set, rows per step, halo and chunking for geometry G, or
 // return false when the sliding-window kernel does not apply.
-namespace {
-
-// The ring plan.  stage_item: LDS bytes per item besides the ring (the fused
-// kernel's staging area); hy_min: the least halo accepted; max_gs: the most
-// groups per workgroup; wide_ok: 1024-thread workgroups allowed.
-bool plan_ring_impl(const Geom& G0, int dtype, int lds_limit, int num_cus, int stage_item, int hy_min, int max_gs,
-                    bool wide_ok, RingCfg* rc, Geom* gk)
+bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const void* mask, const void* out,
+               int lds_limit, int num_cus, RingCfg* rc, Geom* gk)
 {
     if (G0.kh != 3 || G0.kw != 3) return false;
     const int es = dtype == DT_F32 ? 4 : 2;
     if (G0.d * es % 16 != 0) return false;
+    if ((uintptr_t)x % 16 || (uintptr_t)off % 16 || (uintptr_t)mask % 16 || (uintptr_t)out % 16) return false;
     const long x_bytes = (long)G0.n * G0.h * G0.w * G0.c * es;
     const long off_bytes = (long)G0.items * G0.K * 2 * es, mask_bytes = (long)G0.items * G0.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
@@ -814,10 +536,10 @@ bool plan_ring_impl(const Geom& G0, int dtype, int lds_limit, int num_cus, int s
     // For a target number of items per step, try group sets from all groups
     // down; take the first that keeps a halo of at least HY_MIN rows in LDS
     // with one workgroup per CU.
-    const int HY_MIN = hy_min, HY_MAX = 8;
+    const int HY_MIN = 4, HY_MAX = 8;
     auto try_plan = [&](int target) -> bool {
         const int max_thr = target > 448 ? 1024 : 512;
-        for (int gs = std::min(G.g, max_gs); gs >= 1; --gs) {
+        for (int gs = G.g; gs >= 1; --gs) {
             if (G.g % gs) continue;
             const int items_row = G.wo * gs;
             if (items_row > max_thr) continue;
@@ -834,12 +556,11 @@ bool plan_ring_impl(const Geom& G0, int dtype, int lds_limit, int num_cus, int s
             const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
             if (row_iters > 4) continue;   // ROW_IT
             const int adv = tr * G.sh;
-            const long budget = lds_limit - ((long)items_step * stage_item + 15) / 16 * 16;
             int hy = -1, nw = 0, R = 0;
             for (int h = HY_MAX; h >= HY_MIN; --h) {
                 const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
                 const int Rh = nwh + adv;
-                if ((long)(Rh + 1) * pitch <= budget) {
+                if ((long)(Rh + 1) * pitch <= lds_limit) {
                     hy = h;
                     nw = nwh;
                     R = Rh;
@@ -886,39 +607,7 @@ bool plan_ring_impl(const Geom& G0, int dtype, int lds_limit, int num_cus, int s
     // Where a tap's data and the prefetched offsets fit in 128 VGPRs (nch * es
     // <= 4: f16/bf16 with D <= 16, f32 with D = 4), a 1024-thread workgroup
     // (four waves per SIMD) hides the LDS latency better; try that first.
-    return (wide_ok && nch * es <= 4 && try_plan(896)) || try_plan(448);
-}
-
-}  // namespace
-
-bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const void* mask, const void* out,
-               int lds_limit, int num_cus, RingCfg* rc, Geom* gk)
-{
-    if ((uintptr_t)x % 16 || (uintptr_t)off % 16 || (uintptr_t)mask % 16 || (uintptr_t)out % 16) return false;
-    return plan_ring_impl(G0, dtype, lds_limit, num_cus, 0, 4, G0.g << 6, true, rc, gk);
-}
-
-bool plan_ring_fused(const Geom& G, int dtype, int lds_limit, int num_cus, RingCfg* rc, FrontArgs* fa)
-{
-    if (dtype != DT_F16 && dtype != DT_BF16) return false;
-    if (G.kh != 3 || G.kw != 3 || G.sh != 1 || G.sw != 1 || G.ph != 1 || G.pw != 1 || G.dh != 1 || G.dw != 1)
-        return false;
-    if (G.softmax || G.c % 8 != 0 || G.d * 2 > 64) return false;
-    // a group set's 28*gs staged rows in at most 4 blocks of 16 (gs <= 2):
-    // the front-end's sums for more blocks do not fit in the registers
-    Geom gk;
-    if (!plan_ring_impl(G, dtype, lds_limit, num_cus, 56, 2, 2, false, rc, &gk)) return false;
-    if (rc->split_log != 0) return false;
-    const int items_step = rc->tr * G.wo * rc->gs;
-    rc->threads = 512;   // eight waves: the front-end's units spread over all of them
-    rc->row_iters = (int)((((long)G.w * rc->cpp + 63) / 64 + 7) / 8);
-    fa->s_off = (rc->ring_bytes + 15) / 16 * 16;
-    rc->lds_bytes = fa->s_off + (items_step * 56 + 15) / 16 * 16;
-    if (rc->lds_bytes > lds_limit || items_step > 512) return false;
-    rc->off_bytes = rc->mask_bytes = 0;
-    fa->ks = (G.c + 31) / 32;
-    fa->ncb = (28 * rc->gs + 15) / 16;
-    return true;
+    return (nch * es <= 4 && try_plan(896)) || try_plan(448);
 }
 
 void device_limits(int* lds_limit, int* num_cus)

@@ -39,29 +39,6 @@ bool plan_ring(const Geom& G, int dtype, const void* x, const void* off, const v
 hipError_t launch_dcn_forward_ring(const Geom& G, const RingCfg& rc, int dtype, const void* x, const void* off,
                                    const void* mask, void* out, hipStream_t s);
 
-// The DCNv4 front-end inputs of the fused kernel (front-end and core op in
-// one launch): the module input, the depthwise 3x3 weights and bias, and the
-// merged offset/mask linear layer.
-struct FrontArgs {
-    const void* xin;      // [n][h][w][c], the storage type
-    const void* dww;      // [3][3][c]
-    const void* dwb;      // [c]
-    const void* omw;      // [g*K*3][c]
-    const void* omb;      // [g*K*3]
-    int ks;               // 32-channel MFMA k steps: ceil(c / 32)
-    int ncb;              // 16-row blocks of the group set's 28*gs staged linear rows
-    int s_off;            // LDS byte offset of the step's offset/mask staging area
-};
-
-// Plan of the fused kernel: the ring plan with LDS left for the staging area
-// (56 bytes per item), at most 2 groups per workgroup, 512 threads.  False
-// where the fused kernel does not apply (f16/bf16, a 3x3 core of stride 1,
-// padding 1, dilation 1, no softmax, c % 8 == 0, groups of at most 64 bytes).
-bool plan_ring_fused(const Geom& G, int dtype, int lds_limit, int num_cus, RingCfg* rc, FrontArgs* fa);
-
-hipError_t launch_dcn_forward_fused(const Geom& G, const RingCfg& rc, const FrontArgs& fa, int dtype,
-                                    const void* value, void* out, hipStream_t s);
-
 // Per-device properties cached on first use (LDS bytes per workgroup, CU count).
 void device_limits(int* lds_limit, int* num_cus);
 

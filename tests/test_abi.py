@@ -318,33 +318,3 @@ def test_offset_mask_validation():
         args[i] = vp(p)
         assert call(desc, args) == B.DCN_ERR_UNSUPPORTED, i
     assert L.dcn_offset_mask(None, *good, None) == B.DCN_ERR_INVALID
-
-
-def test_forward_fused_validation():
-    """The fused front-end + core takes f16/bf16, the DCNv4 core (no softmax)
-    with a 3x3 kernel of stride 1, padding 1 and dilation 1, c % 8 == 0 and
-    all seven tensors (16-byte aligned but for om_bias); each violation is
-    refused before any launch."""
-    L = B.lib()
-    vp = ctypes.c_void_p
-    good = [vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), vp(0x7000)]
-
-    def call(desc, args=good):
-        return L.dcn_forward_fused(ctypes.byref(desc), *args, None)
-
-    assert call(B.make_desc(1, 8, 8, 16, 2)) == B.DCN_ERR_UNSUPPORTED                       # f32
-    assert call(B.make_desc(1, 8, 8, 16, 2, softmax=True, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
-    assert call(B.make_desc(1, 8, 8, 12, 2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED      # c % 8
-    assert call(B.make_desc(1, 8, 8, 16, 2, stride=2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
-    assert call(B.make_desc(1, 8, 8, 16, 2, kernel=5, pad=2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
-    assert call(B.make_desc(1, 8, 8, 16, 2, dil=2, pad=2, dtype=B.DCN_F16)) == B.DCN_ERR_UNSUPPORTED
-    desc = B.make_desc(1, 8, 8, 16, 2, dtype=B.DCN_BF16)
-    for i in range(7):
-        args = list(good)
-        args[i] = None
-        assert call(desc, args) == B.DCN_ERR_INVALID, i
-    for i, p in ((0, 0x1008), (1, 0x2008), (2, 0x3004), (3, 0x4008), (4, 0x5008), (5, 0x6001), (6, 0x7004)):
-        args = list(good)
-        args[i] = vp(p)
-        assert call(desc, args) == B.DCN_ERR_UNSUPPORTED, i
-    assert L.dcn_forward_fused(None, *good, None) == B.DCN_ERR_INVALID

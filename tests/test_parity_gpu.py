@@ -916,60 +916,6 @@ def test_frontend_feeds_the_core(sds, dtype):
     assert err <= TOL[dtype]
 
 
-# ---------------------------------------------------------------- front-end and core in one launch
-
-
-def check_fused(sds, name, n, h, w, c, g, dtype, seed=1):
-    """dcn_forward_fused against the oracle's front-end followed by its core
-    op, on inputs whose front-end values are exact in the storage type (no
-    rounding between the halves, see test_frontend_feeds_the_core); then, on
-    N(0,1) inputs, item by item against the two-launch GPU path
-    (dcn_offset_mask, dcn_forward), which it must equal but where an offset
-    or mask value rounds differently (the fused sums start from the bias)."""
-    d = synth.frontend_exact_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
-    d["value"] = synth.module_inputs(n, h, w, c, g, dtype=dtype, seed=seed)["value"]
-    say(name, dtype, (n, h, w, c, g))
-
-    def fused(d):
-        dev = {k: to_dev(d[k], dtype) for k in FRONT_KEYS + ("value",)}
-        out = sds.dcnv4_forward_fused(dev["x"], dev["value"], dev["dw_weight"], dev["dw_bias"], dev["om_weight"],
-                                      dev["om_bias"], group=g)
-        return dev, to_host(out).astype(np.float64)
-
-    _, out = fused(d)
-    roff, rmask = oracle.dcnv4_offset_mask(*(d[k] for k in FRONT_KEYS), group=g, dtype=dtype)
-    ref = oracle.dcn_forward(d["value"], roff, rmask, group=g, softmax=False)
-    err = rel_err(out, ref)
-    d = synth.module_inputs(n, h, w, c, g, dtype=dtype, seed=seed)
-    dev, out = fused(d)
-    off, mask = sds.dcnv4_offset_mask(*(dev[k] for k in FRONT_KEYS), group=g)
-    two = to_host(sds.dcn_forward(dev["value"], off, mask, group=g, softmax=False)).astype(np.float64)
-    diff = np.abs(out - two).reshape(n * h * w * g, -1).max(axis=1)
-    frac = float(np.mean(diff > 1e-3 * np.sqrt(np.mean(two * two))))
-    say("  err", name, dtype, "oracle %.3e, items off the two-launch result %.2e" % (err, frac))
-    assert err <= TOL[dtype], (name, dtype, err)
-    assert np.isfinite(out).all() and frac <= 1e-2, (name, dtype, frac)
-
-
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_fused_table10_full(sds, dtype):
-    """The pages' module shape at the benched batch: 64 x 56 x 56 x 128, 4
-    groups of 32 channels (two groups per workgroup, 28 rows of four steps)."""
-    check_fused(sds, "fused-table10", 64, 56, 56, 128, 4, dtype)
-
-
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 1, 1, 8, 1), (1, 5, 33, 64, 4), (2, 9, 7, 24, 3), (1, 3, 70, 40, 5),
-                                   (2, 16, 16, 256, 8), (3, 11, 17, 32, 2), (1, 28, 28, 128, 8)])
-def test_fused_ragged_shapes(sds, dtype, shape):
-    """One pixel; a 33-wide map (a last strip with one column) of 5 rows (a
-    partial last step and row pair); C = 24 and 40 (k steps with idle lanes);
-    odd group counts (one group per workgroup); C = 256 with 8 groups of 32;
-    the stage-2 map size."""
-    n, h, w, c, g = shape
-    check_fused(sds, "fused-ragged", n, h, w, c, g, dtype, seed=41)
-
-
 # ---------------------------------------------------------------- streams
 
 
