@@ -42,7 +42,6 @@ namespace dcn {
 namespace {
 
 constexpr int FT_THREADS = 512;
-constexpr int FT_LDS_TARGET = 80 * 1024;   // two workgroups per CU
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
@@ -661,24 +660,35 @@ void layout(const Geom& G, int mb, FrontCfg* F)
     F->div_h = make_fastdiv((uint32_t)G.h);
 }
 
-// Tile plan: the largest tile whose LDS keeps two workgroups per CU and that
-// still gives a tile per CU (larger tiles reuse each weight fragment read
-// from L2 for more pixels); else the largest that fits at all.  False if
-// not even a 16-pixel tile fits.
+// Tile plan.  Every tile reads all of W_om from L2 as MFMA fragments, 16
+// rows x 64 bytes per load instruction (16 cache-line lookups per KB, the
+// vector memory's rate limit), so per CU the cost is about (tiles per CU) x
+// (W_om's fragment lines + the tile's own depthwise reads and output lines).
+// Take the tile size that fits in LDS with the least such cost (ties to the
+// larger tile).  At stage-3 (320 channels, 540 outputs) 64-pixel tiles, one
+// workgroup per CU, take 28.7 us against 33.5 for 32-pixel tiles at two per
+// CU and 50.9 for 16-pixel tiles.  False if not even a 16-pixel tile fits.
 bool plan_frontend(const Geom& G, int dtype, int lds_limit, int num_cus, FrontCfg* F)
 {
     if (dtype != DT_F16 && dtype != DT_BF16) return false;
     if (G.c % 8 != 0) return false;
     if ((long)G.n * G.h * G.w * G.c * 2 >= (1l << 31)) return false;   // buffer offsets, out-of-range marker 2^31
+    int best = 0;
+    double best_cost = 0.0;
     for (int mb = 4; mb >= 1; mb /= 2) {
         layout(G, mb, F);
-        if (F->lds_bytes <= std::min(FT_LDS_TARGET, lds_limit) && F->ntiles >= num_cus) return true;
+        if (F->lds_bytes > lds_limit) continue;
+        const double w_lines = (double)F->ncb * (F->KP / 32) * 16;
+        const double px_lines = 9.0 * G.c * 2 / 128 + (double)F->NO * 2 / 128;
+        const double cost = (double)((F->ntiles + num_cus - 1) / num_cus) * (w_lines + 16.0 * mb * px_lines);
+        if (best == 0 || cost < best_cost) {
+            best = mb;
+            best_cost = cost;
+        }
     }
-    for (int mb = 4; mb >= 1; mb /= 2) {
-        layout(G, mb, F);
-        if (F->lds_bytes <= lds_limit) return true;
-    }
-    return false;
+    if (best == 0) return false;
+    layout(G, best, F);
+    return true;
 }
 
 }  // namespace

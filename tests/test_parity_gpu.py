@@ -61,10 +61,10 @@ def test_stage1_forward_full(sds, dtype, softmax):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("softmax", [False, True])
 def test_table10_shape(sds, dtype, softmax):
-    """The pages' module shape 56x56x128, 4 groups of 32 channels (batch 16
-    of 64): f32 groups are 128 bytes per pixel and run as two 64-byte lane
-    items sharing the group's offsets and mask."""
-    check_fwd(sds, "table10", 16, 56, 56, 128, 4, dtype, softmax)
+    """The pages' module shape 56x56x128, 4 groups of 32 channels, at the
+    benched batch of 64: f32 groups are 128 bytes per pixel and run as two
+    64-byte lane items sharing the group's offsets and mask."""
+    check_fwd(sds, "table10", 64, 56, 56, 128, 4, dtype, softmax)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -858,11 +858,10 @@ def check_frontend(sds, name, n, h, w, c, g, dtype, kernel=3, dil=1, seed=1):
 @pytest.mark.parametrize("stage", ["stage1", "stage2", "stage3", "table10"])
 def test_frontend_stages_full(sds, dtype, stage):
     """The DCNv4 front-end at the three stage shapes (C=64/128/320, G=4/8/20)
-    and the pages' module shape (56x56x128, G=4), batch 8 of the full 64: the
-    kernels are per-pixel, so the smaller batch runs the same code paths
+    and the pages' module shape (56x56x128, G=4), at the benched batch of 64
     (the wave kernel for C=64/128, the tile kernel for C=320)."""
-    n, hw, c, g = {"stage1": (8, 56, 64, 4), "stage2": (8, 28, 128, 8), "stage3": (8, 14, 320, 20),
-                   "table10": (8, 56, 128, 4)}[stage]
+    n, hw, c, g = {"stage1": (64, 56, 64, 4), "stage2": (64, 28, 128, 8), "stage3": (64, 14, 320, 20),
+                   "table10": (64, 56, 128, 4)}[stage]
     check_frontend(sds, stage, n, hw, hw, c, g, dtype)
 
 
