@@ -530,12 +530,12 @@ __global__ __launch_bounds__(1024) void msda_bwd_scan(int* __restrict__ cnt, int
 // records already in flight.  A level whose blocks expect long runs gives
 // each block gpc groups (interleaved batches), summed through LDS.
 // A coarse cell gathers thousands of terms (about 1300 per head on the
-// 13x17 level of the encoder shape), so the sums are kept in fp64: a term is
-// the product of two fp32 values, exact in fp64, and the sum then carries
-// about 2^-53 of relative error per term instead of 2^-24, so a cell's
-// gradient comes out within one fp32 rounding of the exact sum of its terms.
-// fp64 FMAs issue at the rate of non-packed fp32 ones on this chip, and the
-// kernel is bound by its loads.
+// 13x17 level of the encoder shape), too many for one fp32 running sum to
+// stay within 1e-5 of the exact sum.  So each round's LPC terms are summed
+// in fp32 (a chain of LPC, about 2^-24 of relative error per term) and the
+// round sums are added in fp64, which keeps the long chain's error at about
+// 2^-53 per round.  (fp64 products for every term cost the kernel 35% more
+// time; the short fp32 chains cost nothing measurable.)
 constexpr int CB = 4;
 
 template <int LPC>
@@ -615,20 +615,32 @@ __global__ __launch_bounds__(256) void msda_bwd_cells(MsdaGeom G, MsdaSortCfg C,
 #pragma unroll
         for (int c = 0; c < CB; ++c) stage[c + 1][t] = w[c];
         wave_lds_sync();
+        // the LPC records of this round summed in fp32, the round's sum
+        // added to the fp64 total (short fp32 chains, one fp64 add per
+        // output and round instead of one fp64 product per record)
+        float part32[CB][4];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part32[c][i] = 0.f;
 #pragma unroll
         for (int u = 0; u < LPC; ++u) {
             const int src = grp * LPC + u;
             const uint32_t o = __float_as_uint(stage[0][src]);
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(gr, o == MS_OOB ? o : o + gbase, 0, 0);
-            const double gv[4] = {(double)__uint_as_float(v.x), (double)__uint_as_float(v.y),
-                                  (double)__uint_as_float(v.z), (double)__uint_as_float(v.w)};
+            const float gv[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                 __uint_as_float(v.w)};
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const double ww = (double)stage[c + 1][src];
+                const float ww = stage[c + 1][src];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[c][i] = fma(ww, gv[i], acc[c][i]);
+                for (int i = 0; i < 4; ++i) part32[c][i] = fmaf(ww, gv[i], part32[c][i]);
             }
         }
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] += (double)part32[c][i];
         wave_lds_sync();
     }
     if (gpc > 1) {   // uniform over the workgroup
