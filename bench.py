@@ -240,12 +240,14 @@ def msda_runner(torch, seed=1):
 
 def msda_ref_runner(torch, seed=1):
     """MSDA read with locations formed in the kernel: the encoder shape with
-    point references, per-image valid ratios and right/bottom padding.
-    min_bytes: value, offsets, attn and out once, plus the references,
-    ratios and the byte mask."""
+    per-image valid ratios and right/bottom padding, every cell a query that
+    refers to its own cell centre in the valid frame (the encoder's
+    reference points, as msda_runner's locations).  min_bytes: value,
+    offsets, attn and out once, plus the references, ratios and the byte
+    mask."""
     from sparse_deformable_sampling_amd import _binding as B, synth
     n, q, heads, dh, pts = 8, 17821, 8, 32, 4
-    d = synth.msda_ref_inputs(n, MSDA_SHAPES, q, heads, dh, pts, ref_dims=2, padded=True, seed=seed)
+    d = synth.msda_ref_inputs(n, MSDA_SHAPES, q, heads, dh, pts, ref_dims=2, padded=True, seed=seed, ref="cells")
     min_bytes = 4 * (d["value"].size + d["offsets"].size + d["attn"].size + n * q * heads * dh +
                      d["reference"].size + d["valid_ratios"].size) + d["padding_mask"].size
     desc = B.MsdaDesc(n, q, heads, dh, len(MSDA_SHAPES), pts, 1, B.DCN_F32)

@@ -152,7 +152,8 @@ def msda_inputs(n, shapes, len_q, heads, head_dim, points, offset_std=2.0, dtype
     return {"value": value, "loc": store(loc, dtype), "attn": attn}
 
 
-def msda_ref_inputs(n, shapes, len_q, heads, head_dim, points, ref_dims=2, offset_std=2.0, padded=True, seed=1):
+def msda_ref_inputs(n, shapes, len_q, heads, head_dim, points, ref_dims=2, offset_std=2.0, padded=True, seed=1,
+                    ref="uniform"):
     """Inputs of the reference-based MSDA read (f32):
     value ~ N(0,1) [n,S,heads,head_dim]; attn logits ~ N(0,1);
     offsets ~ N(0, offset_std) [n,q,heads,L,P,2] (pixels for point references,
@@ -163,7 +164,10 @@ def msda_ref_inputs(n, shapes, len_q, heads, head_dim, points, ref_dims=2, offse
     width and height (at least one cell) at the top-left; the rest is
     right/bottom padding, marked in padding_mask [n,S] (1 = padded), and
     valid_ratios [n,L,2] = (valid W / W_l, valid H / H_l).  padded=False:
-    ratios of 1 and no mask."""
+    ratios of 1 and no mask.
+    ref="cells" (points only): the encoder's queries, one per cell of the
+    flattened maps (len_q must be S), each referring to its own cell centre in
+    its image's valid frame, ((x + 1/2) / (r_w W_l), (y + 1/2) / (r_h H_l))."""
     L = len(shapes)
     S = int(sum(int(hh) * int(ww) for hh, ww in shapes))
     value = normal((n, S, heads, head_dim), 1.0, seed, VALUE)
@@ -190,5 +194,17 @@ def msda_ref_inputs(n, shapes, len_q, heads, head_dim, points, ref_dims=2, offse
                 m[:hv, :wv] = 0
                 mask[b, start:start + hh * ww] = m.reshape(-1)
             start += hh * ww
+    if ref == "cells":
+        if ref_dims != 2 or len_q != S:
+            raise ValueError("ref='cells' needs point references and one query per cell (len_q == %d)" % S)
+        cen = []
+        for l, (hh, ww) in enumerate(shapes):
+            yy, xx = np.meshgrid(np.arange(hh, dtype=np.float64), np.arange(ww, dtype=np.float64), indexing="ij")
+            cx = (xx.ravel()[None, :] + 0.5) / (ratios[:, l, 0:1].astype(np.float64) * ww)
+            cy = (yy.ravel()[None, :] + 0.5) / (ratios[:, l, 1:2].astype(np.float64) * hh)
+            cen.append(np.stack([cx, cy], axis=-1))
+        reference = np.concatenate(cen, axis=1).astype(np.float32)
+    elif ref != "uniform":
+        raise ValueError("ref must be 'uniform' or 'cells'")
     return {"value": value, "reference": np.ascontiguousarray(reference), "offsets": offsets, "attn": attn,
             "valid_ratios": ratios if padded else None, "padding_mask": mask if padded else None}

@@ -626,9 +626,10 @@ def test_msda_levels_points(sds, shapes, points):
 
 # ---------------------------------------------------------------- MSDA from references (NEXT-4)
 
-def check_msda_ref(sds, name, n, shapes, q, heads, dh, points, ref_dims, padded=True, softmax=True, seed=1):
+def check_msda_ref(sds, name, n, shapes, q, heads, dh, points, ref_dims, padded=True, softmax=True, seed=1,
+                   ref="uniform"):
     import torch
-    d = synth.msda_ref_inputs(n, shapes, q, heads, dh, points, ref_dims=ref_dims, padded=padded, seed=seed)
+    d = synth.msda_ref_inputs(n, shapes, q, heads, dh, points, ref_dims=ref_dims, padded=padded, seed=seed, ref=ref)
     v, ref, off, attn = (to_dev(d[k], "f32") for k in ("value", "reference", "offsets", "attn"))
     ratios = to_dev(d["valid_ratios"], "f32") if padded else None
     pad = torch.from_numpy(d["padding_mask"]).cuda() if padded else None
@@ -642,10 +643,13 @@ def check_msda_ref(sds, name, n, shapes, q, heads, dh, points, ref_dims, padded=
     assert err <= TOL["f32"], (name, err)
 
 
-def test_msda_ref_encoder_padded(sds):
+@pytest.mark.parametrize("ref", ["uniform", "cells"])
+def test_msda_ref_encoder_padded(sds, ref):
     """Encoder shape (batch 8, 4 levels 100x134 .. 13x17, 8 heads x 32,
-    4 points), point references, per-image valid ratios and padding."""
-    check_msda_ref(sds, "msda-ref-encoder", 8, ENCODER_SHAPES, 17821, 8, 32, 4, 2)
+    4 points), point references, per-image valid ratios and padding: random
+    references, and every cell a query referring to its own centre in the
+    valid frame (the encoder's reference points, the benched workload)."""
+    check_msda_ref(sds, "msda-ref-encoder-" + ref, 8, ENCODER_SHAPES, 17821, 8, 32, 4, 2, ref=ref)
 
 
 @pytest.mark.parametrize("padded", [True, False])
