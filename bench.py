@@ -238,6 +238,22 @@ def msda_runner(torch, seed=1):
     return r
 
 
+# The MSDA gather's second ceiling: every corner read of a head is one
+# 128-byte line (32 fp32 channels, line-aligned), and the vector L1 looks up
+# about 0.43 lines per clock per CU (measured on gfx950 with scattered 16-byte
+# reads), so 4 lines per sample bound the kernel below the HBM roofline.
+L1_LINES_PER_CLK_CU = 0.43
+CU_COUNT, CLOCK_GHZ = 256, 2.4
+
+
+def msda_line_roofline(kernel_us):
+    n, q, heads, pts = 8, 17821, 8, 4
+    lines = n * q * heads * len(MSDA_SHAPES) * pts * 4
+    floor_us = lines / (L1_LINES_PER_CLK_CU * CU_COUNT * CLOCK_GHZ * 1e3)
+    return {"bound": "vector L1 line lookups", "lines_per_launch": lines, "lines_per_clk_per_cu": L1_LINES_PER_CLK_CU,
+            "floor_us": round(floor_us, 1), "frac": round(floor_us / kernel_us, 4)}
+
+
 def msda_ref_runner(torch, seed=1):
     """MSDA read with locations formed in the kernel: the encoder shape with
     per-image valid ratios and right/bottom padding, every cell a query that
@@ -591,13 +607,12 @@ def main():
         secondary[r.name]["context_pages_a100_fp16_ms"] = 0.873
         print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
         del r
-        r = msda_runner(torch)
-        secondary[r.name] = measure(torch, r, 50, 5)
-        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
-        r = msda_ref_runner(torch)
-        secondary[r.name] = measure(torch, r, 50, 5)
-        print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
-        del r
+        for runner in (msda_runner, msda_ref_runner):
+            r = runner(torch)
+            secondary[r.name] = measure(torch, r, 50, 5)
+            secondary[r.name]["l1_line_roofline"] = msda_line_roofline(secondary[r.name]["kernel_us_mean"])
+            print("[bench] %s: %s" % (r.name, secondary[r.name]), file=sys.stderr, flush=True)
+            del r
         for gather in (True, False):
             r = msda_bwd_runner(torch, gather=gather)
             k = 20 if gather else 5
