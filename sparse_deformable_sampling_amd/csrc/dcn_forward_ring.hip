@@ -343,6 +343,12 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                     float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
                     if (k + 1 < KF) geo(k + 1, An, n00, n01, n10, n11);
                     __builtin_amdgcn_sched_barrier(0);
+                    // A wave whose tap data has landed goes first on its SIMD
+                    // while it multiplies (wave priority, not a stream
+                    // priority): the others' reads then wait in the LDS queue
+                    // behind math rather than the math behind them (stage-1
+                    // f16 45.2 -> 43.4 us, stage-2 25.5 -> 24.4 us).
+                    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
                         fma16<DT>(acc + q * V, c00, cur[4 * q + 0]);
@@ -351,6 +357,7 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                         fma16<DT>(acc + q * V, c11, cur[4 * q + 3]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(0);
                     if (k + 1 < KF) {
                         issue(An, cur);
                         c00 = n00; c01 = n01; c10 = n10; c11 = n11;
