@@ -31,8 +31,9 @@
 // Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
 // accumulation; 16-byte vector stores, one writer per output element.  A
-// group wider than 64 bytes per pixel runs as several 64-byte items that
-// share the group's offsets and mask (the plan's split_log).
+// group wider than 64 bytes (f32) or 32 bytes (f16/bf16) per pixel runs as
+// several items of that width that share the group's offsets and mask (the
+// plan's split_log).
 // WMAX is the workgroup's wave count bound: 16 (four waves per SIMD, <=128
 // VGPRs) where a corner is at most 32 bytes, the next tap's geometry then
 // being computed while its reads land; 8 otherwise, with the geometry of all
@@ -521,12 +522,14 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
     const long x_bytes = (long)G0.n * G0.h * G0.w * G0.c * es;
     const long off_bytes = (long)G0.items * G0.K * 2 * es, mask_bytes = (long)G0.items * G0.K * es;
     if (x_bytes >= (1L << 31) || off_bytes >= (1L << 31) - 64 || mask_bytes >= (1L << 31) - 64) return false;
-    // A group wider than 64 bytes per pixel (f32 with D > 16, f16/bf16 with
-    // D > 32) runs as 2^split_log groups of 64 bytes, each lane item with its
-    // own share of the channels and the group's offsets and mask: the tap
-    // geometry is then computed once per 64 bytes, but a lane's sums and
-    // corner data stay within the registers of the 4-chunk kernel.
-    const int lane_bytes = 64;
+    // A group wider than lane_bytes per pixel runs as 2^split_log groups of
+    // lane_bytes, each lane item with its own share of the channels and the
+    // group's offsets and mask: the tap geometry is then computed once per
+    // lane item, but a lane's sums and corner data stay within the
+    // registers of the 4-chunk kernel (f32, 64 bytes) or of the 1024-thread
+    // 2-chunk kernel (f16/bf16, 32 bytes: at 56x56x128 with 4 groups of 32
+    // channels, 71 us against 75 us for 64-byte items in 512-thread groups).
+    const int lane_bytes = es == 2 ? 32 : 64;
     int split_log = 0;
     while ((G0.d * es >> split_log) > lane_bytes) ++split_log;
     if (split_log > 0 && (G0.d % (1 << split_log) != 0 || (G0.d >> split_log) * es != lane_bytes)) return false;
