@@ -23,14 +23,17 @@
 //  - dcn_offset_mask_wave (C up to 256, C/8 dividing 64): W_om in LDS once
 //    per workgroup, then each wave alone on its own 16-pixel blocks (see the
 //    comment above it);
-//  - dcn_offset_mask_k, the tile kernel for the other C: a workgroup of eight
+//  - dcn_offset_mask_k, the tile kernel for the other C: a workgroup of 16
 //    waves takes TM = 16, 32 or 64 pixels, computes their depthwise 3x3 (a
 //    thread per (pixel, 8 channels), 16-byte loads, fp32 sums, d rounded
 //    once to the storage type) into an LDS tile A[TM][C] (rows C+8 elements
 //    apart, so that the 16 rows one operand read touches fall on distinct
-//    banks), and wave w takes the 16-output blocks w, w+8, ..., reading
-//    the weight rows straight from L2 (eight waves, not four, so that fewer
-//    blocks wait on those reads one after another).
+//    banks), and wave w takes the 16-output blocks w, w+16, ..., reading
+//    the weight rows straight from L2.  The kernel waits on memory more than
+//    it works (one workgroup per CU at 64-pixel tiles), so it runs as many
+//    waves as a workgroup takes: each then walks fewer blocks, whose L2
+//    reads would otherwise wait one after another (stage-3: 4 waves 33.4 us,
+//    8 waves 28.8, 16 waves 25.6).
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -41,7 +44,7 @@ namespace dcn {
 
 namespace {
 
-constexpr int FT_THREADS = 512;
+constexpr int FT_THREADS = 1024;
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
