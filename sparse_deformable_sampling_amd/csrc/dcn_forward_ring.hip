@@ -223,6 +223,11 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     for (int kx = 0; kx < KW; ++kx) bxk[kx] = c * G.sw - G.pw + 1 + kx * G.dw;
 #pragma unroll
     for (int ky = 0; ky < KH; ++ky) byk[ky] = (r_begin + rl) * G.sh - G.ph - lo0 + ky * G.dh;
+    float bxf[KW], byf[KH];
+#pragma unroll
+    for (int kx = 0; kx < KW; ++kx) bxf[kx] = (float)bxk[kx];
+#pragma unroll
+    for (int ky = 0; ky < KH; ++ky) byf[ky] = (float)byk[ky];
 
     for (int s = 0; s < nsteps; ++s) {
         const int r_s = r_begin + s * rc.tr;
@@ -293,12 +298,34 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                     dxk = h2f<DT>(pc[k] & 0xffffu);
                     dyk = h2f<DT>(pc[k] >> 16);
                 }
-                const float tx = fminf(fmaxf(G.scale * dxk, -lim), lim);
-                const float ty = fminf(fmaxf(G.scale * dyk, -lim), lim);
-                const float fx = floorf(tx), fy = floorf(ty);
-                const float a = tx - fx, b = ty - fy;
-                const int xs = bxk[kx] + (int)fx;                   // x0 + 1 (LDS column of the left corners - 1)
-                const int yi = byk[ky] + (int)fy;                   // window row of the top corners
+                int xs, yi;   // x0 + 1 (LDS column of the left corners - 1), window row of the top corners
+                float a, b;   // fractions
+                if constexpr (ES == 2) {
+                    // 16-bit offsets: the position sigma*d + base in one
+                    // multiply-add (v_fma_mix_f32 takes the 16-bit operand),
+                    // then floor-and-convert and the fraction in one
+                    // instruction each; the compiler forms neither
+                    // v_cvt_flr_i32_f32 nor the fused base, hence the asm.
+                    // The sum rounds to fp32 (at most 2^-24 of |position|),
+                    // which moves the bilinear sample continuously by that
+                    // much, far below the 16-bit output's rounding.
+                    const float tx = fminf(fmaxf(fmaf(G.scale, dxk, bxf[kx]), -lim), lim);
+                    const float ty = fminf(fmaxf(fmaf(G.scale, dyk, byf[ky]), -lim), lim);
+                    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(xs) : "v"(tx));
+                    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(yi) : "v"(ty));
+                    a = __builtin_amdgcn_fractf(tx);
+                    b = __builtin_amdgcn_fractf(ty);
+                } else {
+                    // fp32: floor and fraction of sigma*d alone, then the
+                    // integer base, so the fraction is exact.
+                    const float tx = fminf(fmaxf(G.scale * dxk, -lim), lim);
+                    const float ty = fminf(fmaxf(G.scale * dyk, -lim), lim);
+                    const float fx = floorf(tx), fy = floorf(ty);
+                    a = tx - fx;
+                    b = ty - fy;
+                    xs = bxk[kx] + (int)fx;
+                    yi = byk[ky] + (int)fy;
+                }
                 const bool colok = (unsigned)xs <= (unsigned)G.w;   // image column in [-1, W-1]
                 const bool inwin = (unsigned)yi < (unsigned)(rc.nw - 1);
                 fb |= (colok && !inwin) ? (1u << k) : 0u;
@@ -308,11 +335,12 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 const uint32_t addr = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
                 Ak = use ? addr : 0u;   // LDS columns 0, 1 of slots 0, 1: zeros
                 const float mm = use ? m[k] : 0.f;
-                const float ma = mm * (1.f - a), mb = mm * a;
-                w00 = ma * (1.f - b);
-                w01 = mb * (1.f - b);
+                // m(1-a) = m - ma: one multiply per pair of weights
+                const float mb = mm * a, ma = mm - mb;
                 w10 = ma * b;
+                w00 = ma - w10;
                 w11 = mb * b;
+                w01 = mb - w11;
             };
             // The four corners' addresses are pointers into the ring, so that
             // the 16-byte chunk offsets fold into the reads' immediate offsets.
