@@ -29,11 +29,13 @@
 //    once to the storage type) into an LDS tile A[TM][C] (rows C+8 elements
 //    apart, so that the 16 rows one operand read touches fall on distinct
 //    banks), and wave w takes the 16-output blocks w, w+16, ..., reading
-//    the weight rows straight from L2.  The kernel waits on memory more than
-//    it works (one workgroup per CU at 64-pixel tiles), so it runs as many
-//    waves as a workgroup takes: each then walks fewer blocks, whose L2
-//    reads would otherwise wait one after another (stage-3: 4 waves 33.4 us,
-//    8 waves 28.8, 16 waves 25.6).
+//    the weight rows straight from L2 in whole 128-byte lines, one batch
+//    ahead of its products.  The kernel waits on memory more than it works
+//    (one workgroup per CU at 64-pixel tiles), so it runs as many waves as
+//    a workgroup takes: each then walks fewer blocks, whose L2 reads would
+//    otherwise wait one after another (stage-3: 4 waves 33.4 us, 8 waves
+//    28.8, 16 waves 25.6; whole-line weight reads with batched operand
+//    reads 25.0).
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -213,58 +215,118 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     __syncthreads();
 
     // ---- NO x TM product om^T = W_om d^T: wave w takes output blocks w,
-    // w+8, ...; the A operand is 16 weight rows, the B operand 16 pixels of d.
-    // Lane l then holds outputs j0..j0+3 (j0 = 16*cb + 4*(l/16)) of pixel
+    // w+NWV, ... (NWV waves); the A operand is 16 weight rows, the B operand 16 pixels of
+    // d.  Lane l then holds outputs j0..j0+3 (j0 = 16*cb + 4*(l/16)) of pixel
     // 16*rb + l%16.
+    //
+    // Weight rows come from L2 two k steps (64 channels, one 128-byte line of
+    // a row) at a time: load i of a pair reads rows 8i..8i+7 of the block in
+    // full lines (lane l: row 8i + l%8, 16-byte chunk l/16 + 4*((l/8)%2)),
+    // 8 line lookups per KB where the operand layout (16 rows x 64 bytes)
+    // would touch 16.  A rotation by 8 lanes within each row of 16 (DPP
+    // row_ror) and a select then give each lane its operand chunk: row l%16,
+    // chunk l/16 of the pair's first step and 4 + l/16 of its second.  A
+    // wave's loads run one batch (FP pairs) ahead of its products, across
+    // its blocks, and each block's bias comes with the block's first batch.
     const int kg = 8 * (lane >> 4);
     const bool quad = (NMASK & 3) == 0;   // 4 consecutive outputs of a pixel are 8-byte aligned in LDS
-    for (int cb = wave; cb < F.ncb; cb += FT_THREADS / 64) {
-        const T* wrow = omw + (long)min(cb * 16 + (lane & 15), F.NO - 1) * C;   // rows past NO compute a copy, not stored
-        f4_t acc[MB];
+    const int prow = lane & 7, pchunk = (lane >> 4) + ((lane >> 1) & 4);
+    const bool hi8 = (lane & 8) != 0;
+    constexpr int FP = (DT == DT_BF16 && MB == 4) ? 2 : 3;          // k-step pairs per batch (bf16 rounding needs the registers)
+    const int nkb = (F.KP + 64 * FP - 1) / (64 * FP);              // batches per block
+    constexpr int NWV = FT_THREADS / 64;
+    const int nblk = wave < F.ncb ? (F.ncb - wave + NWV - 1) / NWV : 0;
+    const int nit = nblk * nkb;
+    auto load_batch = [&](int it, uint4* w, uint32_t* bias) {
+        const int j = it / nkb, kb = it - j * nkb;
+        const int cb = wave + NWV * j, kc = 64 * FP * kb;
+        const T* r0 = omw + (long)min(cb * 16 + prow, F.NO - 1) * C;       // rows past NO compute a copy, not stored
+        const T* r1 = omw + (long)min(cb * 16 + 8 + prow, F.NO - 1) * C;
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) acc[rb] = f4_t{0.f, 0.f, 0.f, 0.f};
-        // weight fragments eight k steps at a time: the eight loads are in
-        // flight together instead of one L2 round trip per step
-        for (int kc = 0; kc < F.KP; kc += 256) {
-            uint4 wf[8];
+        for (int t = 0; t < FP; ++t) {
+            const int k0 = kc + 64 * t + 8 * pchunk;
+            w[2 * t] = k0 < C ? *reinterpret_cast<const uint4*>(r0 + k0) : make_uint4(0u, 0u, 0u, 0u);
+            w[2 * t + 1] = k0 < C ? *reinterpret_cast<const uint4*>(r1 + k0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (kb == 0) {
+            const int j0 = cb * 16 + 4 * (lane >> 4);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int k0 = kc + 32 * s + kg;
-                wf[s] = k0 < C ? *reinterpret_cast<const uint4*>(wrow + k0) : make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < 4; ++i) bias[i] = __builtin_bit_cast(uint16_t, omb[min(j0 + i, F.NO - 1)]);
+        }
+    };
+    auto ror8 = [](uint4 v) {
+        return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xF, 0xF, false),
+                          (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xF, 0xF, false),
+                          (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, 0x128, 0xF, 0xF, false),
+                          (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, 0x128, 0xF, 0xF, false));
+    };
+    auto sel = [](bool c, uint4 a, uint4 b) {
+        return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+    };
+    uint4 wcur[2 * FP], wnxt[2 * FP];
+    uint32_t bcur[4] = {0u, 0u, 0u, 0u}, bnxt[4] = {0u, 0u, 0u, 0u};   // raw bias bits, widened when used
+    f4_t acc[MB];
+    if (nit > 0) load_batch(0, wcur, bcur);
+    for (int it = 0; it < nit; ++it) {
+        const int j = it / nkb, kb = it - j * nkb;
+        const int cb = wave + NWV * j, kc = 64 * FP * kb;
+        if (it + 1 < nit) load_batch(it + 1, wnxt, bnxt);
+        if (kb == 0) {
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) acc[rb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int t = 0; t < FP; ++t) {
+            if (kc + 64 * t >= F.KP) break;
+            const uint4 e = sel(hi8, ror8(wcur[2 * t + 1]), wcur[2 * t]);
+            const uint4 o = sel(hi8, wcur[2 * t + 1], ror8(wcur[2 * t]));
+            const int k0 = kc + 64 * t + kg;
+            // A step's MB operand reads are issued together, ahead of its
+            // products, so that their LDS latency is paid once per step.
+            uint4 bf[MB];
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) bf[rb] = *reinterpret_cast<const uint4*>(A + (rb * 16 + (lane & 15)) * F.AST + k0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) acc[rb] = mfma32<DT>(e, bf[rb], acc[rb]);
+            if (kc + 64 * t + 32 < F.KP) {
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb)
+                    bf[rb] = *reinterpret_cast<const uint4*>(A + (rb * 16 + (lane & 15)) * F.AST + k0 + 32);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rb = 0; rb < MB; ++rb) acc[rb] = mfma32<DT>(o, bf[rb], acc[rb]);
             }
+        }
+        if (kb == nkb - 1) {
+            const int j0 = cb * 16 + 4 * (lane >> 4);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                if (kc + 32 * s >= F.KP) break;
-                const int k0 = kc + 32 * s + kg;
+            for (int rb = 0; rb < MB; ++rb) {
+                const int row = rb * 16 + (lane & 15);
+                float v[4];
 #pragma unroll
-                for (int rb = 0; rb < MB; ++rb) {
-                    const uint4 b = *reinterpret_cast<const uint4*>(A + (rb * 16 + (lane & 15)) * F.AST + k0);
-                    acc[rb] = mfma32<DT>(wf[s], b, acc[rb]);
+                for (int i = 0; i < 4; ++i) v[i] = acc[rb][i] + to_f32(__builtin_bit_cast(T, (uint16_t)bcur[i]));
+                if (quad && j0 + 3 < NOFF) {
+                    *reinterpret_cast<uint2*>(Ooff + row * NOFF + j0) = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+                } else if (quad && j0 >= NOFF && j0 + 3 < F.NO) {
+                    *reinterpret_cast<uint2*>(Omask + row * NMASK + (j0 - NOFF)) =
+                        make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int jj = j0 + i;
+                        if (jj < NOFF) Ooff[row * NOFF + jj] = from_f32<DT>(v[i]);
+                        else if (jj < F.NO) Omask[row * NMASK + (jj - NOFF)] = from_f32<DT>(v[i]);
+                    }
                 }
             }
         }
-        const int j0 = cb * 16 + 4 * (lane >> 4);
-        float bias[4];
+        if (it + 1 < nit) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bias[i] = to_f32(omb[min(j0 + i, F.NO - 1)]);
+            for (int i = 0; i < 2 * FP; ++i) wcur[i] = wnxt[i];
+            if ((it + 1) % nkb == 0) {
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-            const int row = rb * 16 + (lane & 15);
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[rb][i] + bias[i];
-            if (quad && j0 + 3 < NOFF) {
-                *reinterpret_cast<uint2*>(Ooff + row * NOFF + j0) = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
-            } else if (quad && j0 >= NOFF && j0 + 3 < F.NO) {
-                *reinterpret_cast<uint2*>(Omask + row * NMASK + (j0 - NOFF)) =
-                    make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = j0 + i;
-                    if (j < NOFF) Ooff[row * NOFF + j] = from_f32<DT>(v[i]);
-                    else if (j < F.NO) Omask[row * NMASK + (j - NOFF)] = from_f32<DT>(v[i]);
-                }
+                for (int i = 0; i < 4; ++i) bcur[i] = bnxt[i];
             }
         }
     }
@@ -663,14 +725,17 @@ void layout(const Geom& G, int mb, FrontCfg* F)
     F->div_h = make_fastdiv((uint32_t)G.h);
 }
 
-// Tile plan.  Every tile reads all of W_om from L2 as MFMA fragments, 16
-// rows x 64 bytes per load instruction (16 cache-line lookups per KB, the
-// vector memory's rate limit), so per CU the cost is about (tiles per CU) x
-// (W_om's fragment lines + the tile's own depthwise reads and output lines).
-// Take the tile size that fits in LDS with the least such cost (ties to the
-// larger tile).  At stage-3 (320 channels, 540 outputs) 64-pixel tiles, one
-// workgroup per CU, take 28.7 us against 33.5 for 32-pixel tiles at two per
-// CU and 50.9 for 16-pixel tiles.  False if not even a 16-pixel tile fits.
+// Tile plan.  Every tile streams all of W_om from L2, so per CU the cost is
+// about (tiles per CU) x (W_om's lines + the tile's own depthwise reads and
+// output lines), the weights counted at 16 lookups per KB of the operand
+// layout (the load order reads whole lines, 8 per KB, but the stream's
+// latency scales the same way).  Take the tile size that fits in LDS with
+// the least such cost (ties to the larger tile).  At stage-3 (320 channels,
+// 540 outputs) 64-pixel tiles, one 16-wave workgroup per CU, take 25.0 us
+// against 35.4 for 32-pixel tiles and 33.6 for 32-pixel tiles in 8-wave
+// workgroups two per CU: the time grows with the number of tiles, each of
+// which streams the 346 KB of weights.  False if not even a 16-pixel tile
+// fits.
 bool plan_frontend(const Geom& G, int dtype, int lds_limit, int num_cus, FrontCfg* F)
 {
     if (dtype != DT_F16 && dtype != DT_BF16) return false;
