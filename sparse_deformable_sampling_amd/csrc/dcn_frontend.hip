@@ -35,7 +35,7 @@
 //    a workgroup takes: each then walks fewer blocks, whose L2 reads would
 //    otherwise wait one after another (stage-3: 4 waves 33.4 us, 8 waves
 //    28.8, 16 waves 25.6; whole-line weight reads with batched operand
-//    reads 25.0).
+//    reads 25.0; the first weight batch issued before the depthwise 24.5).
 #include <algorithm>
 
 #include "dcn_device.h"
@@ -170,6 +170,40 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     const int px0 = tile * TM;
     const int npx = min(TM, F.npix - px0);
 
+    // ---- weight stream set-up (see the product below)
+    const int kg = 8 * (lane >> 4);
+    const bool quad = (NMASK & 3) == 0;   // 4 consecutive outputs of a pixel are 8-byte aligned in LDS
+    const int prow = lane & 7, pchunk = (lane >> 4) + ((lane >> 1) & 4);
+    const bool hi8 = (lane & 8) != 0;
+    constexpr int FP = (DT == DT_BF16 && MB == 4) ? 2 : 3;          // k-step pairs per batch (bf16 rounding needs the registers)
+    const int nkb = (F.KP + 64 * FP - 1) / (64 * FP);              // batches per block
+    constexpr int NWV = FT_THREADS / 64;
+    const int nblk = wave < F.ncb ? (F.ncb - wave + NWV - 1) / NWV : 0;
+    const int nit = nblk * nkb;
+    auto load_batch = [&](int it, uint4* w, uint32_t* bias) {
+        const int j = it / nkb, kb = it - j * nkb;
+        const int cb = wave + NWV * j, kc = 64 * FP * kb;
+        const T* r0 = omw + (long)min(cb * 16 + prow, F.NO - 1) * C;       // rows past NO compute a copy, not stored
+        const T* r1 = omw + (long)min(cb * 16 + 8 + prow, F.NO - 1) * C;
+#pragma unroll
+        for (int t = 0; t < FP; ++t) {
+            const int k0 = kc + 64 * t + 8 * pchunk;
+            w[2 * t] = k0 < C ? *reinterpret_cast<const uint4*>(r0 + k0) : make_uint4(0u, 0u, 0u, 0u);
+            w[2 * t + 1] = k0 < C ? *reinterpret_cast<const uint4*>(r1 + k0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (kb == 0) {
+            const int j0 = cb * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bias[i] = __builtin_bit_cast(uint16_t, omb[min(j0 + i, F.NO - 1)]);
+        }
+    };
+    uint4 wcur[2 * FP], wnxt[2 * FP];
+    uint32_t bcur[4] = {0u, 0u, 0u, 0u}, bnxt[4] = {0u, 0u, 0u, 0u};   // raw bias bits, widened when used
+    f4_t acc[MB];
+    // The first batch of this wave's weights does not depend on the tile:
+    // it is in flight during the depthwise phase.
+    if (nit > 0) load_batch(0, wcur, bcur);
+
     // ---- depthwise 3x3 into A.  A thread's items are (pixel p, channels
     // 8*cg..) for e = tid, tid + FT_THREADS, ...; rows past the last pixel and
     // channels past C are written as zeros.  A neighbour outside the image
@@ -228,32 +262,6 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     // chunk l/16 of the pair's first step and 4 + l/16 of its second.  A
     // wave's loads run one batch (FP pairs) ahead of its products, across
     // its blocks, and each block's bias comes with the block's first batch.
-    const int kg = 8 * (lane >> 4);
-    const bool quad = (NMASK & 3) == 0;   // 4 consecutive outputs of a pixel are 8-byte aligned in LDS
-    const int prow = lane & 7, pchunk = (lane >> 4) + ((lane >> 1) & 4);
-    const bool hi8 = (lane & 8) != 0;
-    constexpr int FP = (DT == DT_BF16 && MB == 4) ? 2 : 3;          // k-step pairs per batch (bf16 rounding needs the registers)
-    const int nkb = (F.KP + 64 * FP - 1) / (64 * FP);              // batches per block
-    constexpr int NWV = FT_THREADS / 64;
-    const int nblk = wave < F.ncb ? (F.ncb - wave + NWV - 1) / NWV : 0;
-    const int nit = nblk * nkb;
-    auto load_batch = [&](int it, uint4* w, uint32_t* bias) {
-        const int j = it / nkb, kb = it - j * nkb;
-        const int cb = wave + NWV * j, kc = 64 * FP * kb;
-        const T* r0 = omw + (long)min(cb * 16 + prow, F.NO - 1) * C;       // rows past NO compute a copy, not stored
-        const T* r1 = omw + (long)min(cb * 16 + 8 + prow, F.NO - 1) * C;
-#pragma unroll
-        for (int t = 0; t < FP; ++t) {
-            const int k0 = kc + 64 * t + 8 * pchunk;
-            w[2 * t] = k0 < C ? *reinterpret_cast<const uint4*>(r0 + k0) : make_uint4(0u, 0u, 0u, 0u);
-            w[2 * t + 1] = k0 < C ? *reinterpret_cast<const uint4*>(r1 + k0) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if (kb == 0) {
-            const int j0 = cb * 16 + 4 * (lane >> 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bias[i] = __builtin_bit_cast(uint16_t, omb[min(j0 + i, F.NO - 1)]);
-        }
-    };
     auto ror8 = [](uint4 v) {
         return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x128, 0xF, 0xF, false),
                           (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x128, 0xF, 0xF, false),
@@ -263,10 +271,6 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     auto sel = [](bool c, uint4 a, uint4 b) {
         return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
     };
-    uint4 wcur[2 * FP], wnxt[2 * FP];
-    uint32_t bcur[4] = {0u, 0u, 0u, 0u}, bnxt[4] = {0u, 0u, 0u, 0u};   // raw bias bits, widened when used
-    f4_t acc[MB];
-    if (nit > 0) load_batch(0, wcur, bcur);
     for (int it = 0; it < nit; ++it) {
         const int j = it / nkb, kb = it - j * nkb;
         const int cb = wave + NWV * j, kc = 64 * FP * kb;
