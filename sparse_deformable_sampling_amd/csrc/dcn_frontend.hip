@@ -359,7 +359,7 @@ struct WaveCfg {
     int NO, NOFF;    // G*K*3 outputs, G*K*2 of them offsets
     int ncb;         // 16-output blocks
     int npix, nblk;  // pixels, 16-pixel blocks
-    int nw;          // waves per workgroup (4 or 8, chosen at launch)
+    int nw;          // waves per workgroup (4 or 8, or 9-16 for one block per wave; chosen at launch)
     int nwg;         // workgroups, a multiple of 8 (chosen at launch)
     int bias_off;    // LDS byte offsets: Bt at 0, bias (fp32), wave slices
     int dw_off;      // bf16 only: depthwise weights [9][KP] and bias [KP] as fp32
@@ -398,8 +398,8 @@ __device__ __forceinline__ void wave_copy_out(const unsigned char* src, unsigned
             *reinterpret_cast<const uint16_t*>(src + nv * 16 + lane * 2);
 }
 
-template <int DT, int C8, int R>
-__global__ __launch_bounds__(512) void dcn_offset_mask_wave(Geom G, WaveCfg F, const typename Elem<DT>::T* __restrict__ x,
+template <int DT, int C8, int R, int NWMAX>
+__global__ __launch_bounds__(NWMAX * 64) void dcn_offset_mask_wave(Geom G, WaveCfg F, const typename Elem<DT>::T* __restrict__ x,
                                                              const typename Elem<DT>::T* __restrict__ dww,
                                                              const typename Elem<DT>::T* __restrict__ dwb,
                                                              const typename Elem<DT>::T* __restrict__ omw,
@@ -597,7 +597,34 @@ hipError_t launch_wave_c8(const Geom& G, const WaveCfg& F, const void* x, const 
                           const void* omw, const void* omb, void* off, void* mask, hipStream_t s)
 {
     using T = typename Elem<DT>::T;
-    auto* fn = dcn_offset_mask_wave<DT, C8, R>;
+    // Where 8-wave workgroups would leave some waves two blocks and others
+    // one (between 8 and 16 blocks per CU), one workgroup per CU with a wave
+    // for each block, up to 16 waves (one-pixel runs, <= 128 registers),
+    // ends every wave after one block (stage-2, 28x28x128: f16 22.2 ->
+    // 20.2 us, bf16 29.8 -> 24.3 us).
+    {
+        int lds_limit, num_cus;
+        device_limits(&lds_limit, &num_cus);
+        const int nw1 = (F.nblk + num_cus - 1) / num_cus;
+        if (R == 1 && nw1 > 8 && nw1 <= 16 && F.w_off + nw1 * F.w_bytes <= lds_limit) {
+            auto* fb = dcn_offset_mask_wave<DT, C8, 1, 16>;
+            WaveCfg L = F;
+            L.nw = nw1;
+            L.lds_bytes = F.w_off + nw1 * F.w_bytes;
+            hipError_t e = hipFuncSetAttribute((const void*)fb, hipFuncAttributeMaxDynamicSharedMemorySize, L.lds_bytes);
+            if (e != hipSuccess) return e;
+            int per_cu = 0;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fb, nw1 * 64, L.lds_bytes);
+            if (e != hipSuccess) return e;
+            if (per_cu >= 1) {
+                L.nwg = (std::min((F.nblk + nw1 - 1) / nw1, num_cus) + 7) / 8 * 8;
+                fb<<<dim3(L.nwg), dim3(nw1 * 64), L.lds_bytes, s>>>(G, L, (const T*)x, (const T*)dww, (const T*)dwb,
+                                                                  (const T*)omw, (const T*)omb, (T*)off, (T*)mask);
+                return hipGetLastError();
+            }
+        }
+    }
+    auto* fn = dcn_offset_mask_wave<DT, C8, R, 8>;
     // Workgroups of 4 or 8 waves, whichever keeps more waves resident on a
     // CU (the weights are loaded once per workgroup: ties go to 8); as many
     // workgroups as stay resident together, a multiple of 8 (one range of
@@ -635,8 +662,13 @@ hipError_t launch_wave(const Geom& G, const WaveCfg& F, int c8, const void* x, c
 {
     // Runs of two pixels need an even width.  bf16 keeps its whole widened
     // 3x4 window live (96 registers); from 128 channels on one-pixel runs
-    // leave room for more waves (Table 10 shape: 55 -> 46 us).
-    const bool r2 = G.w % 2 == 0 && !(DT == DT_BF16 && c8 >= 16);
+    // leave room for more waves (Table 10 shape: 55 -> 46 us).  The
+    // one-block-per-wave launch (see launch_wave_c8) takes one-pixel runs.
+    int lds_limit, num_cus;
+    device_limits(&lds_limit, &num_cus);
+    const int nw1 = (F.nblk + num_cus - 1) / num_cus;
+    const bool one = nw1 > 8 && nw1 <= 16 && F.w_off + nw1 * F.w_bytes <= lds_limit;
+    const bool r2 = !one && G.w % 2 == 0 && !(DT == DT_BF16 && c8 >= 16);
 #define DCN_FE_CASE(N)                                                                          \
     case N:                                                                                     \
         return r2 ? launch_wave_c8<DT, N, 2>(G, F, x, dww, dwb, omw, omb, off, mask, s)        \
