@@ -31,13 +31,12 @@
 // Lane = one (output pixel, group) item holding all D channels: the tap
 // geometry is computed once per item and reused for every channel; fp32
 // accumulation; 16-byte vector stores, one writer per output element.  A
-// group wider than 64 bytes (f32) or 32 bytes (f16/bf16) per pixel runs as
-// several items of that width that share the group's offsets and mask (the
-// plan's split_log).
+// group wider than 32 bytes per pixel runs as several items of 32 bytes that
+// share the group's offsets and mask (the plan's split_log).
 // WMAX is the workgroup's wave count bound: 16 (four waves per SIMD, <=128
-// VGPRs) where a corner is at most 32 bytes, the next tap's geometry then
-// being computed while its reads land; 8 otherwise, with the geometry of all
-// taps computed first and the next tap's reads in flight during the math.
+// VGPRs), the next tap's geometry computed while its reads land; 8 where a
+// 1024-thread plan does not fit, with the geometry of all taps computed
+// first and the next tap's reads in flight during the math.
 #include "dcn_device.h"
 #include "dcn_ring.h"
 
@@ -217,17 +216,19 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
     const uint32_t gbyte = (uint32_t)gl * gsize + (uint32_t)rc.pb;
     const float lim = 16777216.0f;
     // Window-relative row and LDS column of each tap's top-left corner before
-    // the offset (they do not change from step to step).
-    int bxk[KW], byk[KH];
+    // the offset (they do not change from step to step): bx0 + kx*dw and
+    // by0 + ky*dh, the second term uniform.  16-bit offsets take them as
+    // floats, one register per tap (the multiply-add that forms a position
+    // adds them); fp32 adds them as integers, two registers in all.
+    const int bx0 = c * G.sw - G.pw + 1;
+    const int by0 = (r_begin + rl) * G.sh - G.ph - lo0;
+    float bxf[ES == 2 ? KW : 1], byf[ES == 2 ? KH : 1];
+    if constexpr (ES == 2) {
 #pragma unroll
-    for (int kx = 0; kx < KW; ++kx) bxk[kx] = c * G.sw - G.pw + 1 + kx * G.dw;
+        for (int kx = 0; kx < KW; ++kx) bxf[kx] = (float)(bx0 + kx * G.dw);
 #pragma unroll
-    for (int ky = 0; ky < KH; ++ky) byk[ky] = (r_begin + rl) * G.sh - G.ph - lo0 + ky * G.dh;
-    float bxf[KW], byf[KH];
-#pragma unroll
-    for (int kx = 0; kx < KW; ++kx) bxf[kx] = (float)bxk[kx];
-#pragma unroll
-    for (int ky = 0; ky < KH; ++ky) byf[ky] = (float)byk[ky];
+        for (int ky = 0; ky < KH; ++ky) byf[ky] = (float)(by0 + ky * G.dh);
+    }
 
     for (int s = 0; s < nsteps; ++s) {
         const int r_s = r_begin + s * rc.tr;
@@ -260,9 +261,11 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
             }
         }
 
-        // ---- the next step's new rows go straight to LDS, its offsets to registers
+        // ---- the next step's new rows go straight to LDS, its offsets to
+        // registers (fp32 in 1024-thread workgroups: tap by tap, below)
+        constexpr bool TAPWISE = ES == 4 && WMAX == 16;
         if (s + 1 < nsteps) {
-            load_offsets(s + 1);
+            if constexpr (!TAPWISE) load_offsets(s + 1);
             for (int rr = 0; rr < adv; ++rr) load_row(lo + rc.nw + rr);
         }
 
@@ -323,8 +326,8 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                     const float fx = floorf(tx), fy = floorf(ty);
                     a = tx - fx;
                     b = ty - fy;
-                    xs = bxk[kx] + (int)fx;
-                    yi = byk[ky] + (int)fy;
+                    xs = bx0 + kx * G.dw + (int)fx;
+                    yi = by0 + ky * G.dh + (int)fy;
                 }
                 const bool colok = (unsigned)xs <= (unsigned)G.w;   // image column in [-1, W-1]
                 const bool inwin = (unsigned)yi < (unsigned)(rc.nw - 1);
@@ -361,16 +364,69 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 // Four waves per SIMD hide the LDS latency, so registers go to
                 // occupancy: one tap's data in flight, the next tap's geometry
                 // computed while it lands.
+                //
+                // fp32 offsets and mask take 27 registers per item: rather
+                // than hold the next step's set beside this one, the registers
+                // are refilled with the next step's values as soon as the taps
+                // that read them are done, in the same 16-byte pieces as a
+                // whole-set load (offset dwords 4i..4i+3 after tap 2i+1, mask
+                // dwords 4j..4j+3 after tap 4j+3, the rest after the last
+                // tap).  A lane live in the next step is live in this one (its
+                // row only moves down), so only live lanes load.
+                uint32_t nob = OOB, nmb = OOB;
+                if constexpr (TAPWISE) {
+                    const int rr = r + rc.tr;
+                    if (s + 1 < nsteps && rr < r_end) {
+                        const uint32_t item =
+                            ((uint32_t)(n * G.ho + rr) * G.wo + c) * (G.g >> rc.split_log) + (g >> rc.split_log);
+                        nob = item * K2B;
+                        nmb = item * KMB;
+                    }
+                }
+                auto refill = [&](int k) {
+                    if constexpr (TAPWISE) {
+                        // offset dwords [4i, 4i + 4) once tap k has read dword 2k + 1
+#pragma unroll
+                        for (int i = 0; i < OW; i += 4) {
+                            const int last = i + 4 <= OW ? (i + 3) / 2 : KF - 1;
+                            if (k != last) continue;
+                            if (i + 4 <= OW) {
+                                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(orr, nob + 4u * i, 0, 0);
+                                po[i] = v.x; po[i + 1] = v.y; po[i + 2] = v.z; po[i + 3] = v.w;
+                            } else {
+#pragma unroll
+                                for (int j = i; j < OW; ++j) po[j] = __builtin_amdgcn_raw_buffer_load_b32(orr, nob + 4u * j, 0, 0);
+                            }
+                        }
+                        // mask dwords [4i, 4i + 4) once tap k has read dword k
+#pragma unroll
+                        for (int i = 0; i < MW; i += 4) {
+                            const int last = i + 4 <= MW ? i + 3 : KF - 1;
+                            if (k != last) continue;
+                            if (i + 4 <= MW) {
+                                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(mr, nmb + 4u * i, 0, 0);
+                                pmr[i] = v.x; pmr[i + 1] = v.y; pmr[i + 2] = v.z; pmr[i + 3] = v.w;
+                            } else {
+#pragma unroll
+                                for (int j = i; j < MW; ++j) pmr[j] = __builtin_amdgcn_raw_buffer_load_b32(mr, nmb + 4u * j, 0, 0);
+                            }
+                        }
+                    }
+                };
                 uint32_t Ac;
                 float c00, c01, c10, c11;
                 geo(0, Ac, c00, c01, c10, c11);
+                refill(0);
                 u32x4 cur[4 * NCH];
                 issue(Ac, cur);
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
                     uint32_t An = 0;
                     float n00 = 0.f, n01 = 0.f, n10 = 0.f, n11 = 0.f;
-                    if (k + 1 < KF) geo(k + 1, An, n00, n01, n10, n11);
+                    if (k + 1 < KF) {
+                        geo(k + 1, An, n00, n01, n10, n11);
+                        refill(k + 1);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                     // A wave whose tap data has landed goes first on its SIMD
                     // while it multiplies (wave priority, not a stream
@@ -399,20 +455,16 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 float W00[KF], W01[KF], W10[KF], W11[KF];
 #pragma unroll
                 for (int k = 0; k < KF; ++k) geo(k, A[k], W00[k], W01[k], W10[k], W11[k]);
-                // Reads of tap k+1 are in flight while tap k accumulates (with four
-                // chunks per corner the two taps' data would not fit in registers,
-                // so each tap's reads are issued just before its math).  Chunk q of
-                // a corner sits 16*q bytes past its first, an immediate offset of
-                // the read.  (Rotating the chunk order between neighbouring lanes
-                // spreads a read over more LDS bank groups, but its address
+                // Reads of tap k+1 are in flight while tap k accumulates.  Chunk q
+                // of a corner sits 16*q bytes past its first, an immediate offset
+                // of the read.  (Rotating the chunk order between neighbouring
+                // lanes spreads a read over more LDS bank groups, but its address
                 // arithmetic cost more than the conflicts it saved.)
-                constexpr bool PIPE = NCH <= 2;
-                u32x4 cur[4 * NCH], nxt[PIPE ? 4 * NCH : 1];
+                u32x4 cur[4 * NCH], nxt[4 * NCH];
                 issue(A[0], cur);
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
-                    if (!PIPE && k > 0) issue(A[k], cur);
-                    if (PIPE && k + 1 < KF) issue(A[k + 1], nxt);
+                    if (k + 1 < KF) issue(A[k + 1], nxt);
                     __builtin_amdgcn_sched_barrier(0);   // keep the next tap's reads ahead of this tap's math
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
@@ -422,9 +474,9 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                         fma16<DT>(acc + q * V, W11[k], cur[4 * q + 3]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if (PIPE && k + 1 < KF) {
+                    if (k + 1 < KF) {
 #pragma unroll
-                        for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[PIPE ? q : 0];
+                        for (int q = 0; q < 4 * NCH; ++q) cur[q] = nxt[q];
                     }
                 }
             }
@@ -505,19 +557,14 @@ hipError_t launch_ring_typed(const Geom& G, const RingCfg& rc, const void* x, co
                              void* out, hipStream_t s)
 {
     using T = typename Elem<DT>::T;
-    const int nch = G.d * (int)sizeof(T) / 16;
+    const int nch = G.d * (int)sizeof(T) / 16;   // 1 or 2: lane items are at most 32 bytes
     const bool wide = rc.threads > 512;
-    // 1024-thread workgroups are planned only where nch * es <= 4 (f16/bf16
-    // with D <= 16, f32 with D = 4), so no f32 two-chunk one is built.
     if (wide && nch == 1) return launch_one<DT, SOFTMAX, 1, 16>(G, rc, x, off, mask, out, s);
-    if constexpr (DT != DT_F32) {
-        if (wide && nch == 2) return launch_one<DT, SOFTMAX, 2, 16>(G, rc, x, off, mask, out, s);
-    }
+    if (wide && nch == 2) return launch_one<DT, SOFTMAX, 2, 16>(G, rc, x, off, mask, out, s);
     if (wide) return hipErrorInvalidValue;
     switch (nch) {
         case 1: return launch_one<DT, SOFTMAX, 1, 8>(G, rc, x, off, mask, out, s);
         case 2: return launch_one<DT, SOFTMAX, 2, 8>(G, rc, x, off, mask, out, s);
-        case 4: return launch_one<DT, SOFTMAX, 4, 8>(G, rc, x, off, mask, out, s);
     }
     return hipErrorInvalidValue;
 }
@@ -553,11 +600,12 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
     // A group wider than lane_bytes per pixel runs as 2^split_log groups of
     // lane_bytes, each lane item with its own share of the channels and the
     // group's offsets and mask: the tap geometry is then computed once per
-    // lane item, but a lane's sums and corner data stay within the
-    // registers of the 4-chunk kernel (f32, 64 bytes) or of the 1024-thread
-    // 2-chunk kernel (f16/bf16, 32 bytes: at 56x56x128 with 4 groups of 32
-    // channels, 71 us against 75 us for 64-byte items in 512-thread groups).
-    const int lane_bytes = es == 2 ? 32 : 64;
+    // lane item, but a lane's sums and corner data stay within the registers
+    // of the 1024-thread 2-chunk kernel.  At 56x56x128 with 4 groups of 32
+    // channels: f16 71 us against 75 for 64-byte items in 512-thread groups;
+    // f32 102 us against 117 for 64-byte items; 56x56x64 f32 (16 channels a
+    // group): 66 us against 72.
+    const int lane_bytes = 32;
     int split_log = 0;
     while ((G0.d * es >> split_log) > lane_bytes) ++split_log;
     if (split_log > 0 && (G0.d % (1 << split_log) != 0 || (G0.d >> split_log) * es != lane_bytes)) return false;
@@ -567,7 +615,7 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
     G.items = G0.items << split_log;
     if ((long)G0.items << split_log >= (1L << 31)) return false;
     const int nch = G.d * es / 16;
-    if (nch != 1 && nch != 2 && nch != 4) return false;
+    if (nch != 1 && nch != 2) return false;
     *gk = G;
     rc->split_log = split_log;
 
@@ -642,10 +690,10 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
         }
         return false;
     };
-    // Where a tap's data and the prefetched offsets fit in 128 VGPRs (nch * es
-    // <= 4: f16/bf16 with D <= 16, f32 with D = 4), a 1024-thread workgroup
-    // (four waves per SIMD) hides the LDS latency better; try that first.
-    return (nch * es <= 4 && try_plan(896)) || try_plan(448);
+    // A 1024-thread workgroup (four waves per SIMD, <= 128 VGPRs: a tap's
+    // 32-byte corners and the item's offsets fit) hides the LDS latency
+    // better than 512 threads; try that first.
+    return try_plan(896) || try_plan(448);
 }
 
 void device_limits(int* lds_limit, int* num_cus)

@@ -26,7 +26,7 @@ struct RingCfg {
     int ring_bytes;   // (R + 1) * pitch
     int lds_bytes;    // the ring (each lane loads its offsets and mask into registers)
     uint32_t x_bytes, off_bytes, mask_bytes;   // buffer extents, rounded up to whole dwords
-    int split_log;    // log2 of the lane items per channel group: a wide group (more than 64 bytes
+    int split_log;    // log2 of the lane items per channel group: a wide group (more than 32 bytes
                       // per pixel) runs as 2^split_log groups of its channels sharing its offsets and mask
 };
 
