@@ -262,7 +262,8 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
         }
 
         // ---- the next step's new rows go straight to LDS, its offsets to
-        // registers (fp32 in 1024-thread workgroups: tap by tap, below)
+        // registers (fp32 in 1024-thread workgroups: piece by piece as the
+        // taps consume them, below)
         constexpr bool TAPWISE = ES == 4 && WMAX == 16;
         if (s + 1 < nsteps) {
             if constexpr (!TAPWISE) load_offsets(s + 1);
@@ -338,7 +339,8 @@ __global__ __launch_bounds__(WMAX * 64) __attribute__((amdgpu_waves_per_eu(WMAX 
                 const uint32_t addr = __umul24(s0, (uint32_t)rc.pitch) + __umul24((uint32_t)xs, (uint32_t)rc.pb) + gbyte;
                 Ak = use ? addr : 0u;   // LDS columns 0, 1 of slots 0, 1: zeros
                 const float mm = use ? m[k] : 0.f;
-                // m(1-a) = m - ma: one multiply per pair of weights
+                // m(1-a) = m - m*a, m(1-a)(1-b) = m(1-a) - m(1-a)b, ...: one
+                // multiply per pair of weights
                 const float mb = mm * a, ma = mm - mb;
                 w10 = ma * b;
                 w00 = ma - w10;
