@@ -62,8 +62,9 @@ def test_stage1_forward_full(sds, dtype, softmax):
 @pytest.mark.parametrize("softmax", [False, True])
 def test_table10_shape(sds, dtype, softmax):
     """The pages' module shape 56x56x128, 4 groups of 32 channels, at the
-    benched batch of 64: f32 groups are 128 bytes per pixel and run as two
-    64-byte lane items sharing the group's offsets and mask."""
+    benched batch of 64: a group is 128 bytes per pixel in f32 (64 in
+    f16/bf16) and runs as four (two) 32-byte lane items sharing the group's
+    offsets and mask."""
     check_fwd(sds, "table10", 64, 56, 56, 128, 4, dtype, softmax)
 
 
@@ -80,7 +81,7 @@ def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
 def test_channel_splits(sds, dtype, c, g):
     """Every D = C/G path: one channel, odd D, D not a multiple of the vector
     width, vector widths exactly, several vectors per item, and groups of 512
-    channels (split into up to 32 lane items of 64 bytes)."""
+    channels (split into up to 64 lane items of 32 bytes)."""
     for softmax in (False, True):
         check_fwd(sds, "split", 2, 9, 11, c, g, dtype, softmax, seed=3)
 
