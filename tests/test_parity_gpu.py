@@ -68,6 +68,17 @@ def test_table10_shape(sds, dtype, softmax):
     check_fwd(sds, "table10", 64, 56, 56, 128, 4, dtype, softmax)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_chunks_ending_in_a_partial_step(sds, dtype, softmax):
+    """N=64, 50x56, C=64, G=4: every workgroup's chunk ends in a one-row
+    step (f32: 25 rows, six steps of 4 and one of 1; f16/bf16: 13 rows,
+    three of 4 and one of 1), so in the step before the last most lanes have
+    an item and none in the next (their next-step offsets and mask are not
+    loaded), and the last step runs a quarter full."""
+    check_fwd(sds, "partial-step", 64, 50, 56, 64, 4, dtype, softmax, seed=23)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("stage", ["stage2", "stage3"])
 def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
