@@ -882,6 +882,14 @@ def test_frontend_stages_full(sds, dtype, stage):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_frontend_one_block_per_wave(sds, dtype):
+    """N=48, 28x28x128, G=8: 2352 blocks of 16 pixels, between 8 and 16 per
+    CU, so the launch gives each CU one workgroup with a wave per block (10
+    waves, 240 workgroups for 2352 blocks: the last ones short)."""
+    check_frontend(sds, "one-block", 48, 28, 28, 128, 8, dtype, seed=41)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 1, 1, 8, 1), (2, 3, 70, 8, 2), (1, 5, 129, 24, 3), (3, 9, 11, 40, 5),
                                    (1, 2, 64, 136, 1), (1, 4, 65, 16, 16), (1, 7, 3, 512, 8), (1, 3, 10, 64, 2),
                                    (2, 6, 20, 256, 4), (1, 5, 7, 192, 2), (2, 4, 9, 256, 8),
