@@ -32,6 +32,21 @@ template <> __device__ __forceinline__ uint16_t from_f32<DT_BF16>(float v)
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values rounded to nearest even into one dword of the 16-bit
+// storage type, the first in the low half: gfx950's packed conversions (one
+// instruction for the pair; the f16 one rounds exactly as v_cvt_f16_f32, the
+// bf16 one as the bit-level rounding of from_f32<DT_BF16>).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_rne(float lo, float hi)
+{
+    uint32_t r;
+    if constexpr (DT == DT_F16)
+        asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    else
+        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+
 // Channels per 16-byte vector.
 template <int DT> struct Vec { static constexpr int N = 16 / (int)sizeof(typename Elem<DT>::T); };
 
@@ -71,20 +86,10 @@ __device__ __forceinline__ void store_vec(typename Elem<DT>::T* p, const float* 
         r.x = __float_as_uint(v[0]); r.y = __float_as_uint(v[1]);
         r.z = __float_as_uint(v[2]); r.w = __float_as_uint(v[3]);
     } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t lo, hi;
-            if constexpr (DT == DT_F16) {
-                lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
-                hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
-            } else {
-                lo = from_f32<DT_BF16>(v[2 * i]);
-                hi = from_f32<DT_BF16>(v[2 * i + 1]);
-            }
-            w[i] = lo | (hi << 16);
-        }
-        r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+        r.x = pack2_rne<DT>(v[0], v[1]);
+        r.y = pack2_rne<DT>(v[2], v[3]);
+        r.z = pack2_rne<DT>(v[4], v[5]);
+        r.w = pack2_rne<DT>(v[6], v[7]);
     }
     *reinterpret_cast<u32x4*>(p) = r;
 }

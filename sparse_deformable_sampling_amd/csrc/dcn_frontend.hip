@@ -126,8 +126,7 @@ __device__ __forceinline__ void widen8(u32x4 r, float* v)
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
-    return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<DT>(a)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<DT>(b)) << 16);
+    return pack2_rne<DT>(a, b);
 }
 
 // Copy `bytes` (even) bytes from LDS to global memory: 16 bytes per thread and
