@@ -174,7 +174,7 @@ __global__ __launch_bounds__(FT_THREADS) void dcn_offset_mask_k(Geom G, FrontCfg
     const bool quad = (NMASK & 3) == 0;   // 4 consecutive outputs of a pixel are 8-byte aligned in LDS
     const int prow = lane & 7, pchunk = (lane >> 4) + ((lane >> 1) & 4);
     const bool hi8 = (lane & 8) != 0;
-    constexpr int FP = (DT == DT_BF16 && MB == 4) ? 2 : 3;          // k-step pairs per batch (bf16 rounding needs the registers)
+    constexpr int FP = (DT == DT_BF16 && MB == 4) ? 2 : 3;          // k-step pairs per batch (3 spill at bf16 64-pixel tiles)
     const int nkb = (F.KP + 64 * FP - 1) / (64 * FP);              // batches per block
     constexpr int NWV = FT_THREADS / 64;
     const int nblk = wave < F.ncb ? (F.ncb - wave + NWV - 1) / NWV : 0;
