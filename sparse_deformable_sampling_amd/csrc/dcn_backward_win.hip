@@ -75,13 +75,10 @@ __device__ __forceinline__ unsigned long long to_fixed(float t)
     return (unsigned long long)(long long)r;
 }
 
-// Widen N consecutive storage-type values (N * sizeof(T) a multiple of 8
-// bytes, 8-byte aligned) to fp32.
-template <int DT, int N>
-__device__ __forceinline__ void load_n(const typename Elem<DT>::T* p, float* v)
+// RW consecutive dwords at p (RW a multiple of 4, or 2; p 16- or 8-byte aligned).
+template <int RW, typename T>
+__device__ __forceinline__ void load_words(const T* p, uint32_t* w)
 {
-    constexpr int RW = N * (int)sizeof(typename Elem<DT>::T) / 4;   // dwords
-    uint32_t w[RW];
     if constexpr (RW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < RW / 4; ++i) {
@@ -92,13 +89,6 @@ __device__ __forceinline__ void load_n(const typename Elem<DT>::T* p, float* v)
         static_assert(RW == 2, "8 or a multiple of 16 bytes");
         const uint2 r = *reinterpret_cast<const uint2*>(p);
         w[0] = r.x; w[1] = r.y;
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-        if constexpr (DT == DT_F32) v[j] = __uint_as_float(w[j]);
-        else if constexpr (DT == DT_F16)
-            v[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? w[j >> 1] >> 16 : w[j >> 1] & 0xffffu));
-        else v[j] = __uint_as_float((j & 1) ? w[j >> 1] & 0xffff0000u : w[j >> 1] << 16);
     }
 }
 
@@ -113,6 +103,33 @@ __device__ __forceinline__ void widen(const uint32_t* w, float* v)
             v[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? w[j >> 1] >> 16 : w[j >> 1] & 0xffffu));
         else v[j] = __uint_as_float((j & 1) ? w[j >> 1] & 0xffff0000u : w[j >> 1] << 16);
     }
+}
+
+// Sum over a lane's CPL channels of g_c * X_c, with X_c one corner's channels
+// as loaded (RW dwords of the storage type) and g_c grad_out: in fp32 as
+// widened floats (gf), and for f16/bf16 straight from the packed pairs (gp)
+// with the two-product dot instructions, whose products are exact in fp32 and
+// which sum in fp32.
+template <int DT, int CPL>
+__device__ __forceinline__ float corner_dot(const uint32_t* w, const float* gf, const uint32_t* gp)
+{
+    constexpr int RW = CPL * (int)sizeof(typename Elem<DT>::T) / 4;
+    float s = 0.f;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) s = fmaf(gf[j], __uint_as_float(w[j]), s);
+    } else if constexpr (DT == DT_F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w[i]), __builtin_bit_cast(h2, gp[i]), s, false);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w[i]), __builtin_bit_cast(b2, gp[i]), s, false);
+    }
+    return s;
 }
 
 // Buffer loads of RW dwords at byte offset o (an offset past the buffer reads zero).
@@ -197,7 +214,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
         float gm = 0.f;
         {
             float a[CPL];
-            load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, a);
+            uint32_t w[RW];
+            load_words<RW>(gout + pix * C + (long)g * D + CPL * c4, w);
+            widen<DT, CPL>(w, a);
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 gm = fmaxf(gm, fabsf(a[j]));
@@ -295,7 +314,9 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                 }
             }
             float gc[CPL];
-            load_n<DT, CPL>(gout + pix * C + (long)g * D + CPL * c4, gc);
+            uint32_t gp[RW];
+            load_words<RW>(gout + pix * C + (long)g * D + CPL * c4, gp);
+            widen<DT, CPL>(gp, gc);
             // Largest |g_c| of this lane's channels; NaN when one of them is
             // NaN (fmaxf would drop it), so that such a lane fails the
             // fixed-point test below.
@@ -312,22 +333,21 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
             float sdm = 0.f;
             // One tap's channel sums, its writes of grad_offset, and its
             // scatter into grad_x (LDS window or global), given its corners.
-            auto tap_finish = [&](int k, float a, float b, int x0, int y0, const uint32_t* o4, const float* X00,
-                                  const float* X01, const float* X10, const float* X11) {
-                float sm = 0.f, sdx = 0.f, sdy = 0.f;
+            auto tap_finish = [&](int k, float a, float b, int x0, int y0, const uint32_t* o4, const uint32_t* X00,
+                                  const uint32_t* X01, const uint32_t* X10, const uint32_t* X11) {
                 const float wa = 1.f - a, wb = 1.f - b;
                 const float w4[4] = {wa * wb, a * wb, wa * b, a * b};
-                // Per channel, as interpolations: top/bottom rows at a, then b;
-                // dv/da = t0 + b (t1 - t0) and dv/db = bottom - top.
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    const float t0 = X01[j] - X00[j], t1 = X11[j] - X10[j];
-                    const float top = fmaf(a, t0, X00[j]), bot = fmaf(a, t1, X10[j]);
-                    const float dvdb = bot - top;
-                    sm = fmaf(gc[j], fmaf(b, dvdb, top), sm);
-                    sdx = fmaf(gc[j], fmaf(b, t1 - t0, t0), sdx);
-                    sdy = fmaf(gc[j], dvdb, sdy);
-                }
+                // The sample is v_c = sum_q w_q X_qc, linear in the corners, so
+                // the channel sums need only each corner's dot product with
+                // grad_out, S_q = sum_c g_c X_qc:
+                //   sum_c g_c v_c     = sum_q w_q S_q,
+                //   sum_c g_c dv_c/da = (1-b)(S01 - S00) + b (S11 - S10),
+                //   sum_c g_c dv_c/db = (1-a)(S10 - S00) + a (S11 - S01).
+                const float s00 = corner_dot<DT, CPL>(X00, gc, gp), s01 = corner_dot<DT, CPL>(X01, gc, gp);
+                const float s10 = corner_dot<DT, CPL>(X10, gc, gp), s11 = corner_dot<DT, CPL>(X11, gc, gp);
+                float sm = fmaf(w4[0], s00, fmaf(w4[1], s01, fmaf(w4[2], s10, w4[3] * s11)));
+                float sdx = fmaf(wb, s01 - s00, b * (s11 - s10));
+                float sdy = fmaf(wa, s10 - s00, a * (s11 - s01));
                 if (gx) {
                     const bool small = fabsf(m[k]) * gl < Bf;   // every contribution of this tap below B
 #pragma unroll
@@ -405,9 +425,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
 #pragma unroll
                         for (int q = 0; q < 4; ++q) load_raw<RW>(xr, o4[k + 1][q], buf[(k + 1) & 1][q]);
                     }
-                    float X[4][CPL];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) widen<DT, CPL>(buf[k & 1][q], X[q]);
+                    const uint32_t (*X)[RW] = buf[k & 1];
                     tap_finish(k, fa[k], fb[k], xk[k], yk[k], o4[k], X[0], X[1], X[2], X[3]);
                 }
             } else {
@@ -419,11 +437,11 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                 float a = 0.f, b = 0.f;
                 int x0 = -2, y0 = -2;
                 uint32_t o4[4] = {OOB, OOB, OOB, OOB};
-                float X[4][CPL];
+                uint32_t X[4][RW];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int j = 0; j < CPL; ++j) X[q][j] = 0.f;
+                    for (int j = 0; j < RW; ++j) X[q][j] = 0u;
                 if (coord_ok(tx) && coord_ok(ty)) {
                     const float fx = floorf(tx), fy = floorf(ty);
                     a = tx - fx;
@@ -440,11 +458,7 @@ __global__ __launch_bounds__(512) void dcn_bwd_win(Geom G, BwdWinCfg bc, const t
                         o4[2] = (cy1 && cx0) ? b00 + bR : OOB;
                         o4[3] = (cy1 && cx1) ? b00 + bR + bC : OOB;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            uint32_t w[RW];
-                            load_raw<RW>(xr, o4[q], w);
-                            widen<DT, CPL>(w, X[q]);
-                        }
+                        for (int q = 0; q < 4; ++q) load_raw<RW>(xr, o4[q], X[q]);
                     }
                 }
                 tap_finish(k, a, b, x0, y0, o4, X[0], X[1], X[2], X[3]);
