@@ -47,7 +47,32 @@ def lib():
     if not os.path.exists(LIB_PATH) and "LIBDCN_PATH" not in os.environ:
         from . import build as _build
         _build.build()
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = load(LIB_PATH)
+    return _lib
+
+
+COUNT_LIB_PATH = os.path.join(HERE, "libdcn_count.so")
+_count_lib = None
+
+
+def count_lib():
+    """The write-counting debug build, libdcn_count.so (include/dcn_debug.h):
+    the entry points of libdcn.so plus dcn_debug_count_writes.  Built by
+    build.build(); loaded only by tests."""
+    global _count_lib
+    if _count_lib is None:
+        if not os.path.exists(COUNT_LIB_PATH):
+            raise FileNotFoundError("%s is not built (sparse_deformable_sampling_amd.build.build())" % COUNT_LIB_PATH)
+        L = load(COUNT_LIB_PATH)
+        L.dcn_debug_count_writes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        L.dcn_debug_count_writes.restype = ctypes.c_int
+        _count_lib = L
+    return _count_lib
+
+
+def load(path):
+    """Open a build of libdcn at path and declare its entry points' argument types."""
+    L = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     L.dcn_output_size.argtypes = [ctypes.POINTER(DcnDesc), ctypes.POINTER(ctypes.c_int32),
                                   ctypes.POINTER(ctypes.c_int32)]
@@ -82,7 +107,6 @@ def lib():
     L.dcn_status_str.restype = ctypes.c_char_p
     L.dcn_last_error.argtypes = []
     L.dcn_last_error.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

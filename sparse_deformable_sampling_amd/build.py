@@ -26,14 +26,44 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libdcn.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + sources()
+# The debug build: the same sources with every forward output store counted
+# (DCN_COUNT_WRITES; include/dcn_debug.h).  Only the tests load it.
+COUNT_LIB = os.path.join(HERE, "libdcn_count.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+
+
+def _compile_link(lib: str, defines: list, verbose: bool) -> str:
+    """Compile each source to an object (in parallel), then link lib."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = "count" if defines else "prod"
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cflags = [f for f in FLAGS if f != "-shared"] + defines + ["-I", os.path.join(ROOT, "include"), "-c"]
+    jobs = []
+    for src in sources():
+        obj = os.path.join(BUILD_DIR, "%s.%s.%d.o" % (os.path.basename(src)[:-4], tag, os.getpid()))
+        jobs.append(([HIPCC] + cflags + ["-o", obj, src], obj))
     if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+        for cmd, _ in jobs:
+            print(" ".join(cmd), file=sys.stderr)
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: subprocess.check_call(j[0]), jobs))
+    tmp = lib + ".tmp%d" % os.getpid()
+    try:
+        subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs])
+        os.replace(tmp, lib)
+    finally:
+        for _, o in jobs:
+            if os.path.exists(o):
+                os.remove(o)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libdcn.so, and the write-counting debug
+    build libdcn_count.so (always recompiles both)."""
+    _compile_link(LIB, [], verbose)
+    _compile_link(COUNT_LIB, ["-DDCN_COUNT_WRITES"], verbose)
     return LIB
 
 

@@ -9,6 +9,9 @@
 #include "../../include/dcn.h"
 #include "dcn_launch.h"
 #include "dcn_ring.h"
+#ifdef DCN_COUNT_WRITES
+#include "../../include/dcn_debug.h"
+#endif
 
 namespace {
 
@@ -409,5 +412,19 @@ dcn_status msda_backward_ws(const msda_desc* d, const int32_t* shapes, const voi
     return msda_backward_impl(d, shapes, value, loc, attn, grad_out, grad_value, grad_loc, grad_attn, workspace,
                               workspace_bytes, true, stream);
 }
+
+#ifdef DCN_COUNT_WRITES
+dcn_status dcn_debug_count_writes(unsigned int* counts, const void* out, size_t n, int dtype)
+{
+    if (dtype != DCN_F32 && dtype != DCN_F16 && dtype != DCN_BF16)
+        return fail(DCN_ERR_INVALID, "dcn_debug_count_writes: bad dtype %d", dtype);
+    if (counts && !out) return fail(DCN_ERR_INVALID, "dcn_debug_count_writes: NULL out");
+    const unsigned int es = dtype == DCN_F32 ? 4u : 2u;
+    hipError_t e = dcn::ring_count_writes(counts, out, n, es);
+    if (e == hipSuccess) e = dcn::fwd_count_writes(counts, out, n, es);
+    if (e == hipSuccess) e = dcn::msda_count_writes(counts, out, n, es);
+    return hip_status(e);
+}
+#endif
 
 }  // extern "C"

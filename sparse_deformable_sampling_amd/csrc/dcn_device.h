@@ -12,6 +12,42 @@
 
 namespace dcn {
 
+#ifdef DCN_COUNT_WRITES
+// Debug build only: every store of an op output also adds one, per element
+// written, to counts[i] for element i of the registered output buffer, or to
+// counts[n] for an address outside it, so the host can check that each
+// output element of an atomic-free kernel has exactly one writer and that no
+// store lands elsewhere.  Each translation unit holds its own registration
+// (NULL counts: nothing is counted, as for stores to LDS or to other buffers
+// in translation units that never register one).
+struct WriteCounts {
+    unsigned int* counts;
+    unsigned long long base, n;
+    unsigned int es;
+};
+static __device__ WriteCounts g_write_counts;
+
+__device__ __forceinline__ void count_writes(const void* p, int elems)
+{
+    const WriteCounts w = g_write_counts;
+    if (!w.counts) return;
+    for (int i = 0; i < elems; ++i) {
+        const unsigned long long a = (unsigned long long)p + (unsigned long long)i * w.es;
+        const bool in = a >= w.base && (a - w.base) % w.es == 0 && (a - w.base) / w.es < w.n;
+        atomicAdd(w.counts + (in ? (a - w.base) / w.es : w.n), 1u);
+    }
+}
+
+#define DCN_WRITE_COUNT_SETTER(name)                                                                        \
+    hipError_t name(unsigned int* counts, const void* base, unsigned long long n, unsigned int es)          \
+    {                                                                                                       \
+        const WriteCounts w = {counts, (unsigned long long)base, n, es};                                   \
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_write_counts), &w, sizeof w);                                 \
+    }
+#else
+__device__ __forceinline__ void count_writes(const void*, int) {}
+#endif
+
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { using T = float; };
 template <> struct Elem<DT_F16> { using T = _Float16; };
@@ -92,6 +128,7 @@ __device__ __forceinline__ void store_vec(typename Elem<DT>::T* p, const float* 
         r.w = pack2_rne<DT>(v[6], v[7]);
     }
     *reinterpret_cast<u32x4*>(p) = r;
+    count_writes(p, 16 / (int)sizeof(typename Elem<DT>::T));
 }
 
 // exp(z) for z <= 0 through the hardware base-2 exponential.

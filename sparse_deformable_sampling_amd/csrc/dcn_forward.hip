@@ -266,7 +266,10 @@ __global__ __launch_bounds__(256) void dcn_fwd_generic(Geom G, const typename El
                 for (int i = 0; i < nc; ++i) acc[i] = fmaf(w[q], to_f32(r[o[q] + i]), acc[i]);
             }
         }
-        for (int i = 0; i < nc; ++i) ob_out[c0 + i] = from_f32<DT>(acc[i]);
+        for (int i = 0; i < nc; ++i) {
+            ob_out[c0 + i] = from_f32<DT>(acc[i]);
+            count_writes(ob_out + c0 + i, 1);
+        }
     }
 }
 
@@ -316,5 +319,9 @@ hipError_t launch_dcn_forward(const Geom& G, int dtype, const void* x, const voi
     }
     return hipErrorInvalidValue;
 }
+
+#ifdef DCN_COUNT_WRITES
+DCN_WRITE_COUNT_SETTER(fwd_count_writes)
+#endif
 
 }  // namespace dcn

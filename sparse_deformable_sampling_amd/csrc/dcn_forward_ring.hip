@@ -718,4 +718,8 @@ void device_limits(int* lds_limit, int* num_cus)
     *num_cus = cached_cus[dev];
 }
 
+#ifdef DCN_COUNT_WRITES
+DCN_WRITE_COUNT_SETTER(ring_count_writes)
+#endif
+
 }  // namespace dcn

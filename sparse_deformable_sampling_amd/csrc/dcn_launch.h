@@ -60,4 +60,13 @@ hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const flo
                                 const float* gout, float* gvalue, float* gloc, float* gattn, void* ws,
                                 size_t ws_bytes, hipStream_t s);
 
+#ifdef DCN_COUNT_WRITES
+// Debug build only (libdcn_count.so): point the output-write counter of the
+// forward kernels' translation units at counts[0..n] for the output buffer
+// `base` of n elements of es bytes (counts == NULL: stop counting).
+hipError_t ring_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
+hipError_t fwd_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
+hipError_t msda_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
+#endif
+
 }  // namespace dcn

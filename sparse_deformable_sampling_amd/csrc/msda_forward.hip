@@ -468,4 +468,8 @@ hipError_t launch_msda_forward_ref(const MsdaGeom& G, int ref_dims, const float*
     return ref_dims == 4 ? launch_src<4>(G, value, src, attn, out, s) : launch_src<2>(G, value, src, attn, out, s);
 }
 
+#ifdef DCN_COUNT_WRITES
+DCN_WRITE_COUNT_SETTER(msda_count_writes)
+#endif
+
 }  // namespace dcn

@@ -33,6 +33,24 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
 
 
+def test_debug_build_exports_the_write_counter():
+    """libdcn_count.so (the write-counting debug build) exports what
+    include/dcn.h and include/dcn_debug.h declare; libdcn.so does not carry
+    the debug entry point.  A bad dtype is rejected before any HIP call."""
+    if not os.path.exists(B.COUNT_LIB_PATH):
+        pytest.skip("libdcn_count.so not built")
+    debug_h = open(os.path.join(os.path.dirname(HEADER), "dcn_debug.h")).read()
+    debug_h = re.sub(r"/\*.*?\*/", "", debug_h, flags=re.S)
+    debug = re.findall(r"^\s*dcn_status\s+(\w+)\s*\(", debug_h, flags=re.M)
+    assert debug == ["dcn_debug_count_writes"]
+    L = B.count_lib()
+    for name in declared_functions() + debug:
+        assert hasattr(L, name), name
+    assert not hasattr(ctypes.CDLL(B.LIB_PATH), "dcn_debug_count_writes")
+    assert L.dcn_debug_count_writes(None, None, 0, 7) == B.DCN_ERR_INVALID
+    assert L.dcn_debug_count_writes(ctypes.c_void_p(64), None, 16, B.DCN_F32) == B.DCN_ERR_INVALID
+
+
 def test_struct_layouts_match_header():
     # the header's structs are all 4-byte fields
     assert ctypes.sizeof(B.DcnDesc) == 16 * 4
