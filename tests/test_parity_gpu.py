@@ -87,6 +87,24 @@ def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("case", ["9x9-g16", "27-stride2", "13x11-dcnv3", "wide-offsets"])
+def test_small_maps_many_images(sds, dtype, case):
+    """Small maps in large batches, where a row chunk is most or all of an
+    image and its halo reaches past the image on both sides: a 9x9 map with
+    16 groups (batch 128); a 27x27 map at stride 2 (14x14 out, 20 groups); a
+    ragged 13x11 map with the DCNv3 softmax (batch 256); and offsets wide
+    enough that many samples fall outside the image, above and below it."""
+    if case == "9x9-g16":
+        check_fwd(sds, "whole", 128, 9, 9, 256, 16, dtype, False, seed=31)
+    elif case == "27-stride2":
+        check_fwd(sds, "whole", 64, 27, 27, 320, 20, dtype, False, seed=32, stride=2)
+    elif case == "13x11-dcnv3":
+        check_fwd(sds, "whole", 256, 13, 11, 96, 6, dtype, True, seed=33)
+    else:
+        check_fwd(sds, "whole", 64, 14, 14, 320, 20, dtype, False, offset=("normal", 6.0), seed=34)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("c,g", [(4, 4), (12, 4), (15, 3), (16, 2), (32, 1), (64, 1), (256, 2), (24, 3), (512, 1),
                                  (1024, 2)])
 def test_channel_splits(sds, dtype, c, g):
