@@ -560,7 +560,7 @@ hipError_t launch_ring_typed(const Geom& G, const RingCfg& rc, const void* x, co
 {
     using T = typename Elem<DT>::T;
     const int nch = G.d * (int)sizeof(T) / 16;   // 1 or 2: lane items are at most 32 bytes
-    const bool wide = rc.threads > 512;
+    const bool wide = rc.wmax == 16;
     if (wide && nch == 1) return launch_one<DT, SOFTMAX, 1, 16>(G, rc, x, off, mask, out, s);
     if (wide && nch == 2) return launch_one<DT, SOFTMAX, 2, 16>(G, rc, x, off, mask, out, s);
     if (wide) return hipErrorInvalidValue;
@@ -621,10 +621,73 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
     *gk = G;
     rc->split_log = split_log;
 
-    // For a target number of items per step, try group sets from all groups
-    // down; take the first that keeps a halo of at least HY_MIN rows in LDS
-    // with one workgroup per CU.
     const int HY_MIN = 4, HY_MAX = 8;
+    // The plan for gs groups per workgroup and tr output rows per step, if
+    // its ring fits in `lds` bytes with a halo of at least HY_MIN rows: cus is
+    // the number of workgroups wanted at least (CUs times workgroups per CU),
+    // wmax the kernel variant.
+    auto fit = [&](int gs, int tr, int max_thr, long cus, long lds, int wmax) -> bool {
+        const int items_row = G.wo * gs;
+        const int items_step = tr * items_row;
+        const int threads = (items_step + 63) / 64 * 64;
+        const int pb = gs * G.d * es;
+        const int cpp = pb / 16;
+        // W image columns, two zero columns left and one right, and 5 bank
+        // groups of skew so that nearby rows spread over the banks.
+        const long pitch = (long)(G.w + 3) * pb + 80;
+        const int nwaves = threads / 64;
+        const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
+        if (row_iters > 4 || threads > max_thr) return false;   // ROW_IT
+        const int adv = tr * G.sh;
+        int hy = -1, nw = 0, R = 0;
+        for (int h = HY_MAX; h >= HY_MIN; --h) {
+            const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
+            const int Rh = nwh + adv;
+            if ((long)(Rh + 1) * pitch <= lds) {
+                hy = h;
+                nw = nwh;
+                R = Rh;
+                break;
+            }
+        }
+        if (hy < 0) return false;
+        const int gsets = G.g / gs;
+        const long units = (long)G.n * gsets;
+        int chunks = (int)std::max(1L, (cus + units - 1) / units);
+        chunks = std::min(chunks, (G.ho + tr - 1) / tr);
+        int chunk_rows = (G.ho + chunks - 1) / chunks;
+        // A chunk need not be a whole number of steps (its last step may be
+        // partial): rounding it up would leave the last chunk short.
+        chunks = (G.ho + chunk_rows - 1) / chunk_rows;
+        if (units * chunks >= (1L << 31)) return false;
+        rc->gs = gs;
+        rc->gsets = gsets;
+        rc->pb = pb;
+        rc->cpp = cpp;
+        rc->pitch = (int)pitch;
+        rc->R = R;
+        rc->nw = nw;
+        rc->hy = hy;
+        rc->tr = tr;
+        rc->chunk_rows = chunk_rows;
+        rc->chunks = chunks;
+        rc->nwg = (int)(units * chunks);
+        rc->threads = threads;
+        rc->wmax = wmax;
+        rc->row_iters = row_iters;
+        rc->ring_bytes = (int)((R + 1) * pitch);
+        rc->lds_bytes = rc->ring_bytes;   // offsets and mask go to registers, not LDS
+        // Buffer loads range-check each dword: a dword that straddles num_records
+        // reads as zero.  Rounding the extents up to whole dwords keeps the last
+        // values of an odd-length 16-bit tensor readable; the extra bytes share
+        // a dword (and so a page) with valid data and are never used.
+        rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
+        rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
+        rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
+        return true;
+    };
+    // For a target number of items per step, try group sets from all groups
+    // down; take the first that fits with one workgroup per CU.
     auto try_plan = [&](int target) -> bool {
         const int max_thr = target > 448 ? 1024 : 512;
         for (int gs = G.g; gs >= 1; --gs) {
@@ -633,69 +696,36 @@ bool plan_ring(const Geom& G0, int dtype, const void* x, const void* off, const 
             if (items_row > max_thr) continue;
             int tr = (target + items_row - 1) / items_row;
             tr = std::max(1, std::min(tr, std::min(max_thr / items_row, G.ho)));
-            const int items_step = tr * items_row;
-            const int threads = (items_step + 63) / 64 * 64;
-            const int pb = gs * G.d * es;
-            const int cpp = pb / 16;
-            // W image columns, two zero columns left and one right, and 5 bank
-            // groups of skew so that nearby rows spread over the banks.
-            const long pitch = (long)(G.w + 3) * pb + 80;
-            const int nwaves = threads / 64;
-            const int row_iters = (int)((((long)G.w * cpp + 63) / 64 + nwaves - 1) / nwaves);
-            if (row_iters > 4) continue;   // ROW_IT
-            const int adv = tr * G.sh;
-            int hy = -1, nw = 0, R = 0;
-            for (int h = HY_MAX; h >= HY_MIN; --h) {
-                const int nwh = (tr - 1) * G.sh + (G.kh - 1) * G.dh + 2 + 2 * h;
-                const int Rh = nwh + adv;
-                if ((long)(Rh + 1) * pitch <= lds_limit) {
-                    hy = h;
-                    nw = nwh;
-                    R = Rh;
-                    break;
-                }
-            }
-            if (hy < 0) continue;
-            const int gsets = G.g / gs;
-            const long units = (long)G.n * gsets;
-            int chunks = (int)std::max(1L, ((long)num_cus + units - 1) / units);
-            chunks = std::min(chunks, (G.ho + tr - 1) / tr);
-            int chunk_rows = (G.ho + chunks - 1) / chunks;
-            // A chunk need not be a whole number of steps (its last step may be
-            // partial): rounding it up would leave the last chunk short.
-            chunks = (G.ho + chunk_rows - 1) / chunk_rows;
-            if (units * chunks >= (1L << 31)) continue;
-            rc->gs = gs;
-            rc->gsets = gsets;
-            rc->pb = pb;
-            rc->cpp = cpp;
-            rc->pitch = (int)pitch;
-            rc->R = R;
-            rc->nw = nw;
-            rc->hy = hy;
-            rc->tr = tr;
-            rc->chunk_rows = chunk_rows;
-            rc->chunks = chunks;
-            rc->nwg = (int)(units * chunks);
-            rc->threads = threads;
-            rc->row_iters = row_iters;
-            rc->ring_bytes = (int)((R + 1) * pitch);
-            rc->lds_bytes = rc->ring_bytes;   // offsets and mask go to registers, not LDS
-            // Buffer loads range-check each dword: a dword that straddles num_records
-            // reads as zero.  Rounding the extents up to whole dwords keeps the last
-            // values of an odd-length 16-bit tensor readable; the extra bytes share
-            // a dword (and so a page) with valid data and are never used.
-            rc->x_bytes = (uint32_t)((x_bytes + 3) & ~3L);
-            rc->off_bytes = (uint32_t)((off_bytes + 3) & ~3L);
-            rc->mask_bytes = (uint32_t)((mask_bytes + 3) & ~3L);
-            return true;
+            if (fit(gs, tr, max_thr, num_cus, lds_limit, max_thr > 512 ? 16 : 8)) return true;
+        }
+        return false;
+    };
+    // Two workgroups per CU, each with half the LDS and at most 512 threads
+    // of the 128-register kernel: while one loads its window the other
+    // computes.
+    auto try_pair = [&]() -> bool {
+        for (int gs = G.g; gs >= 1; --gs) {
+            if (G.g % gs) continue;
+            const int items_row = G.wo * gs;
+            if (items_row > 512) continue;
+            const int tr = std::max(1, std::min((448 + items_row - 1) / items_row, std::min(512 / items_row, G.ho)));
+            if (fit(gs, tr, 512, 2L * num_cus, lds_limit / 2, 16)) return true;
         }
         return false;
     };
     // A 1024-thread workgroup (four waves per SIMD, <= 128 VGPRs: a tap's
     // 32-byte corners and the item's offsets fit) hides the LDS latency
     // better than 512 threads; try that first.
-    return try_plan(896) || try_plan(448);
+    if (!(try_plan(896) || try_plan(448))) return false;
+    // Where a workgroup of that plan walks a single step, its window load is
+    // not overlapped with any compute; two workgroups per CU then overlap
+    // one's loads with the other's step.
+    if ((rc->chunk_rows + rc->tr - 1) / rc->tr <= 1) {
+        const RingCfg one = *rc;
+        if (try_pair() && rc->nwg >= 2L * num_cus) return true;
+        *rc = one;
+    }
+    return true;
 }
 
 void device_limits(int* lds_limit, int* num_cus)

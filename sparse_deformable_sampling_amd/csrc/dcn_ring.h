@@ -22,6 +22,7 @@ struct RingCfg {
     int chunks;       // row chunks per (image, group set)
     int nwg;          // workgroups
     int threads;      // threads per workgroup (one item per thread per step)
+    int wmax;         // kernel variant: 16 (<= 128 VGPRs, four waves per SIMD) or 8 (<= 256 VGPRs)
     int row_iters;    // 1 KB copy instructions per wave for one input row
     int ring_bytes;   // (R + 1) * pitch
     int lds_bytes;    // the ring (each lane loads its offsets and mask into registers)
