@@ -254,6 +254,22 @@ def msda_line_roofline(kernel_us):
             "floor_us": round(floor_us, 1), "frac": round(floor_us / kernel_us, 4)}
 
 
+# fp32 multiply-add issue rate without packed fp32 instructions (which this
+# library does not use): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+VALU_FMA_PEAK_TFLOPS = CU_COUNT * 4 * 16 * 2 * CLOCK_GHZ / 1e3
+
+
+def valu_roofline(kernel_us, items=64 * 56 * 56 * 4, d=16, taps=9):
+    """The headline's second ceiling, the vector ALU: its arithmetic is one
+    fp32 multiply-add per (item, channel, tap, corner), 2 flops each (the
+    tap geometry, computed once per item and tap, comes on top)."""
+    flops = items * d * taps * 4 * 2
+    achieved = flops / (kernel_us * 1e-6) / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(VALU_FMA_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FMA_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+            "flops": "4 corners x 9 taps x D channels x 2 per (pixel, group) item: the bilinear multiply-adds in fp32"}
+
+
 def msda_ref_runner(torch, seed=1):
     """MSDA read with locations formed in the kernel: the encoder shape with
     per-image valid ratios and right/bottom padding, every cell a query that
@@ -640,6 +656,7 @@ def main():
                      "algorithmic_bytes_per_launch": s["min_bytes"],
                      "algorithmic_bytes": "(2*D + 3*K) * 2 B per (pixel, group) item: x read once, offsets, mask, "
                                           "out written once; 118 B x 802816 items"},
+        "roofline_valu": valu_roofline(s["kernel_us_mean"]),
         "tiny_dcnv3_f32": tiny,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": None if args.no_cpu_baseline else cpu_baseline_threads(args.cpu_seconds),
