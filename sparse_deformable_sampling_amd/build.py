@@ -46,16 +46,16 @@ def _compile_link(lib: str, defines: list, verbose: bool) -> str:
         for cmd, _ in jobs:
             print(" ".join(cmd), file=sys.stderr)
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 16))
-    with ThreadPoolExecutor(workers) as ex:
-        list(ex.map(lambda j: subprocess.check_call(j[0]), jobs))
     tmp = lib + ".tmp%d" % os.getpid()
     try:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda j: subprocess.check_call(j[0]), jobs))
         subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs])
         os.replace(tmp, lib)
     finally:
-        for _, o in jobs:
-            if os.path.exists(o):
-                os.remove(o)
+        for f in [o for _, o in jobs] + [tmp]:
+            if os.path.exists(f):
+                os.remove(f)
     return lib
 
 
