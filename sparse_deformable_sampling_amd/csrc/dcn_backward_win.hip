@@ -57,9 +57,15 @@ namespace {
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int KMAX_WIN = 64;
 
+// Sum of v over aligned groups of `width` lanes (a power of two).  Partners
+// 1 and 2 apart are read with DPP quad permutations, which stay in the VALU;
+// __shfl_xor would go through the LDS crossbar (ds_bpermute) and wait behind
+// the wave's queued LDS atomics on every tap.
 __device__ __forceinline__ float lane_sum(float v, int width)
 {
-    for (int o = 1; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (width > 1) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    if (width > 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    for (int o = 4; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
