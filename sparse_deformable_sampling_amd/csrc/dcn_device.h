@@ -131,6 +131,28 @@ __device__ __forceinline__ void store_vec(typename Elem<DT>::T* p, const float* 
     count_writes(p, 16 / (int)sizeof(typename Elem<DT>::T));
 }
 
+// Max or sum over aligned groups of w lanes (w a power of two, every lane of
+// a group active), each lane of a group ending with the group's result: DPP
+// moves within a row of 16 (neighbours, pairs, then mirrors within 8 and 16
+// lanes), which stay in the VALU, and cross-lane shuffles beyond 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <bool MAX>
+__device__ __forceinline__ float group_reduce(float v, int w)
+{
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if (w >= 2) v = op(v, dpp_read<0xB1>(v));    // quad_perm [1,0,3,2]
+    if (w >= 4) v = op(v, dpp_read<0x4E>(v));    // quad_perm [2,3,0,1]
+    if (w >= 8) v = op(v, dpp_read<0x141>(v));   // half-row mirror
+    if (w >= 16) v = op(v, dpp_read<0x140>(v));  // row mirror
+    for (int o = 16; o < w; o <<= 1) v = op(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
 // exp(z) for z <= 0 through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_nonpos(float z) { return exp2f(z * 1.44269504088896341f); }
 

@@ -275,10 +275,10 @@ __global__ __launch_bounds__(256) void msda_fwd_tile(MsdaGeom G, int LPlog, int 
         float A = attn[item * LP + i];
         if constexpr (SOFTMAX) {
             float mx = A;
-            for (int o = 1; o < LP; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            mx = group_reduce<true>(mx, LP);
             const float e = exp_nonpos(A - mx);
             float sum = e;
-            for (int o = 1; o < LP; o <<= 1) sum += __shfl_xor(sum, o, 64);
+            sum = group_reduce<false>(sum, LP);
             A = e * (1.0f / sum);
         }
         const int l = i / G.P;
