@@ -87,21 +87,25 @@ def test_dcnv4_stage2_stage3_full(sds, dtype, stage):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("case", ["9x9-g16", "27-stride2", "13x11-dcnv3", "wide-offsets"])
+@pytest.mark.parametrize("case", ["9x9-g16", "27-stride2", "13x11-dcnv3", "wide-offsets", "13x13-ragged-chunks"])
 def test_small_maps_many_images(sds, dtype, case):
     """Small maps in large batches, where a row chunk is most or all of an
     image and its halo reaches past the image on both sides: a 9x9 map with
     16 groups (batch 128); a 27x27 map at stride 2 (14x14 out, 20 groups); a
-    ragged 13x11 map with the DCNv3 softmax (batch 256); and offsets wide
-    enough that many samples fall outside the image, above and below it."""
+    ragged 13x11 map with the DCNv3 softmax (batch 256); offsets wide
+    enough that many samples fall outside the image, above and below it; and
+    a 13x13 map with 20 groups, whose chunks of one step each (two workgroups
+    per CU) are 7 and 6 rows, with the DCNv3 softmax."""
     if case == "9x9-g16":
-        check_fwd(sds, "whole", 128, 9, 9, 256, 16, dtype, False, seed=31)
+        check_fwd(sds, "small-map", 128, 9, 9, 256, 16, dtype, False, seed=31)
     elif case == "27-stride2":
-        check_fwd(sds, "whole", 64, 27, 27, 320, 20, dtype, False, seed=32, stride=2)
+        check_fwd(sds, "small-map", 64, 27, 27, 320, 20, dtype, False, seed=32, stride=2)
     elif case == "13x11-dcnv3":
-        check_fwd(sds, "whole", 256, 13, 11, 96, 6, dtype, True, seed=33)
+        check_fwd(sds, "small-map", 256, 13, 11, 96, 6, dtype, True, seed=33)
+    elif case == "wide-offsets":
+        check_fwd(sds, "small-map", 64, 14, 14, 320, 20, dtype, False, offset=("normal", 6.0), seed=34)
     else:
-        check_fwd(sds, "whole", 64, 14, 14, 320, 20, dtype, False, offset=("normal", 6.0), seed=34)
+        check_fwd(sds, "small-map", 64, 13, 13, 320, 20, dtype, True, seed=35)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
