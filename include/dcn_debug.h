@@ -5,10 +5,12 @@
  *
  * The forward ops are atomic-free: every output element is written by exactly
  * one store of one thread.  In the debug build every store of an output of
- * dcn_forward and of msda_forward / msda_forward_ref (their vector paths) also
- * adds one to a per-element counter, so a caller can check that claim after a
- * launch: each of counts[0..n) must read 1 and counts[n] (stores whose address
- * falls outside the registered buffer) must read 0.
+ * dcn_forward, of msda_forward / msda_forward_ref (their vector paths) and of
+ * dcn_offset_mask (offsets and mask) also adds one to a per-element counter,
+ * so a caller can check that claim after a launch: each of counts[0..n) must
+ * read 1, and counts[n] counts the output stores whose address falls outside
+ * the registered buffer (0 for a single-output op; for dcn_offset_mask, the
+ * elements of its other output).
  */
 #ifndef DCN_DEBUG_H
 #define DCN_DEBUG_H

@@ -423,6 +423,7 @@ dcn_status dcn_debug_count_writes(unsigned int* counts, const void* out, size_t 
     hipError_t e = dcn::ring_count_writes(counts, out, n, es);
     if (e == hipSuccess) e = dcn::fwd_count_writes(counts, out, n, es);
     if (e == hipSuccess) e = dcn::msda_count_writes(counts, out, n, es);
+    if (e == hipSuccess) e = dcn::frontend_count_writes(counts, out, n, es);
     return hip_status(e);
 }
 #endif

@@ -18,8 +18,8 @@ namespace dcn {
 // counts[n] for an address outside it, so the host can check that each
 // output element of an atomic-free kernel has exactly one writer and that no
 // store lands elsewhere.  Each translation unit holds its own registration
-// (NULL counts: nothing is counted, as for stores to LDS or to other buffers
-// in translation units that never register one).
+// (NULL counts: nothing is counted, as in translation units that never
+// register one).  Stores to LDS are never counted.
 struct WriteCounts {
     unsigned int* counts;
     unsigned long long base, n;
@@ -30,7 +30,7 @@ static __device__ WriteCounts g_write_counts;
 __device__ __forceinline__ void count_writes(const void* p, int elems)
 {
     const WriteCounts w = g_write_counts;
-    if (!w.counts) return;
+    if (!w.counts || __builtin_amdgcn_is_shared((const __attribute__((address_space(0))) void*)p)) return;   // LDS stores are not outputs
     for (int i = 0; i < elems; ++i) {
         const unsigned long long a = (unsigned long long)p + (unsigned long long)i * w.es;
         const bool in = a >= w.base && (a - w.base) % w.es == 0 && (a - w.base) / w.es < w.n;

@@ -134,12 +134,16 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 __device__ __forceinline__ void copy_out(const unsigned char* src, unsigned char* dst, int bytes, int tid)
 {
     const int nv = bytes >> 4;
-    for (int u = tid; u < nv; u += FT_THREADS)
+    for (int u = tid; u < nv; u += FT_THREADS) {
         *reinterpret_cast<uint4*>(dst + (size_t)u * 16) = *reinterpret_cast<const uint4*>(src + u * 16);
+        count_writes(dst + (size_t)u * 16, 8);
+    }
     const int tail = (bytes - nv * 16) >> 1;
-    if (tid < tail)
+    if (tid < tail) {
         *reinterpret_cast<uint16_t*>(dst + (size_t)nv * 16 + tid * 2) =
             *reinterpret_cast<const uint16_t*>(src + nv * 16 + tid * 2);
+        count_writes(dst + (size_t)nv * 16 + tid * 2, 1);
+    }
 }
 
 template <int DT, int MB>
@@ -389,12 +393,16 @@ __device__ __forceinline__ void fma8(u32x4 w, u32x4 x, float* acc)
 __device__ __forceinline__ void wave_copy_out(const unsigned char* src, unsigned char* dst, int bytes, int lane)
 {
     const int nv = bytes >> 4;
-    for (int u = lane; u < nv; u += 64)
+    for (int u = lane; u < nv; u += 64) {
         *reinterpret_cast<uint4*>(dst + (size_t)u * 16) = *reinterpret_cast<const uint4*>(src + u * 16);
+        count_writes(dst + (size_t)u * 16, 8);
+    }
     const int tail = (bytes - nv * 16) >> 1;
-    if (lane < tail)
+    if (lane < tail) {
         *reinterpret_cast<uint16_t*>(dst + (size_t)nv * 16 + lane * 2) =
             *reinterpret_cast<const uint16_t*>(src + nv * 16 + lane * 2);
+        count_writes(dst + (size_t)nv * 16 + lane * 2, 1);
+    }
 }
 
 template <int DT, int C8, int R, int NWMAX>
@@ -817,5 +825,9 @@ hipError_t launch_dcn_offset_mask(const Geom& G, int dtype, const void* x, const
     return dtype == DT_F16 ? launch_typed<DT_F16>(G, F, x, dww, dwb, omw, omb, off, mask, s)
                            : launch_typed<DT_BF16>(G, F, x, dww, dwb, omw, omb, off, mask, s);
 }
+
+#ifdef DCN_COUNT_WRITES
+DCN_WRITE_COUNT_SETTER(frontend_count_writes)
+#endif
 
 }  // namespace dcn

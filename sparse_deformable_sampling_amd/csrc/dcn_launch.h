@@ -67,6 +67,7 @@ hipError_t launch_msda_backward(const MsdaGeom& g, const float* value, const flo
 hipError_t ring_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
 hipError_t fwd_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
 hipError_t msda_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
+hipError_t frontend_count_writes(unsigned int* counts, const void* base, unsigned long long n, unsigned int es);
 #endif
 
 }  // namespace dcn

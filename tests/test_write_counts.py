@@ -1,7 +1,7 @@
 """One writer per output element: the forward kernels are atomic-free, so every
 element of dcn_forward's output (and of msda_forward / msda_forward_ref's, on
-their vector paths) must be stored exactly once, and no store may land outside
-the output.  The debug build libdcn_count.so counts every output store per
+their vector paths, and of dcn_offset_mask's two outputs) must be stored
+exactly once, and no store may land outside the outputs.  The debug build libdcn_count.so counts every output store per
 element (include/dcn_debug.h); these tests run the ops through it, in the
 launch configurations the library picks at the workloads' full sizes and on
 the fallback kernels, and check every count and that the outputs equal the
@@ -115,3 +115,56 @@ def test_msda_forward_one_writer_per_output(sds, monkeypatch, ref):
         again = sds.msda_forward_ref(*args, **kw)
     check_counts("msda-" + ref, counts)
     assert torch.equal(out.view(torch.int32), again.view(torch.int32))
+
+
+FRONTEND_CASES = [
+    # name, (n, h, w, c, g), dtype: the wave kernel (C=64/128), its one-workgroup-per-CU launch, the
+    # tile kernel (C=320) and a ragged map whose pixel count is not a whole number of blocks
+    ("stage1", (64, 56, 56, 64, 4), "f16"),
+    ("table10", (64, 56, 56, 128, 4), "bf16"),
+    ("one-block", (48, 28, 28, 128, 8), "f16"),
+    ("stage3", (64, 14, 14, 320, 20), "f16"),
+    ("stage3", (64, 14, 14, 320, 20), "bf16"),
+    ("ragged", (3, 13, 11, 96, 2), "f16"),
+]
+
+
+@pytest.mark.parametrize("name,shape,dtype", FRONTEND_CASES)
+def test_frontend_one_writer_per_output(sds, name, shape, dtype):
+    """dcn_offset_mask writes two outputs: with the offsets registered, every
+    offset element is stored once and the stores outside them are exactly the
+    mask's elements; then the same with the mask registered.  Called through
+    the debug build's C ABI on preallocated outputs."""
+    import torch
+    n, h, w, c, g = shape
+    d = synth.frontend_inputs(n, h, w, c, g, dtype=dtype, seed=7)
+    t = {k: to_dev(v, dtype) for k, v in d.items()}
+    say("write-count front-end", name, dtype, shape)
+    ref_off, ref_mask = sds.dcnv4_offset_mask(t["x"], t["dw_weight"], t["dw_bias"], t["om_weight"], t["om_bias"],
+                                              group=g)
+    L = B.count_lib()
+    desc = B.make_desc(n, h, w, c, g, kernel=3, stride=1, pad=1, dil=1, dtype=CODE[dtype])
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda a: ctypes.c_void_p(a.data_ptr())
+    for which in ("offset", "mask"):
+        off = torch.full_like(ref_off, float("nan"))
+        mask = torch.full_like(ref_mask, float("nan"))
+        reg, other = (off, mask) if which == "offset" else (mask, off)
+        counts = torch.zeros(reg.numel() + 1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        B.check(L.dcn_debug_count_writes(ptr(counts), ptr(reg), reg.numel(), CODE[dtype]))
+        try:
+            B.check(L.dcn_offset_mask(ctypes.byref(desc), ptr(t["x"]), ptr(t["dw_weight"]), ptr(t["dw_bias"]),
+                                      ptr(t["om_weight"]), ptr(t["om_bias"]), ptr(off), ptr(mask), stream))
+            torch.cuda.synchronize()
+        finally:
+            B.check(L.dcn_debug_count_writes(None, None, 0, CODE[dtype]))
+        cnt = counts.cpu().numpy()
+        m = cnt.size - 1
+        bad = np.flatnonzero(cnt[:m] != 1)
+        say("  counts", name, which, "elements %d, not written once %d, other output's stores %d (expected %d)"
+            % (m, bad.size, cnt[m], other.numel()))
+        assert bad.size == 0, (name, which, bad[:8], cnt[bad[:8]])
+        assert cnt[m] == other.numel(), (name, which, int(cnt[m]), other.numel())
+        assert torch.equal(off.view(torch.int16), ref_off.view(torch.int16))
+        assert torch.equal(mask.view(torch.int16), ref_mask.view(torch.int16))
